@@ -1,0 +1,192 @@
+"""Benchmark of the SCAPE optimizer step on one MI355X.
+
+    python bench.py [--config llama1.8b] [--steps 5] [--warmup 2]
+
+A step is one call of scape_step: error-feedback compression of all K
+workers' gradients with the fused owner statistic, the partitioned top-k of
+the next mask, the sparse reduction and AdamS at the current mask.  Inputs
+(parameters, a pool of per-step gradient sets) are generated on the device
+before the timed region; the timed region is bracketed by synchronisations
+and holds exactly --steps calls.  Prints one JSON line.
+
+Algorithmic bytes per step (what the method must move, independent of this
+implementation):  B = (12K + 4 + (K+1)/8) * n + (8K + 28) * P * k.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "optimizer-step params/s + HBM GB/s (% peak), Llama-1.8B shape, 99% sparsity"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes_step(n, P, K, k):
+    return (12 * K + 4 + (K + 1) / 8) * n + (8 * K + 28) * P * k
+
+
+def alg_bytes_compress(n, P, K, k):
+    """The compress+statistic kernel: K workers read g and e and write e,
+    the owner statistic reads m, the mask words are read, and the K sparse
+    buffers are written."""
+    return (12 * K + 4) * n + n / 8 + 4 * K * P * k
+
+
+def cpu_baseline(cfg, g_dev, w_dev, seed, parts, log_fn):
+    """Times the CPU oracle on one step of the first `parts` partitions of
+    the same workload (their inputs copied from the device)."""
+    import torch
+    from oracle import scape_oracle as O
+    hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    total_t, total_n = 0.0, 0
+    for p in range(parts):
+        sl = slice(p * cfg.n_p, (p + 1) * cfg.n_p)
+        g = g_dev[:, sl].cpu().numpy()
+        w0 = w_dev[sl].cpu().numpy()
+        st = O.PartitionState.fresh(w0, cfg.K)
+        log_fn(f"cpu baseline: oracle step on partition {p} ({cfg.n_p} params)")
+        t0 = time.perf_counter()
+        O.step_partition(st, g, cfg.k, O.owner(p, cfg.P, cfg.K), hp, 1)
+        total_t += time.perf_counter() - t0
+        total_n += cfg.n_p
+        del g, st
+    torch.cuda.synchronize()
+    return {"value": total_n / total_t, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"step 1 of {parts} of {cfg.P} partitions ({total_n} params, {cfg.K} workers), "
+                      f"numpy single-threaded, {total_t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="llama1.8b")
+    ap.add_argument("--pool", type=int, default=3, help="distinct gradient sets cycled through")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-parts", type=int, default=1, help="partitions timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the simulated workers share one device and no "
+              "collective runs; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_communication_distributed_amd import scape as S
+    from sparse_communication_distributed_amd import workload as W
+
+    cfg = W.CONFIGS[args.config]
+    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.lib()
+    log(f"config {cfg.name}: n={n} P={P} K={K} k={k} pool={args.pool}")
+
+    d = S.dims(n, P, K)
+    bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
+    params = torch.empty(n, dtype=torch.float32, device=dev)
+    W.device_init_params(cfg, args.seed, params)
+    w_init = params.clone() if not args.no_cpu_baseline else None
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    e = torch.zeros((K, n), dtype=torch.float32, device=dev)
+    mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+    sigma = W.device_sigma(cfg, args.seed, dev)
+    pool = []
+    for s in range(args.pool):
+        gset = torch.empty((K, n), dtype=torch.float32, device=dev)
+        W.device_grads(cfg, s + 1, args.seed, sigma, gset)
+        pool.append(gset)
+        log(f"gradient set {s + 1}/{args.pool} generated")
+    del sigma
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    t = 0
+
+    def one_step():
+        nonlocal t
+        t += 1
+        S.step(d, params, pool[(t - 1) % len(pool)], m, v, e, mask, k, bt, cfg.lr, t, ws, stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+
+    # per-stage durations of the same steps, recorded with HIP events on the
+    # stream the kernels run on (a second, profiled pass of --steps steps)
+    S.profile_enable(True)
+    for _ in range(args.steps):
+        one_step()
+    stages = S.profile_collect()
+    S.profile_enable(False)
+    stage_ms = {name: tot / cnt for name, (tot, cnt) in stages.items() if cnt}
+    log("stage ms: " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in stage_ms.items()))
+
+    b_step = alg_bytes_step(n, P, K, k)
+    b_comp = alg_bytes_compress(n, P, K, k)
+    gbps = b_step / (ms * 1e-3) / 1e9
+    comp_ms = stage_ms.get("compress_stat", float("nan"))
+    comp_gbps = b_comp / (comp_ms * 1e-3) / 1e9
+    traffic = None
+    prof_path = os.path.join(ROOT, "profiles", f"compress_stat_{cfg.name}_counters.json")
+    if os.path.exists(prof_path):
+        with open(prof_path) as f:
+            traffic = json.load(f).get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": n / (ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n_params": n, "tensors": len(cfg.tensors), "partitions": P,
+                   "workers": K, "k_per_partition": k, "sparsity": cfg.sparsity,
+                   "gradient_law": cfg.grad_law, "gradient_sets": args.pool},
+        "hbm_gbps_alg": gbps,
+        "hbm_frac_alg": gbps / HBM_PEAK_GBPS,
+        "bytes_alg_per_step": b_step,
+        "stage_ms": stage_ms,
+        "roofline": {"bound": "hbm", "kernel": "compress_stat", "achieved": comp_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": comp_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, pool[0], w_init, args.seed, args.cpu_parts, log)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * scape.h — C ABI of libscape.so: SCAPE's per-step sparse optimizer path on
+ * one MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [P] SCAPE paper (Zheng, Chen, Xie, Zhang; arXiv 2607.01678, Chinese
+ *       translation): §II-A sharded data parallelism, §II-B top-k with error
+ *       feedback, §II-C AdamS eq. (2) and the bias-correction remark.
+ *   [S] "Sintesi Tecnica: SCAPE" (technical summary), §2 "Componenti del
+ *       Design del Sistema": partitioned mask synchronisation, one-step
+ *       mask lag, single-buffer second-moment rebuild, single-bit packed
+ *       masks ("Ottimizzazione della Memoria").
+ *
+ * Model.  The optimizer state is one flat fp32 buffer of n parameters cut
+ * into P equal contiguous partitions of n_p = n / P elements (the even
+ * optimizer shards of [P] §II-A).  K data-parallel workers are simulated on
+ * the one device: worker i's gradient and error-feedback buffer are rows i
+ * of [K][n] arrays.  Partition p is owned by worker floor(p*K/P).  In every
+ * partition the mask selects exactly k elements (k = per-partition count).
+ *
+ * Common rules for every call:
+ *   - Pointers are DEVICE pointers unless stated; the caller allocates and
+ *     owns every buffer, including workspaces and mask blobs.  The library
+ *     never allocates or frees device memory and keeps no device state.
+ *   - Arguments are validated synchronously before anything is enqueued; a
+ *     failed check returns a status and touches no buffer.
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     Calls on the same buffers must use one stream.  A launch failure
+ *     returns SCAPE_EHIP; device faults surface at the caller's next sync.
+ *   - Limits: 1 <= P <= 65535, 1 <= K, n % P == 0, n < 2^32, 1 <= k <= n_p.
+ *   - Arithmetic: IEEE binary32, each operation rounded separately (no
+ *     contraction), correctly rounded sqrt and division, subnormals kept.
+ *     Results are deterministic and match the CPU oracle bit for bit.
+ */
+#ifndef SCAPE_H
+#define SCAPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SCAPE_OK = 0,
+  SCAPE_EINVAL = 1,     /* null pointer, bad hyper-parameter, step < 1     */
+  SCAPE_ESHAPE = 2,     /* n, P, K or k outside the limits above           */
+  SCAPE_EWORKSPACE = 3, /* workspace smaller than scape_workspace_bytes()  */
+  SCAPE_EHIP = 4        /* a HIP launch or event call failed               */
+} scape_status;
+
+/* n = total parameters, num_partitions = P, num_workers = K. */
+typedef struct {
+  int64_t n;
+  int32_t num_partitions;
+  int32_t num_workers;
+} scape_dims;
+
+/* AdamS hyper-parameters ([P] §II-C eq. (2)): beta1, beta2 in [0, 1),
+ * eps > 0 and finite, weight_decay finite (lambda of eq. (2)). */
+typedef struct {
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} scape_betas;
+
+/*
+ * One mask M (k selected elements per partition), three views of it:
+ *   bits     u64[P * W], W = ceil(n_p / 64): partition p's bit j (local
+ *            index j) is bit (j % 64) of word p*W + j/64; bits past n_p are
+ *            zero.  This is the single-bit packed form of [S] §2.
+ *   idx      u32[P * k]: global indices (p*n_p + j) in ascending order;
+ *            partition p's k entries are idx[p*k .. p*k + k).
+ *   tile_off u32[P * T], T = ceil(n_p / scape_tile_elems()): for tile t of
+ *            partition p, the number of selected elements of p that lie
+ *            before local index t*scape_tile_elems().
+ * The sparse buffers b are laid out like idx: entry r of a buffer belongs to
+ * element idx[r].
+ */
+typedef struct {
+  uint64_t* bits;
+  uint32_t* idx;
+  uint32_t* tile_off;
+} scape_mask_view;
+
+/* ---------------------------------------------------------------- layout */
+
+/* Elements per compaction tile (the granularity of tile_off). */
+int64_t scape_tile_elems(void);
+
+/* Bytes of a mask blob holding TWO mask slots (the current mask M_t and the
+ * next one, for the one-step lag of [S] §2).  0 if dims/k are invalid. */
+size_t scape_mask_bytes(const scape_dims* dims, int64_t k);
+
+/* Fills *out with the views of slot 0 or 1 inside a blob of
+ * scape_mask_bytes() bytes starting at mask_blob (device pointer, 256-byte
+ * aligned).  Pure pointer arithmetic: nothing is read or written on the
+ * device. */
+scape_status scape_mask_slot(const scape_dims* dims, int64_t k, void* mask_blob, int slot,
+                             scape_mask_view* out);
+
+/* Bytes of scratch that scape_mask_topk and scape_step need (256-byte
+ * aligned device memory; contents undefined before and after a call). */
+size_t scape_workspace_bytes(const scape_dims* dims, int64_t k);
+
+/* ------------------------------------------------------------ components */
+
+/*
+ * Partitioned top-k mask ([S] §2, partitioned mask synchronisation; [P]
+ * abstract and §I): in each partition, select the k elements of stat[n]
+ * with the largest |stat|, ties going to the lower index (|x| is ranked by
+ * the binary32 pattern with the sign bit cleared, so -0 == +0 and NaN ranks
+ * above +inf).  Writes all three views of `out`; reads stat only.
+ */
+scape_status scape_mask_topk(const scape_dims* dims, int64_t k, const float* stat,
+                             scape_mask_view out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * Error-feedback compression at a fixed index set ([P] §II-B, with the
+ * shared mask of [S] §2): for every worker i and element j,
+ *   a = grads[i][j] + e[i][j];
+ *   if j is in `cur`:  b[i][r] = a (r = position of j in cur.idx), e[i][j] = 0
+ *   else:              e[i][j] = a.
+ * grads [K][n] is read-only; e [K][n] is updated in place; b is [K][P*k].
+ * Reads cur.bits and cur.tile_off (not cur.idx).
+ */
+scape_status scape_compress(const scape_dims* dims, int64_t k, const float* grads, float* e,
+                            scape_mask_view cur, float* b, hipStream_t stream);
+
+/*
+ * Reduction of the K workers' sparse buffers ([S] §2, the single
+ * synchronised sparse buffer): b_bar[r] = (((b[0][r] + b[1][r]) + ...) +
+ * b[K-1][r]) * fp32(1/K), for r < P*k.  In a multi-GPU run this is the
+ * sparse reduce-scatter; here the K buffers sit in the one device's HBM.
+ */
+scape_status scape_reduce_sparse(const scape_dims* dims, int64_t k, const float* b, float* b_bar,
+                                 hipStream_t stream);
+
+/*
+ * AdamS at the masked indices ([P] §II-C eq. (2) with bias correction; [S]
+ * §2, second moment rebuilt from the single buffer): for r < P*k with
+ * j = cur.idx[r], x = b_bar[r], mo = m[j], wo = params[j]:
+ *   mn = b1*mo + (1-b1)*x;  vn = b2*mo*mo + (1-b2)*x*x
+ *   mh = mn / (1 - b1^step); vh = vn / (1 - b2^step)   (host-computed fp32
+ *                                                        reciprocals)
+ *   params[j] = wo - lr*(mh/(sqrt(vh) + eps) + weight_decay*wo)
+ *   m[j] = mn; v[j] = vn.
+ * Entries off the mask are untouched; v is written, never read.
+ */
+scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params, float* m,
+                                float* v, const float* b_bar, scape_mask_view cur,
+                                scape_betas betas, float lr, int64_t step, hipStream_t stream);
+
+/* ------------------------------------------------------------ fused step */
+
+/*
+ * One SCAPE optimizer step t = `step` (>= 1) ([P] abstract, §II-B, §II-C;
+ * [S] §2).  mask_blob holds two slots (scape_mask_bytes): the step applies
+ * M_t from slot (t-1)&1 and writes M_{t+1} to slot t&1.
+ *   t == 1: slot 0 is ignored and filled first with the top-k of the
+ *           statistic below (bootstrap), so M_1 = M_2.
+ *   1. a^i = grads[i] + e[i]; error-feedback compression at M_t into the
+ *      K sparse buffers (kept in the workspace); e updated in place.
+ *   2. statistic per partition p with owner o: s = b1*m + (1-b1)*a^o, using
+ *      m before this step's update; M_{t+1} = per-partition top-k of |s|.
+ *   3. b_bar = worker mean of the sparse buffers; AdamS at M_t.
+ * params, m, v [n], e [K][n] and mask_blob are in/out; grads [K][n] is
+ * read-only; workspace as scape_workspace_bytes().
+ */
+scape_status scape_step(const scape_dims* dims, float* params, const float* grads, float* m,
+                        float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
+                        int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Overlap of two masks: *count_out (device u64) = |A ∩ B| summed over all
+ * partitions (the consecutive-step mask stability the [P] §I insight
+ * rests on; divide by P*k for the fraction).  Reads a.bits and b.bits.
+ */
+scape_status scape_mask_overlap(const scape_dims* dims, int64_t k, scape_mask_view a,
+                                scape_mask_view b, uint64_t* count_out, hipStream_t stream);
+
+/* -------------------------------------------------------------- utility */
+
+const char* scape_status_string(scape_status s);
+/* Detail of the last failing call on this thread (static storage). */
+const char* scape_last_error(void);
+
+/*
+ * Stage timing with HIP events recorded on the caller's stream.  While
+ * enabled, scape_step records an event pair around each of its stages.
+ * scape_profile_collect waits for the recorded events, writes per-stage
+ * total milliseconds and launch counts (arrays of scape_profile_stages()
+ * entries, host memory) and clears the record.  Stage names come from
+ * scape_profile_stage_name().  Not thread-safe.
+ */
+int scape_profile_stages(void);
+const char* scape_profile_stage_name(int stage);
+scape_status scape_profile_enable(int on);
+scape_status scape_profile_collect(double* ms_out, int64_t* count_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCAPE_H */

@@ -1,0 +1,104 @@
+// Sparse-buffer reduction and the AdamS update at the masked indices.
+//
+// Reduction: b_bar[r] = (((b0 + b1) + ...) + b_{K-1}) * fp32(1/K), the
+// in-HBM stand-in for the sparse reduce-scatter of the single synchronised
+// buffer (technical summary §2).
+// AdamS (SCAPE paper §II-C eq. (2), with bias correction): the second
+// moment is rebuilt from m_{t-1} and the synchronised buffer alone.
+// Every float operation below is rounded on its own: contraction is off for
+// this file, and sqrtf and '/' are the correctly rounded forms.
+#include "scape_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace scape {
+namespace {
+
+struct AdamsK {
+  float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr;
+  int64_t n;
+};
+
+__device__ __forceinline__ void adams_one(int64_t j, float x, float* __restrict__ w,
+                                          float* __restrict__ m, float* __restrict__ v,
+                                          const AdamsK& c) {
+  if (j >= c.n) return;  // an index list from a malformed mask stays in bounds
+  const float mo = m[j];
+  const float wo = w[j];
+  const float mn = (c.b1 * mo) + (c.c1 * x);
+  const float vn = (c.b2 * (mo * mo)) + (c.c2 * (x * x));
+  const float mh = mn * c.ibc1;
+  const float vh = vn * c.ibc2;
+  const float d = sqrtf(vh) + c.eps;
+  const float u = mh / d;
+  const float wn = wo - (c.lr * (u + (c.wd * wo)));
+  m[j] = mn;
+  v[j] = vn;
+  w[j] = wn;
+}
+
+__device__ __forceinline__ float worker_mean(const float* __restrict__ b, int K, int64_t pk,
+                                             int64_t r, float invK) {
+  float s = b[r];
+  for (int i = 1; i < K; ++i) s = s + b[(int64_t)i * pk + r];
+  return s * invK;
+}
+
+__global__ void __launch_bounds__(kThreads)
+reduce_kernel(const float* __restrict__ b, int K, int64_t pk, float invK, float* __restrict__ bbar) {
+  for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < pk; r += (int64_t)gridDim.x * kThreads)
+    bbar[r] = worker_mean(b, K, pk, r, invK);
+}
+
+__global__ void __launch_bounds__(kThreads)
+adams_kernel(const float* __restrict__ bbar, const uint32_t* __restrict__ idx, int64_t pk,
+             float* __restrict__ w, float* __restrict__ m, float* __restrict__ v, AdamsK c) {
+  for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < pk; r += (int64_t)gridDim.x * kThreads)
+    adams_one(idx[r], bbar[r], w, m, v, c);
+}
+
+__global__ void __launch_bounds__(kThreads)
+reduce_adams_kernel(const float* __restrict__ b, int K, float invK, const uint32_t* __restrict__ idx,
+                    int64_t pk, float* __restrict__ w, float* __restrict__ m, float* __restrict__ v,
+                    AdamsK c) {
+  for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < pk; r += (int64_t)gridDim.x * kThreads)
+    adams_one(idx[r], worker_mean(b, K, pk, r, invK), w, m, v, c);
+}
+
+unsigned grid_for(int64_t count) {
+  int64_t blocks = (count + kThreads - 1) / kThreads;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  return (unsigned)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const Geom& g, const float* b, float* bbar, hipStream_t s) {
+  const int64_t pk = (int64_t)g.P * g.k;
+  const float invK = (float)(1.0 / (double)g.K);
+  reduce_kernel<<<grid_for(pk), kThreads, 0, s>>>(b, g.K, pk, invK, bbar);
+  return hipGetLastError();
+}
+
+hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, float* w, float* m,
+                        float* v, float b1, float b2, float c1, float c2, float ibc1, float ibc2,
+                        float eps, float wd, float lr, hipStream_t s) {
+  const int64_t pk = (int64_t)g.P * g.k;
+  AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
+  adams_kernel<<<grid_for(pk), kThreads, 0, s>>>(bbar, idx, pk, w, m, v, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_adams(const Geom& g, const float* b, const uint32_t* idx, float* w,
+                               float* m, float* v, float b1, float b2, float c1, float c2,
+                               float ibc1, float ibc2, float eps, float wd, float lr,
+                               hipStream_t s) {
+  const int64_t pk = (int64_t)g.P * g.k;
+  const float invK = (float)(1.0 / (double)g.K);
+  AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
+  reduce_adams_kernel<<<grid_for(pk), kThreads, 0, s>>>(b, g.K, invK, idx, pk, w, m, v, c);
+  return hipGetLastError();
+}
+
+}  // namespace scape

@@ -1,0 +1,393 @@
+// C ABI of libscape (declared in include/scape.h): argument validation,
+// geometry of masks and workspace, and the order of launches of one SCAPE
+// optimizer step.
+#include "scape.h"
+#include "scape_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <vector>
+
+namespace scape {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int bit_width_u64(uint64_t x) {
+  int b = 0;
+  while (x) {
+    ++b;
+    x >>= 1;
+  }
+  return b;
+}
+
+bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
+  if (P < 1 || P > 65535 || K < 1 || n < 1 || n % P != 0 || n >= (int64_t(1) << 32)) return false;
+  const int64_t n_p = n / P;
+  if (k < 1 || k > n_p) return false;
+  Geom r{};
+  r.n = n;
+  r.n_p = n_p;
+  r.k = k;
+  r.P = P;
+  r.K = K;
+  r.wpp = (n_p + 63) / 64;
+  r.tpp = (n_p + kTile - 1) / kTile;
+  int64_t G = (kTargetBlocks + P - 1) / P;
+  if (G > r.tpp) G = r.tpp;
+  if (G < 1) G = 1;
+  r.G = (int)G;
+  r.seg_tiles = (r.tpp + G - 1) / G;
+  r.seg_cap = r.seg_tiles * kTile;
+  r.R = r.G < kRefineBlocks ? r.G : kRefineBlocks;
+  r.idx_bits = bit_width_u64((uint64_t)(n_p - 1));
+  if (r.idx_bits < 1) r.idx_bits = 1;
+  r.idx_mask = (uint32_t)((uint64_t(1) << r.idx_bits) - 1);
+  // levels after level 1: key bits 18..7, 6..0, then the index bits
+  int nl = 0;
+  r.levels[nl++] = Level{32 + kL1Shift - kDigitBits, kDigitBits};
+  r.levels[nl++] = Level{32, kL1Shift - kDigitBits};
+  for (int rem = r.idx_bits; rem > 0;) {
+    const int nb = rem < kDigitBits ? rem : kDigitBits;
+    r.levels[nl++] = Level{rem - nb, nb};
+    rem -= nb;
+  }
+  r.nlevels = nl;
+  // mask slot
+  r.off_bits = 0;
+  r.off_idx = align256((size_t)P * r.wpp * 8);
+  r.off_toff = align256(r.off_idx + (size_t)P * k * 4);
+  r.slot_bytes = align256(r.off_toff + (size_t)P * r.tpp * 4);
+  // workspace
+  size_t o = 0;
+  r.ws_keys = o;    o = align256(o + (size_t)n * 4);
+  r.ws_b = o;       o = align256(o + (size_t)K * P * k * 4);
+  r.ws_hist = o;    o = align256(o + (size_t)P * kBins * 4);
+  r.ws_segcnt = o;  o = align256(o + (size_t)P * r.G * 4);
+  r.ws_cand = o;    o = align256(o + (size_t)P * r.G * r.seg_cap * 8);
+  r.ws_state = o;   o = align256(o + (size_t)P * sizeof(PartSel));
+  r.ws_tilecnt = o; o = align256(o + (size_t)P * r.tpp * 4);
+  r.ws_total = o;
+  *g = r;
+  return true;
+}
+
+}  // namespace scape
+
+using namespace scape;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+scape_status fail(scape_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+scape_status hip_check(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(SCAPE_EHIP, "%s: %s", where, hipGetErrorString(e));
+  return SCAPE_OK;
+}
+
+scape_status check_dims(const scape_dims* d, int64_t k, Geom* g) {
+  if (!d) return fail(SCAPE_EINVAL, "dims is null");
+  if (!make_geom(d->n, d->num_partitions, d->num_workers, k, g))
+    return fail(SCAPE_ESHAPE, "invalid shape: n=%lld P=%d K=%d k=%lld (need 1<=P<=65535, K>=1, n%%P==0, n<2^32, 1<=k<=n/P)",
+                (long long)d->n, d->num_partitions, d->num_workers, (long long)k);
+  return SCAPE_OK;
+}
+
+scape_status check_betas(const scape_betas& b, float lr) {
+  if (!(b.beta1 >= 0.0f && b.beta1 < 1.0f) || !(b.beta2 >= 0.0f && b.beta2 < 1.0f))
+    return fail(SCAPE_EINVAL, "betas must lie in [0, 1)");
+  if (!(b.eps > 0.0f) || !std::isfinite(b.eps)) return fail(SCAPE_EINVAL, "eps must be positive and finite");
+  if (!std::isfinite(b.weight_decay)) return fail(SCAPE_EINVAL, "weight_decay must be finite");
+  if (!std::isfinite(lr)) return fail(SCAPE_EINVAL, "lr must be finite");
+  return SCAPE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+float bias_reciprocal(float beta, int64_t t) {
+  double p = 1.0;
+  for (int64_t i = 0; i < t; ++i) p = p * (double)beta;
+  return (float)(1.0 / (1.0 - p));
+}
+
+scape_mask_view slot_view(const Geom& g, void* blob, int slot) {
+  char* base = static_cast<char*>(blob) + (size_t)slot * g.slot_bytes;
+  return scape_mask_view{reinterpret_cast<uint64_t*>(base + g.off_bits),
+                         reinterpret_cast<uint32_t*>(base + g.off_idx),
+                         reinterpret_cast<uint32_t*>(base + g.off_toff)};
+}
+
+struct Ws {
+  uint32_t* keys;
+  float* b;
+  uint32_t* hist;
+  uint32_t* segcnt;
+  uint64_t* cand;
+  PartSel* state;
+  uint32_t* tilecnt;
+};
+
+Ws ws_view(const Geom& g, void* ws) {
+  char* c = static_cast<char*>(ws);
+  return Ws{reinterpret_cast<uint32_t*>(c + g.ws_keys), reinterpret_cast<float*>(c + g.ws_b),
+            reinterpret_cast<uint32_t*>(c + g.ws_hist), reinterpret_cast<uint32_t*>(c + g.ws_segcnt),
+            reinterpret_cast<uint64_t*>(c + g.ws_cand), reinterpret_cast<PartSel*>(c + g.ws_state),
+            reinterpret_cast<uint32_t*>(c + g.ws_tilecnt)};
+}
+
+// ------------------------------------------------------------- profiling
+
+enum Stage { ST_BOOT = 0, ST_COMPRESS, ST_SELECT, ST_REFINE, ST_EMIT, ST_ADAMS, ST_COUNT };
+const char* kStageNames[ST_COUNT] = {"bootstrap_select", "compress_stat", "select_pass",
+                                     "refine", "emit", "reduce_adams"};
+
+struct Rec {
+  int stage;
+  hipEvent_t a, b;
+};
+
+struct Profiler {
+  bool on = false;
+  bool bad = false;  // an event call failed; the next collect reports it
+  std::vector<Rec> recs;
+  int open = -1;
+  hipStream_t stream = nullptr;
+  void begin(int stage, hipStream_t s) {
+    if (!on) return;
+    end();
+    Rec r{stage, nullptr, nullptr};
+    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) {
+      bad = true;
+      return;
+    }
+    if (hipEventRecord(r.a, s) != hipSuccess) bad = true;
+    recs.push_back(r);
+    open = (int)recs.size() - 1;
+    stream = s;
+  }
+  void end() {
+    if (!on || open < 0) return;
+    if (hipEventRecord(recs[open].b, stream) != hipSuccess) bad = true;
+    open = -1;
+  }
+};
+Profiler g_prof;
+
+// Sub-stage boundaries inside the selection pipeline.
+struct SelectMarks {
+  hipStream_t s;
+};
+void select_mark(void* ctx, int id) {
+  SelectMarks* m = static_cast<SelectMarks*>(ctx);
+  if (id == 1) g_prof.begin(ST_REFINE, m->s);
+  if (id == 2) g_prof.begin(ST_EMIT, m->s);
+}
+
+scape_status run_select(const Geom& g, const Ws& w, scape_mask_view out, hipStream_t s, bool prof) {
+  SelectMarks marks{s};
+  hipError_t e = launch_select(g, w.keys, w.hist, w.segcnt, w.cand, w.state, w.tilecnt, out.bits,
+                               out.idx, out.tile_off, s, prof ? select_mark : nullptr, &marks);
+  return hip_check(e, "select launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t scape_tile_elems(void) { return kTile; }
+
+size_t scape_mask_bytes(const scape_dims* dims, int64_t k) {
+  Geom g;
+  if (!dims || !make_geom(dims->n, dims->num_partitions, dims->num_workers, k, &g)) return 0;
+  return 2 * g.slot_bytes;
+}
+
+scape_status scape_mask_slot(const scape_dims* dims, int64_t k, void* mask_blob, int slot,
+                             scape_mask_view* out) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!mask_blob || !out) return fail(SCAPE_EINVAL, "mask_blob or out is null");
+  if (slot != 0 && slot != 1) return fail(SCAPE_EINVAL, "slot must be 0 or 1");
+  *out = slot_view(g, mask_blob, slot);
+  return SCAPE_OK;
+}
+
+size_t scape_workspace_bytes(const scape_dims* dims, int64_t k) {
+  Geom g;
+  if (!dims || !make_geom(dims->n, dims->num_partitions, dims->num_workers, k, &g)) return 0;
+  return g.ws_total;
+}
+
+scape_status scape_mask_topk(const scape_dims* dims, int64_t k, const float* stat,
+                             scape_mask_view out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!stat || !out.bits || !out.idx || !out.tile_off || !workspace)
+    return fail(SCAPE_EINVAL, "null pointer argument");
+  if (workspace_bytes < g.ws_total)
+    return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
+  Ws w = ws_view(g, workspace);
+  const bool vec = (g.n_p % 4 == 0) && aligned16(stat) && aligned16(w.keys);
+  if ((st = hip_check(launch_zero_u32(w.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
+  if ((st = hip_check(launch_keys_from_stat(g, stat, w.keys, w.hist, vec, stream), "keys"))) return st;
+  return run_select(g, w, out, stream, false);
+}
+
+scape_status scape_compress(const scape_dims* dims, int64_t k, const float* grads, float* e,
+                            scape_mask_view cur, float* b, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!grads || !e || !cur.bits || !cur.tile_off || !b) return fail(SCAPE_EINVAL, "null pointer argument");
+  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e);
+  return hip_check(launch_compress(g, grads, e, cur.bits, cur.tile_off, b, false, nullptr, 0.f, 0.f,
+                                   nullptr, nullptr, vec, stream),
+                   "compress");
+}
+
+scape_status scape_reduce_sparse(const scape_dims* dims, int64_t k, const float* b, float* b_bar,
+                                 hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!b || !b_bar) return fail(SCAPE_EINVAL, "null pointer argument");
+  return hip_check(launch_reduce(g, b, b_bar, stream), "reduce");
+}
+
+scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params, float* m,
+                                float* v, const float* b_bar, scape_mask_view cur,
+                                scape_betas betas, float lr, int64_t step, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!params || !m || !v || !b_bar || !cur.idx) return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = check_betas(betas, lr))) return st;
+  if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  const float b1 = betas.beta1, b2 = betas.beta2;
+  const float c1 = 1.0f - b1, c2 = 1.0f - b2;
+  return hip_check(launch_adams(g, b_bar, cur.idx, params, m, v, b1, b2, c1, c2,
+                                bias_reciprocal(b1, step), bias_reciprocal(b2, step), betas.eps,
+                                betas.weight_decay, lr, stream),
+                   "adams");
+}
+
+scape_status scape_step(const scape_dims* dims, float* params, const float* grads, float* m,
+                        float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
+                        int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!params || !grads || !m || !v || !e || !mask_blob || !workspace)
+    return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = check_betas(betas, lr))) return st;
+  if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  if (workspace_bytes < g.ws_total)
+    return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
+
+  Ws w = ws_view(g, workspace);
+  const scape_mask_view cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
+  const scape_mask_view nxt = slot_view(g, mask_blob, (int)(step & 1));
+  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m) &&
+                   aligned16(w.keys);
+  const float b1 = betas.beta1, b2 = betas.beta2;
+  const float c1 = 1.0f - b1, c2 = 1.0f - b2;
+  const bool prof = g_prof.on;
+
+  if (step == 1) {  // bootstrap: M_1 = top-k of the step-1 statistic
+    g_prof.begin(ST_BOOT, stream);
+    if ((st = hip_check(launch_zero_u32(w.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
+    if ((st = hip_check(launch_keys_from_state(g, m, grads, e, b1, c1, w.keys, w.hist, vec, stream),
+                        "bootstrap keys")))
+      return st;
+    if ((st = run_select(g, w, cur, stream, false))) return st;
+  }
+  g_prof.begin(ST_COMPRESS, stream);
+  if ((st = hip_check(launch_zero_u32(w.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
+  if ((st = hip_check(launch_compress(g, grads, e, cur.bits, cur.tile_off, w.b, true, m, b1, c1,
+                                      w.keys, w.hist, vec, stream),
+                      "compress")))
+    return st;
+  g_prof.begin(ST_SELECT, stream);
+  if ((st = run_select(g, w, nxt, stream, prof))) return st;
+  g_prof.begin(ST_ADAMS, stream);
+  st = hip_check(launch_reduce_adams(g, w.b, cur.idx, params, m, v, b1, b2, c1, c2,
+                                     bias_reciprocal(b1, step), bias_reciprocal(b2, step), betas.eps,
+                                     betas.weight_decay, lr, stream),
+                 "reduce_adams");
+  g_prof.end();
+  return st;
+}
+
+scape_status scape_mask_overlap(const scape_dims* dims, int64_t k, scape_mask_view a,
+                                scape_mask_view b, uint64_t* count_out, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!a.bits || !b.bits || !count_out) return fail(SCAPE_EINVAL, "null pointer argument");
+  return hip_check(launch_overlap(g, a.bits, b.bits, count_out, stream), "overlap");
+}
+
+const char* scape_status_string(scape_status s) {
+  switch (s) {
+    case SCAPE_OK: return "ok";
+    case SCAPE_EINVAL: return "invalid argument";
+    case SCAPE_ESHAPE: return "invalid shape";
+    case SCAPE_EWORKSPACE: return "workspace too small";
+    case SCAPE_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* scape_last_error(void) { return g_err; }
+
+int scape_profile_stages(void) { return ST_COUNT; }
+
+const char* scape_profile_stage_name(int stage) {
+  return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "";
+}
+
+scape_status scape_profile_enable(int on) {
+  g_prof.end();
+  g_prof.on = on != 0;
+  return SCAPE_OK;
+}
+
+scape_status scape_profile_collect(double* ms_out, int64_t* count_out) {
+  if (!ms_out || !count_out) return fail(SCAPE_EINVAL, "null pointer argument");
+  g_prof.end();
+  for (int i = 0; i < ST_COUNT; ++i) {
+    ms_out[i] = 0.0;
+    count_out[i] = 0;
+  }
+  scape_status st = SCAPE_OK;
+  for (Rec& r : g_prof.recs) {
+    float ms = 0.f;
+    if (st == SCAPE_OK) {
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e != hipSuccess) st = hip_check(e, "profile events");
+    }
+    ms_out[r.stage] += ms;
+    count_out[r.stage] += 1;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.recs.clear();
+  if (g_prof.bad && st == SCAPE_OK) st = fail(SCAPE_EHIP, "profile: an event could not be created or recorded");
+  g_prof.bad = false;
+  return st;
+}
+
+}  // extern "C"

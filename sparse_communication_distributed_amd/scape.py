@@ -1,0 +1,246 @@
+"""ctypes binding of libscape.so (C ABI declared in include/scape.h).
+
+Argument marshalling only: every step of the optimizer path runs in the HIP
+library.  Tensors are torch device tensors (fp32 / uint8 blobs); streams are
+torch streams (default: the current stream).  There is no fallback: if the
+library is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libscape.so")
+
+c_int64, c_int32, c_int, c_size_t = ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
+c_float, c_void_p, c_char_p = ctypes.c_float, ctypes.c_void_p, ctypes.c_char_p
+
+STATUS = {0: "SCAPE_OK", 1: "SCAPE_EINVAL", 2: "SCAPE_ESHAPE", 3: "SCAPE_EWORKSPACE", 4: "SCAPE_EHIP"}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n", c_int64), ("num_partitions", c_int32), ("num_workers", c_int32)]
+
+
+class Betas(ctypes.Structure):
+    _fields_ = [("beta1", c_float), ("beta2", c_float), ("eps", c_float), ("weight_decay", c_float)]
+
+
+class MaskView(ctypes.Structure):
+    _fields_ = [("bits", c_void_p), ("idx", c_void_p), ("tile_off", c_void_p)]
+
+
+class ScapeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+# name -> (restype, argtypes); mirrors include/scape.h
+_SIGS = {
+    "scape_tile_elems": (c_int64, []),
+    "scape_mask_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64]),
+    "scape_mask_slot": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, c_int, ctypes.POINTER(MaskView)]),
+    "scape_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64]),
+    "scape_mask_topk": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, MaskView, c_void_p, c_size_t, c_void_p]),
+    "scape_compress": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, c_void_p, MaskView, c_void_p, c_void_p]),
+    "scape_reduce_sparse": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, c_void_p, c_void_p]),
+    "scape_adams_update": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   MaskView, Betas, c_float, c_int64, c_void_p]),
+    "scape_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                           c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p]),
+    "scape_mask_overlap": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, MaskView, c_void_p, c_void_p]),
+    "scape_status_string": (c_char_p, [c_int]),
+    "scape_last_error": (c_char_p, []),
+    "scape_profile_stages": (c_int, []),
+    "scape_profile_stage_name": (c_char_p, [c_int]),
+    "scape_profile_enable": (c_int, [c_int]),
+    "scape_profile_collect": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int64)]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libscape.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_communication_distributed_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def exported_names() -> Tuple[str, ...]:
+    return tuple(_SIGS)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise ScapeError(status, lib().scape_last_error().decode())
+
+
+def dims(n: int, P: int, K: int) -> Dims:
+    return Dims(int(n), int(P), int(K))
+
+
+def betas(beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0) -> Betas:
+    return Betas(beta1, beta2, eps, weight_decay)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+# ------------------------------------------------------------------- layout
+
+
+def tile_elems() -> int:
+    return int(lib().scape_tile_elems())
+
+
+def mask_bytes(d: Dims, k: int) -> int:
+    return int(lib().scape_mask_bytes(ctypes.byref(d), k))
+
+
+def workspace_bytes(d: Dims, k: int) -> int:
+    return int(lib().scape_workspace_bytes(ctypes.byref(d), k))
+
+
+def mask_slot(d: Dims, k: int, blob, slot: int) -> MaskView:
+    mv = MaskView()
+    _check(lib().scape_mask_slot(ctypes.byref(d), k, _ptr(blob), slot, ctypes.byref(mv)))
+    return mv
+
+
+def mask_slot_tensors(d: Dims, k: int, blob, slot: int):
+    """torch views (bits int64 [P*W], idx int32 [P*k], tile_off int32 [P*T])
+    of one slot inside a uint8 blob tensor."""
+    import torch
+    mv = mask_slot(d, k, blob, slot)
+    base = blob.data_ptr()
+    P, n_p = d.num_partitions, d.n // d.num_partitions
+    W = (n_p + 63) // 64
+    T = (n_p + tile_elems() - 1) // tile_elems()
+
+    def sub(ptr, count, dtype, size):
+        off = ptr - base
+        return blob[off:off + count * size].view(dtype)
+
+    return (sub(mv.bits, P * W, torch.int64, 8), sub(mv.idx, P * k, torch.int32, 4),
+            sub(mv.tile_off, P * T, torch.int32, 4))
+
+
+def view_from_tensors(bits=None, idx=None, tile_off=None) -> MaskView:
+    return MaskView(_ptr(bits) or None, _ptr(idx) or None, _ptr(tile_off) or None)
+
+
+# --------------------------------------------------------------- components
+
+
+def mask_topk(d: Dims, k: int, stat, out: MaskView, workspace, stream=None) -> None:
+    _check(lib().scape_mask_topk(ctypes.byref(d), k, _ptr(stat), out, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def compress(d: Dims, k: int, grads, e, cur: MaskView, b, stream=None) -> None:
+    _check(lib().scape_compress(ctypes.byref(d), k, _ptr(grads), _ptr(e), cur, _ptr(b), _stream(stream)))
+
+
+def reduce_sparse(d: Dims, k: int, b, b_bar, stream=None) -> None:
+    _check(lib().scape_reduce_sparse(ctypes.byref(d), k, _ptr(b), _ptr(b_bar), _stream(stream)))
+
+
+def adams_update(d: Dims, k: int, params, m, v, b_bar, cur: MaskView, bt: Betas, lr: float, step: int,
+                 stream=None) -> None:
+    _check(lib().scape_adams_update(ctypes.byref(d), k, _ptr(params), _ptr(m), _ptr(v), _ptr(b_bar), cur,
+                                    bt, lr, step, _stream(stream)))
+
+
+def step(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: float, step_no: int,
+         workspace, stream=None) -> None:
+    _check(lib().scape_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
+                            _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mask_overlap(d: Dims, k: int, a: MaskView, b: MaskView, count_out, stream=None) -> None:
+    _check(lib().scape_mask_overlap(ctypes.byref(d), k, a, b, _ptr(count_out), _stream(stream)))
+
+
+# ---------------------------------------------------------------- profiling
+
+
+def profile_stage_names():
+    L = lib()
+    return [L.scape_profile_stage_name(i).decode() for i in range(L.scape_profile_stages())]
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib().scape_profile_enable(1 if on else 0))
+
+
+def profile_collect():
+    """{stage: (total_ms, launches)} for the steps since the last collect."""
+    L = lib()
+    n = L.scape_profile_stages()
+    ms = (ctypes.c_double * n)()
+    cnt = (c_int64 * n)()
+    _check(L.scape_profile_collect(ms, cnt))
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(profile_stage_names())}
+
+
+# ---------------------------------------------------------------- optimizer
+
+
+class ScapeOptimizer:
+    """Device state of one SCAPE optimizer over a flat fp32 buffer.
+
+    Holds params, m, v [n], the K error-feedback rows e [K][n], the two-slot
+    mask blob and the workspace; ``step(grads)`` runs one fused step with
+    grads [K][n] (fp32, device)."""
+
+    def __init__(self, params, P: int, K: int, k: int, beta1=0.9, beta2=0.95, eps=1e-8,
+                 weight_decay=0.0, lr=1e-3, device=None):
+        import torch
+        self.n = params.numel()
+        self.d = dims(self.n, P, K)
+        self.k, self.P, self.K = int(k), int(P), int(K)
+        self.bt = betas(beta1, beta2, eps, weight_decay)
+        self.lr = float(lr)
+        dev = params.device if device is None else device
+        self.params = params.to(dev, torch.float32).contiguous()
+        self.m = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.e = torch.zeros((K, self.n), dtype=torch.float32, device=dev)
+        mb = mask_bytes(self.d, self.k)
+        wb = workspace_bytes(self.d, self.k)
+        if mb == 0 or wb == 0:
+            raise ScapeError(2, f"invalid shape n={self.n} P={P} K={K} k={k}")
+        self.mask = torch.zeros(mb, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+        self.t = 0
+
+    def step(self, grads, stream=None) -> None:
+        self.t += 1
+        step(self.d, self.params, grads, self.m, self.v, self.e, self.mask, self.k, self.bt, self.lr,
+             self.t, self.ws, stream)
+
+    def slot(self, which: str = "next"):
+        """Mask views (bits, idx, tile_off): "next" = M_{t+1}, "current" = M_t."""
+        s = (self.t & 1) if which == "next" else ((self.t - 1) & 1)
+        return mask_slot_tensors(self.d, self.k, self.mask, s)

@@ -1,0 +1,141 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/scape.h declares, sizes its layouts, and rejects invalid arguments
+synchronously (validation happens before any HIP call)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_communication_distributed_amd import scape as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scape.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(S.LIB_PATH), reason="libscape.so not built")
+
+FAKE = 0x10000  # a non-null address that is never dereferenced by a rejected call
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(scape_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported_and_bound():
+    L = S.lib()
+    names = header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(S.exported_names()) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_layout_sizes():
+    d = S.dims(1 << 20, 4, 2)
+    k = 26214
+    T = S.tile_elems()
+    assert T == 4096
+    P, n_p = 4, (1 << 20) // 4
+    slot_min = P * (n_p // 64) * 8 + P * k * 4 + P * (n_p // T) * 4
+    mb = S.mask_bytes(d, k)
+    assert mb >= 2 * slot_min and mb % 256 == 0
+    ws = S.workspace_bytes(d, k)
+    assert ws >= 4 * (1 << 20) + 2 * P * k * 4
+    mv0 = S.MaskView()
+    mv1 = S.MaskView()
+    L = S.lib()
+    assert L.scape_mask_slot(ctypes.byref(d), k, FAKE, 0, ctypes.byref(mv0)) == 0
+    assert L.scape_mask_slot(ctypes.byref(d), k, FAKE, 1, ctypes.byref(mv1)) == 0
+    assert mv0.bits == FAKE and mv1.bits == FAKE + mb // 2
+    assert mv0.idx - mv0.bits >= P * (n_p // 64) * 8 and mv0.idx % 256 == 0
+    assert mv0.tile_off - mv0.idx >= P * k * 4
+    assert L.scape_mask_slot(ctypes.byref(d), k, FAKE, 2, ctypes.byref(mv0)) == 1
+
+
+@pytest.mark.parametrize("n,P,K,k", [(100, 3, 1, 1), (100, 4, 0, 1), (100, 0, 1, 1), (100, 4, 1, 0),
+                                     (100, 4, 1, 26), (1 << 32, 1, 1, 1), (0, 1, 1, 1)])
+def test_invalid_shapes(n, P, K, k):
+    L = S.lib()
+    d = S.dims(n, P, K)
+    assert S.mask_bytes(d, k) == 0
+    assert S.workspace_bytes(d, k) == 0
+    st = L.scape_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k, S.betas(), 1e-3, 1, FAKE,
+                      1 << 40, None)
+    assert st == 2
+    assert b"invalid shape" in L.scape_last_error()
+
+
+def _step(d, k, ptrs=None, bt=None, lr=1e-3, step=1, wsb=None):
+    L = S.lib()
+    p = dict(params=FAKE, grads=FAKE, m=FAKE, v=FAKE, e=FAKE, mask=FAKE, ws=FAKE)
+    p.update(ptrs or {})
+    return L.scape_step(ctypes.byref(d), p["params"], p["grads"], p["m"], p["v"], p["e"], p["mask"], k,
+                        bt or S.betas(), lr, step, p["ws"],
+                        S.workspace_bytes(d, k) if wsb is None else wsb, None)
+
+
+@pytest.mark.parametrize("which", ["params", "grads", "m", "v", "e", "mask", "ws"])
+def test_step_rejects_null_pointers(which):
+    d = S.dims(4096, 2, 2)
+    assert _step(d, 10, {which: None}) == 1
+
+
+@pytest.mark.parametrize("bt,lr", [
+    (S.betas(beta1=1.0), 1e-3), (S.betas(beta1=-0.1), 1e-3), (S.betas(beta2=1.5), 1e-3),
+    (S.betas(eps=0.0), 1e-3), (S.betas(eps=float("inf")), 1e-3), (S.betas(weight_decay=float("nan")), 1e-3),
+    (S.betas(), float("nan")), (S.betas(), float("inf")), (S.betas(beta1=float("nan")), 1e-3),
+])
+def test_step_rejects_bad_hyper_parameters(bt, lr):
+    d = S.dims(4096, 2, 2)
+    assert _step(d, 10, bt=bt, lr=lr) == 1
+
+
+def test_step_rejects_step_zero_and_small_workspace():
+    d = S.dims(4096, 2, 2)
+    assert _step(d, 10, step=0) == 1
+    assert _step(d, 10, wsb=S.workspace_bytes(d, 10) - 1) == 3
+    assert b"workspace" in S.lib().scape_last_error()
+
+
+def test_component_validation():
+    L = S.lib()
+    d = S.dims(4096, 2, 2)
+    mv = S.MaskView(FAKE, FAKE, FAKE)
+    nul = S.MaskView(FAKE, None, FAKE)
+    ws = S.workspace_bytes(d, 10)
+    assert L.scape_mask_topk(ctypes.byref(d), 10, None, mv, FAKE, ws, None) == 1
+    assert L.scape_mask_topk(ctypes.byref(d), 10, FAKE, nul, FAKE, ws, None) == 1
+    assert L.scape_mask_topk(ctypes.byref(d), 10, FAKE, mv, FAKE, ws - 1, None) == 3
+    assert L.scape_mask_topk(ctypes.byref(d), 2049, FAKE, mv, FAKE, ws, None) == 2
+    assert L.scape_compress(ctypes.byref(d), 10, FAKE, None, mv, FAKE, None) == 1
+    assert L.scape_compress(ctypes.byref(d), 10, FAKE, FAKE, S.MaskView(None, FAKE, FAKE), FAKE, None) == 1
+    assert L.scape_reduce_sparse(ctypes.byref(d), 10, FAKE, None, None) == 1
+    assert L.scape_adams_update(ctypes.byref(d), 10, FAKE, FAKE, FAKE, FAKE, mv, S.betas(), 1e-3, 0, None) == 1
+    assert L.scape_adams_update(ctypes.byref(d), 10, FAKE, FAKE, FAKE, FAKE, nul, S.betas(), 1e-3, 1, None) == 1
+    assert L.scape_adams_update(ctypes.byref(d), 10, FAKE, FAKE, FAKE, FAKE, mv, S.betas(beta2=1.0), 1e-3, 1,
+                                None) == 1
+    assert L.scape_mask_overlap(ctypes.byref(d), 10, mv, mv, None, None) == 1
+    assert L.scape_mask_topk(None, 10, FAKE, mv, FAKE, ws, None) == 1
+
+
+def test_status_strings_and_profile_names():
+    L = S.lib()
+    assert L.scape_status_string(0) == b"ok"
+    assert L.scape_status_string(3) == b"workspace too small"
+    names = S.profile_stage_names()
+    assert names == ["bootstrap_select", "compress_stat", "select_pass", "refine", "emit", "reduce_adams"]
+    assert L.scape_profile_collect(None, None) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(S, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        S.lib()

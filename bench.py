@@ -36,11 +36,13 @@ def alg_bytes_step(n, P, K, k):
     return (12 * K + 4 + (K + 1) / 8) * n + (8 * K + 28) * P * k
 
 
-def alg_bytes_compress(n, P, K, k):
-    """The compress+statistic kernel: K workers read g and e and write e,
-    the owner statistic reads m, the mask words are read, and the K sparse
-    buffers are written."""
-    return (12 * K + 4) * n + n / 8 + 4 * K * P * k
+def alg_bytes_step_pass(n, P, K, k):
+    """The fused step pass: K workers read g and e and write e, the owner
+    statistic reads m, the mask words are read once, the K sparse buffers
+    are written, and AdamS reads w and writes w, m, v at the P*k masked
+    elements (its m read is the statistic's).  Candidate captures and the
+    saved pre-update m are implementation traffic, not counted."""
+    return (12 * K + 4) * n + n / 8 + 4 * K * P * k + 16 * P * k
 
 
 def cpu_baseline(cfg, g_dev, w_dev, seed, parts, log_fn):
@@ -67,6 +69,28 @@ def cpu_baseline(cfg, g_dev, w_dev, seed, parts, log_fn):
                       f"numpy single-threaded, {total_t:.1f} s"}
 
 
+def stream_calibration(torch, dev, log_fn):
+    """A plain copy of 1 GiB (read 1 GiB, write 1 GiB), five times: the
+    known-size kernel that scales the HBM byte counters, and the streaming
+    rate this device reaches."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    gbps = 2 * (1 << 30) / (ms * 1e-3) / 1e9
+    log_fn(f"calibration copy 1 GiB: {ms:.3f} ms, {gbps:.0f} GB/s (read+write)")
+    del src, dst
+    return {"kernel": "torch copy_ fp32 1 GiB", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+            "ms": ms, "GBps": gbps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,6 +101,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-parts", type=int, default=1, help="partitions timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib", action="store_true",
+                    help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the simulated workers share one device and no "
@@ -114,6 +140,7 @@ def main():
     del sigma
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    calib = stream_calibration(torch, dev, log) if args.calib else None
 
     t = 0
 
@@ -148,12 +175,12 @@ def main():
     log("stage ms: " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in stage_ms.items()))
 
     b_step = alg_bytes_step(n, P, K, k)
-    b_comp = alg_bytes_compress(n, P, K, k)
+    b_comp = alg_bytes_step_pass(n, P, K, k)
     gbps = b_step / (ms * 1e-3) / 1e9
-    comp_ms = stage_ms.get("compress_stat", float("nan"))
+    comp_ms = stage_ms.get("step_pass", float("nan"))
     comp_gbps = b_comp / (comp_ms * 1e-3) / 1e9
     traffic = None
-    prof_path = os.path.join(ROOT, "profiles", f"compress_stat_{cfg.name}_counters.json")
+    prof_path = os.path.join(ROOT, "profiles", f"step_pass_{cfg.name}_counters.json")
     if os.path.exists(prof_path):
         with open(prof_path) as f:
             traffic = json.load(f).get("hbm_bytes_per_launch")
@@ -178,11 +205,13 @@ def main():
         "hbm_frac_alg": gbps / HBM_PEAK_GBPS,
         "bytes_alg_per_step": b_step,
         "stage_ms": stage_ms,
-        "roofline": {"bound": "hbm", "kernel": "compress_stat", "achieved": comp_gbps,
+        "roofline": {"bound": "hbm", "kernel": "compress_kernel (step pass)", "achieved": comp_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": comp_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms},
         "cpu_baseline": None,
     }
+    if calib is not None:
+        out["stream_calibration"] = calib
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, pool[0], w_init, args.seed, args.cpu_parts, log)
     print(json.dumps(out), flush=True)

@@ -77,6 +77,13 @@ typedef struct {
  *   tile_off u32[P * T], T = ceil(n_p / scape_tile_elems()): for tile t of
  *            partition p, the number of selected elements of p that lie
  *            before local index t*scape_tile_elems().
+ *   meta     u32[2 * P] threshold record (may be null where a call does not
+ *            need it): meta[p] = the k-th largest key of partition p in the
+ *            selection that produced this mask; meta[P + p] = the key bound
+ *            at which the next step captures selection candidates.  Any
+ *            value is safe: a bound that captures fewer than k keys of a
+ *            partition sends it through an exact recount, so the record only
+ *            affects speed, never the result.
  * The sparse buffers b are laid out like idx: entry r of a buffer belongs to
  * element idx[r].
  */
@@ -84,6 +91,7 @@ typedef struct {
   uint64_t* bits;
   uint32_t* idx;
   uint32_t* tile_off;
+  uint32_t* meta;
 } scape_mask_view;
 
 /* ---------------------------------------------------------------- layout */
@@ -113,7 +121,8 @@ size_t scape_workspace_bytes(const scape_dims* dims, int64_t k);
  * abstract and §I): in each partition, select the k elements of stat[n]
  * with the largest |stat|, ties going to the lower index (|x| is ranked by
  * the binary32 pattern with the sign bit cleared, so -0 == +0 and NaN ranks
- * above +inf).  Writes all three views of `out`; reads stat only.
+ * above +inf).  Writes bits, idx and tile_off of `out`, and meta when it is
+ * not null; reads stat only.
  */
 scape_status scape_mask_topk(const scape_dims* dims, int64_t k, const float* stat,
                              scape_mask_view out, void* workspace, size_t workspace_bytes,
@@ -163,6 +172,9 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
  * M_t from slot (t-1)&1 and writes M_{t+1} to slot t&1.
  *   t == 1: slot 0 is ignored and filled first with the top-k of the
  *           statistic below (bootstrap), so M_1 = M_2.
+ *   The selection of M_{t+1} reads the threshold record of slot (t-1)&1
+ *   (see scape_mask_view) to bound its candidate capture, and writes the
+ *   record of slot t&1.
  *   1. a^i = grads[i] + e[i]; error-feedback compression at M_t into the
  *      K sparse buffers (kept in the workspace); e updated in place.
  *   2. statistic per partition p with owner o: s = b1*m + (1-b1)*a^o, using

@@ -38,9 +38,10 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   if (G > r.tpp) G = r.tpp;
   if (G < 1) G = 1;
   r.G = (int)G;
-  r.seg_tiles = (r.tpp + G - 1) / G;
-  r.seg_cap = r.seg_tiles * kTile;
-  r.R = r.G < kRefineBlocks ? r.G : kRefineBlocks;
+  const int64_t groups = (r.tpp + 63) / 64;
+  int64_t R = (groups + 3) / 4;
+  if (R > kRefineBlocks) R = kRefineBlocks;
+  r.R = (int)(R < 1 ? 1 : R);
   r.idx_bits = bit_width_u64((uint64_t)(n_p - 1));
   if (r.idx_bits < 1) r.idx_bits = 1;
   r.idx_mask = (uint32_t)((uint64_t(1) << r.idx_bits) - 1);
@@ -54,18 +55,20 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
     rem -= nb;
   }
   r.nlevels = nl;
-  // mask slot
+  // mask slot: bits, idx, tile_off, then the threshold record u32[2P]
   r.off_bits = 0;
   r.off_idx = align256((size_t)P * r.wpp * 8);
   r.off_toff = align256(r.off_idx + (size_t)P * k * 4);
-  r.slot_bytes = align256(r.off_toff + (size_t)P * r.tpp * 4);
+  r.off_meta = align256(r.off_toff + (size_t)P * r.tpp * 4);
+  r.slot_bytes = align256(r.off_meta + (size_t)P * 2 * 4);
   // workspace
   size_t o = 0;
-  r.ws_keys = o;    o = align256(o + (size_t)n * 4);
   r.ws_b = o;       o = align256(o + (size_t)K * P * k * 4);
+  r.ws_mold = o;    o = align256(o + (size_t)P * k * 4);
   r.ws_hist = o;    o = align256(o + (size_t)P * kBins * 4);
-  r.ws_segcnt = o;  o = align256(o + (size_t)P * r.G * 4);
-  r.ws_cand = o;    o = align256(o + (size_t)P * r.G * r.seg_cap * 8);
+  r.ws_cand = o;    o = align256(o + (size_t)P * r.tpp * kTile * 8);
+  r.ws_cnt1 = o;    o = align256(o + (size_t)P * r.tpp * 4);
+  r.ws_cnt2 = o;    o = align256(o + (size_t)P * r.tpp * 4);
   r.ws_state = o;   o = align256(o + (size_t)P * sizeof(PartSel));
   r.ws_tilecnt = o; o = align256(o + (size_t)P * r.tpp * 4);
   r.ws_total = o;
@@ -123,32 +126,38 @@ scape_mask_view slot_view(const Geom& g, void* blob, int slot) {
   char* base = static_cast<char*>(blob) + (size_t)slot * g.slot_bytes;
   return scape_mask_view{reinterpret_cast<uint64_t*>(base + g.off_bits),
                          reinterpret_cast<uint32_t*>(base + g.off_idx),
-                         reinterpret_cast<uint32_t*>(base + g.off_toff)};
+                         reinterpret_cast<uint32_t*>(base + g.off_toff),
+                         reinterpret_cast<uint32_t*>(base + g.off_meta)};
 }
 
 struct Ws {
-  uint32_t* keys;
   float* b;
-  uint32_t* hist;
-  uint32_t* segcnt;
-  uint64_t* cand;
-  PartSel* state;
-  uint32_t* tilecnt;
+  float* mold;
+  SelectBufs sel;
 };
 
 Ws ws_view(const Geom& g, void* ws) {
   char* c = static_cast<char*>(ws);
-  return Ws{reinterpret_cast<uint32_t*>(c + g.ws_keys), reinterpret_cast<float*>(c + g.ws_b),
-            reinterpret_cast<uint32_t*>(c + g.ws_hist), reinterpret_cast<uint32_t*>(c + g.ws_segcnt),
-            reinterpret_cast<uint64_t*>(c + g.ws_cand), reinterpret_cast<PartSel*>(c + g.ws_state),
-            reinterpret_cast<uint32_t*>(c + g.ws_tilecnt)};
+  Ws w;
+  w.b = reinterpret_cast<float*>(c + g.ws_b);
+  w.mold = reinterpret_cast<float*>(c + g.ws_mold);
+  w.sel.hist = reinterpret_cast<uint32_t*>(c + g.ws_hist);
+  w.sel.cand = reinterpret_cast<uint64_t*>(c + g.ws_cand);
+  w.sel.cnt1 = reinterpret_cast<uint32_t*>(c + g.ws_cnt1);
+  w.sel.cnt2 = reinterpret_cast<uint32_t*>(c + g.ws_cnt2);
+  w.sel.state = reinterpret_cast<PartSel*>(c + g.ws_state);
+  w.sel.tilecnt = reinterpret_cast<uint32_t*>(c + g.ws_tilecnt);
+  return w;
 }
 
 // ------------------------------------------------------------- profiling
 
-enum Stage { ST_BOOT = 0, ST_COMPRESS, ST_SELECT, ST_REFINE, ST_EMIT, ST_ADAMS, ST_COUNT };
-const char* kStageNames[ST_COUNT] = {"bootstrap_select", "compress_stat", "select_pass",
-                                     "refine", "emit", "reduce_adams"};
+// AdamS inside the step pass (true) or as its own pass after the selection.
+constexpr bool kFuseAdams = true;
+
+enum Stage { ST_BOOT = 0, ST_PASS, ST_SELECT, ST_REFINE, ST_EMIT, ST_ADAMS, ST_COUNT };
+const char* kStageNames[ST_COUNT] = {"bootstrap_select", "step_pass", "select_pass", "refine", "emit",
+                                     "adams"};
 
 struct Rec {
   int stage;
@@ -192,11 +201,38 @@ void select_mark(void* ctx, int id) {
   if (id == 2) g_prof.begin(ST_EMIT, m->s);
 }
 
-scape_status run_select(const Geom& g, const Ws& w, scape_mask_view out, hipStream_t s, bool prof) {
+// Level 1 with the exact fallback: for partitions flagged in the state,
+// count every key (source `src`), bound the capture at the threshold digit,
+// recapture, and redo level 1 on the recaptured keys.
+scape_status run_fallback(const Geom& g, const Ws& w, int src, StatArgs a, bool vec, hipStream_t s) {
+  scape_status st;
+  a.state = w.sel.state;
+  a.only_fb = 1;
+  a.cand = w.sel.cand;
+  a.cnt1 = w.sel.cnt1;
+  a.hist = w.sel.hist;
+  if ((st = hip_check(launch_stat(g, src, kPhaseHist, a, vec, s), "fallback count"))) return st;
+  if ((st = hip_check(launch_level1(g, w.sel, kScanBound, s), "fallback bound"))) return st;
+  if ((st = hip_check(launch_stat(g, src, kPhaseCapture, a, vec, s), "fallback capture"))) return st;
+  return hip_check(launch_level1(g, w.sel, kScanFinal, s), "fallback level 1");
+}
+
+scape_status run_tail(const Geom& g, const Ws& w, scape_mask_view out, hipStream_t s, bool prof) {
   SelectMarks marks{s};
-  hipError_t e = launch_select(g, w.keys, w.hist, w.segcnt, w.cand, w.state, w.tilecnt, out.bits,
-                               out.idx, out.tile_off, s, prof ? select_mark : nullptr, &marks);
+  hipError_t e = launch_select_tail(g, w.sel, out.bits, out.idx, out.tile_off, out.meta, s,
+                                    prof ? select_mark : nullptr, &marks);
   return hip_check(e, "select launch");
+}
+
+// Mask from scratch (no capture bound known): every partition takes the
+// exact two-pass route of the fallback.
+scape_status run_fresh_select(const Geom& g, const Ws& w, int src, const StatArgs& a, bool vec,
+                              scape_mask_view out, hipStream_t s) {
+  scape_status st;
+  if ((st = hip_check(launch_zero_u32(w.sel.hist, (int64_t)g.P * kBins, s), "zero"))) return st;
+  if ((st = hip_check(launch_init_state(g, w.sel.state, s), "init"))) return st;
+  if ((st = run_fallback(g, w, src, a, vec, s))) return st;
+  return run_tail(g, w, out, s, false);
 }
 
 }  // namespace
@@ -239,10 +275,10 @@ scape_status scape_mask_topk(const scape_dims* dims, int64_t k, const float* sta
   if (workspace_bytes < g.ws_total)
     return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
   Ws w = ws_view(g, workspace);
-  const bool vec = (g.n_p % 4 == 0) && aligned16(stat) && aligned16(w.keys);
-  if ((st = hip_check(launch_zero_u32(w.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
-  if ((st = hip_check(launch_keys_from_stat(g, stat, w.keys, w.hist, vec, stream), "keys"))) return st;
-  return run_select(g, w, out, stream, false);
+  const bool vec = (g.n_p % 4 == 0) && aligned16(stat);
+  StatArgs a{};
+  a.stat = stat;
+  return run_fresh_select(g, w, kSrcStat, a, vec, out, stream);
 }
 
 scape_status scape_compress(const scape_dims* dims, int64_t k, const float* grads, float* e,
@@ -252,9 +288,7 @@ scape_status scape_compress(const scape_dims* dims, int64_t k, const float* grad
   if (st) return st;
   if (!grads || !e || !cur.bits || !cur.tile_off || !b) return fail(SCAPE_EINVAL, "null pointer argument");
   const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e);
-  return hip_check(launch_compress(g, grads, e, cur.bits, cur.tile_off, b, false, nullptr, 0.f, 0.f,
-                                   nullptr, nullptr, vec, stream),
-                   "compress");
+  return hip_check(launch_compress(g, grads, e, cur.bits, cur.tile_off, b, stream, vec), "compress");
 }
 
 scape_status scape_reduce_sparse(const scape_dims* dims, int64_t k, const float* b, float* b_bar,
@@ -299,33 +333,64 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   Ws w = ws_view(g, workspace);
   const scape_mask_view cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
   const scape_mask_view nxt = slot_view(g, mask_blob, (int)(step & 1));
-  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m) &&
-                   aligned16(w.keys);
+  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m);
   const float b1 = betas.beta1, b2 = betas.beta2;
   const float c1 = 1.0f - b1, c2 = 1.0f - b2;
   const bool prof = g_prof.on;
+  StatArgs a{};
+  a.m = m;
+  a.grads = grads;
+  a.e = e;
+  a.b = w.b;
+  a.mold = kFuseAdams ? w.mold : nullptr;  // m is updated before the selection only when fused
+  a.bits = cur.bits;
+  a.tile_off = cur.tile_off;
+  a.b1 = b1;
+  a.c1 = c1;
 
   if (step == 1) {  // bootstrap: M_1 = top-k of the step-1 statistic
     g_prof.begin(ST_BOOT, stream);
-    if ((st = hip_check(launch_zero_u32(w.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
-    if ((st = hip_check(launch_keys_from_state(g, m, grads, e, b1, c1, w.keys, w.hist, vec, stream),
-                        "bootstrap keys")))
-      return st;
-    if ((st = run_select(g, w, cur, stream, false))) return st;
+    StatArgs boot = a;
+    boot.mold = nullptr;
+    if ((st = run_fresh_select(g, w, kSrcState, boot, vec, cur, stream))) return st;
   }
-  g_prof.begin(ST_COMPRESS, stream);
-  if ((st = hip_check(launch_zero_u32(w.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
-  if ((st = hip_check(launch_compress(g, grads, e, cur.bits, cur.tile_off, w.b, true, m, b1, c1,
-                                      w.keys, w.hist, vec, stream),
-                      "compress")))
+  g_prof.begin(ST_PASS, stream);
+  if ((st = hip_check(launch_zero_u32(w.sel.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
+  StepArgs sa{};
+  sa.grads = grads;
+  sa.e = e;
+  sa.bits = cur.bits;
+  sa.tile_off = cur.tile_off;
+  sa.b = w.b;
+  sa.m = m;
+  sa.v = kFuseAdams ? v : nullptr;
+  sa.w = kFuseAdams ? params : nullptr;
+  sa.mold = kFuseAdams ? w.mold : nullptr;
+  sa.b1 = b1;
+  sa.b2 = b2;
+  sa.c1 = c1;
+  sa.c2 = c2;
+  sa.ibc1 = bias_reciprocal(b1, step);
+  sa.ibc2 = bias_reciprocal(b2, step);
+  sa.eps = betas.eps;
+  sa.wd = betas.weight_decay;
+  sa.lr = lr;
+  sa.lo = cur.meta + g.P;
+  sa.cand = w.sel.cand;
+  sa.cnt1 = w.sel.cnt1;
+  sa.hist = w.sel.hist;
+  if ((st = hip_check(launch_step_pass(g, sa, vec && aligned16(params) && aligned16(v), stream), "step pass")))
     return st;
   g_prof.begin(ST_SELECT, stream);
-  if ((st = run_select(g, w, nxt, stream, prof))) return st;
-  g_prof.begin(ST_ADAMS, stream);
-  st = hip_check(launch_reduce_adams(g, w.b, cur.idx, params, m, v, b1, b2, c1, c2,
-                                     bias_reciprocal(b1, step), bias_reciprocal(b2, step), betas.eps,
-                                     betas.weight_decay, lr, stream),
-                 "reduce_adams");
+  if ((st = hip_check(launch_level1(g, w.sel, kScanCheck, stream), "level 1"))) return st;
+  if ((st = run_fallback(g, w, kSrcMasked, a, vec, stream))) return st;
+  if ((st = run_tail(g, w, nxt, stream, prof))) return st;
+  if (!kFuseAdams) {
+    g_prof.begin(ST_ADAMS, stream);
+    st = hip_check(launch_reduce_adams(g, w.b, cur.idx, params, m, v, b1, b2, c1, c2, sa.ibc1, sa.ibc2,
+                                       betas.eps, betas.weight_decay, lr, stream),
+                   "reduce_adams");
+  }
   g_prof.end();
   return st;
 }

@@ -1,14 +1,24 @@
-// Streaming passes over the flat buffer: the error-feedback compression of
-// every worker's gradient at the current mask (SCAPE paper §II-B, at the
-// shared index set of the technical summary §2), fused with the owner's
-// first-moment statistic and the level-1 histogram of its keys; and the
-// statistic-only passes used by the mask call and the step-1 bootstrap.
+// Streaming passes over the flat buffer.
+//
+//  * compress_kernel: error-feedback compression of every worker's gradient
+//    at the current mask (SCAPE paper §II-B, at the shared index set of the
+//    technical summary §2), fused with the owner's first-moment statistic
+//    (technical summary §2, lagged mask built from first-moment statistics)
+//    and the capture of the selection candidates: owner keys at or above a
+//    per-partition bound `lo` are written, as unique (key, index)
+//    composites, to a per-tile candidate slot, and a level-1 histogram of
+//    the captured keys is kept.
+//  * stat_kernel: the statistic alone, for the step-1 bootstrap (from
+//    m, g^o, e^o), for scape_mask_topk (from a given array), and for the
+//    exact fallback when a partition captured fewer than k candidates (from
+//    m and the compressed state e', b of the owner).  Phase HIST counts every
+//    key; phase CAPTURE captures keys at or above the partition's bound.
 //
 // Work decomposition: grid (G, P).  Block (b, p) walks tiles b, b+G, ... of
 // partition p; a tile is 4096 elements = 64 mask words; thread `tid` owns
-// the 4 consecutive elements 4*tid .. 4*tid+3 of each 1024-element chunk, so
-// every global access is a 16-byte-per-lane coalesced load or store when the
-// layout allows vector access (n_p % 4 == 0 and 16-byte aligned bases).
+// elements 4*tid .. 4*tid+3 of each 1024-element chunk, so every global
+// access is a 16-byte-per-lane coalesced load or store when vector access
+// is possible (n_p % 4 == 0 and 16-byte aligned bases).
 #include "scape_internal.h"
 
 #pragma clang fp contract(off)
@@ -22,9 +32,18 @@ __device__ __forceinline__ uint32_t stat_key(float m, float a, float b1, float c
   return __float_as_uint(s) & 0x7fffffffu;
 }
 
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Streaming accesses are non-temporal: every byte of g, e and m is touched
+// once per pass, and keeping them out of the caches leaves those to the
+// scattered w / m / v updates and the candidate slots.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void load4(const float* p, int64_t lj, int64_t n_p, bool vec, float out[4]) {
   if (vec) {
-    const float4 v = *reinterpret_cast<const float4*>(p + lj);
+    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + lj));
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   } else {
 #pragma unroll
@@ -34,17 +53,8 @@ __device__ __forceinline__ void load4(const float* p, int64_t lj, int64_t n_p, b
 
 __device__ __forceinline__ void store4(float* p, int64_t lj, int64_t n_p, bool vec, const float v[4]) {
   if (vec) {
-    *reinterpret_cast<float4*>(p + lj) = make_float4(v[0], v[1], v[2], v[3]);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lj + q < n_p) p[lj + q] = v[q];
-  }
-}
-
-__device__ __forceinline__ void store4u(uint32_t* p, int64_t lj, int64_t n_p, bool vec, const uint32_t v[4]) {
-  if (vec) {
-    *reinterpret_cast<uint4*>(p + lj) = make_uint4(v[0], v[1], v[2], v[3]);
+    const v4f t = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f*>(p + lj));
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -63,51 +73,8 @@ __device__ __forceinline__ void hist_merge(const uint32_t* sh, uint32_t* gh) {
   }
 }
 
-// MODE 0: key from stat[].  MODE 1: key from b1*m + c1*(g^o + e^o).
-template <int MODE, bool VEC>
-__global__ void __launch_bounds__(kThreads)
-keys_kernel(Geom g, const float* __restrict__ stat, const float* __restrict__ m,
-            const float* __restrict__ grads, const float* __restrict__ e, float b1, float c1,
-            uint32_t* __restrict__ keys, uint32_t* __restrict__ hist) {
-  __shared__ uint32_t sh[kBins];
-  hist_zero(sh);
-  __syncthreads();
-  const int p = blockIdx.y;
-  const int64_t pbase = (int64_t)p * g.n_p;
-  const int o = (int)(((int64_t)p * g.K) / g.P);
-  const float* gp = grads + (int64_t)o * g.n + pbase;
-  const float* ep = e + (int64_t)o * g.n + pbase;
-  for (int64_t t = blockIdx.x; t < g.tpp; t += gridDim.x) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t lj = t * kTile + c * 1024 + 4 * threadIdx.x;
-      if (lj >= g.n_p) break;
-      uint32_t kk[4];
-      if (MODE == 0) {
-        float s[4];
-        load4(stat + pbase, lj, g.n_p, VEC, s);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kk[q] = __float_as_uint(s[q]) & 0x7fffffffu;
-      } else {
-        float mm[4], gg[4], ee[4];
-        load4(m + pbase, lj, g.n_p, VEC, mm);
-        load4(gp, lj, g.n_p, VEC, gg);
-        load4(ep, lj, g.n_p, VEC, ee);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kk[q] = stat_key(mm[q], gg[q] + ee[q], b1, c1);
-      }
-      store4u(keys + pbase, lj, g.n_p, VEC, kk);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (VEC || lj + q < g.n_p) atomicAdd(&sh[kk[q] >> kL1Shift], 1u);
-    }
-  }
-  __syncthreads();
-  hist_merge(sh, hist + (int64_t)p * kBins);
-}
-
 // Loads the tile's 64 mask words into LDS with their exclusive popcount
-// prefix (one wave scans).
+// prefix (wave 0 scans).
 __device__ __forceinline__ void load_tile_words(const uint64_t* __restrict__ bits, int64_t wbase,
                                                 int64_t wpp, int64_t t, uint64_t* sw, uint32_t* spre) {
   if (threadIdx.x < kWordsPerTile) {
@@ -115,7 +82,6 @@ __device__ __forceinline__ void load_tile_words(const uint64_t* __restrict__ bit
     const uint64_t word = (w < wpp) ? bits[wbase + w] : 0ull;
     sw[threadIdx.x] = word;
     uint32_t c = (uint32_t)__popcll(word);
-    // inclusive scan across the 64 lanes of wave 0
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const uint32_t y = __shfl_up(c, d, 64);
@@ -125,142 +91,361 @@ __device__ __forceinline__ void load_tile_words(const uint64_t* __restrict__ bit
   }
 }
 
-template <bool STAT, bool VEC>
-__global__ void __launch_bounds__(kThreads)
+// Wave-cooperative capture of the lane's 4 keys (elements lj .. lj+3):
+// flagged keys are appended to the tile's candidate slot at positions
+// handed out by the LDS counter `tcnt`, and counted in the LDS histogram.
+// Every lane of the wave must call this (ballots and a lane-0 broadcast).
+__device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], int64_t lj,
+                                         uint32_t idx_mask, uint64_t* __restrict__ slot,
+                                         uint32_t* tcnt, uint32_t* sh) {
+  uint64_t B[4];
+  uint32_t pre[4], tot = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    B[q] = __ballot(f[q]);
+    pre[q] = tot;
+    tot += (uint32_t)__popcll(B[q]);
+  }
+  if (tot == 0) return;  // wave-uniform
+  uint32_t base = 0;
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(tcnt, tot);
+  base = __shfl(base, 0, 64);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (f[q]) {
+      const uint32_t j = (uint32_t)(lj + q);
+      slot[base + pre[q] + mbcnt(B[q])] = ((uint64_t)kk[q] << 32) | (uint64_t)(idx_mask - j);
+      atomicAdd(&sh[kk[q] >> kL1Shift], 1u);
+    }
+  }
+}
+
+struct AdamsC {
+  float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, invK;
+};
+
+// STEP false: error-feedback compression only (the component call).
+// STEP true: the fused step pass.  Besides compressing, it keeps each masked
+// element's worker sum S = ((a^0 + a^1) + ...) + a^{K-1} in registers (the
+// single synchronised buffer of the technical summary §2: on one device all
+// K workers' entries of an element are in the same thread), applies AdamS
+// there with x = S * fp32(1/K) (SCAPE paper §II-C eq. (2)), and saves the
+// pre-update m of masked elements to mold[rank] for the exact fallback;
+// the owner's statistic reads m before its update.
+// Chunks of 1024 elements processed together per pass over the workers:
+// the tile's 4 chunks are walked in groups of kChunkGroup, so that the
+// registers held across the worker loop (m, the worker sum, the loads in
+// flight) stay within an occupancy of 4+ waves per SIMD.
+constexpr int kChunkGroup = 2;
+// Minimum waves per SIMD the step pass is compiled for (caps its VGPRs at
+// 128, which the chunk group of 2 fits without spilling).
+constexpr int kStepMinWaves = 4;
+
+template <bool STEP, bool ADAMS, bool VEC>
+__global__ void __launch_bounds__(kThreads, kStepMinWaves)
 compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
-                float* __restrict__ b, const float* __restrict__ m, float b1, float c1,
-                uint32_t* __restrict__ keys, uint32_t* __restrict__ hist) {
+                float* __restrict__ b, float* __restrict__ m, float* __restrict__ v,
+                float* __restrict__ w, float* __restrict__ mold, AdamsC ac,
+                const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
+                uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist) {
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
-  __shared__ uint32_t sh[STAT ? kBins : 1];
-  if (STAT) hist_zero(sh);
+  __shared__ uint32_t sh[STEP ? kBins : 1];
+  __shared__ uint32_t tcnt;
+  if (STEP) hist_zero(sh);
   const int p = blockIdx.y;
   const int64_t pbase = (int64_t)p * g.n_p;
   const int64_t wbase = (int64_t)p * g.wpp;
   const int64_t pk = (int64_t)g.P * g.k;
   const int owner = (int)(((int64_t)p * g.K) / g.P);
+  const uint32_t lo = STEP ? lo_in[p] : 0u;
   const int lane16 = threadIdx.x & 15;
   const int sh4 = 4 * lane16;
   const uint64_t below = (sh4 == 0) ? 0ull : ((1ull << sh4) - 1ull);
 
   for (int64_t t = blockIdx.x; t < g.tpp; t += gridDim.x) {
-    __syncthreads();  // previous tile's words no longer in use
+    __syncthreads();  // previous tile's LDS words and counter no longer in use
     load_tile_words(bits, wbase, g.wpp, t, sw, spre);
+    if (threadIdx.x == 0) tcnt = 0;
     __syncthreads();
     const int64_t rbase = (int64_t)p * g.k + tile_off[(int64_t)p * g.tpp + t];
     const int64_t rend = (int64_t)(p + 1) * g.k;
+    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
 
-    // Per chunk: the lane's 4 mask bits and the rank of its first element.
-    uint32_t nib[4];
-    int64_t rank0[4];
+    for (int cg = 0; cg < 4; cg += kChunkGroup) {
+      uint32_t nib[kChunkGroup];
+      int64_t rank0[kChunkGroup], lj[kChunkGroup];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int q = c * 16 + (threadIdx.x >> 4);
-      const uint64_t word = sw[q];
-      nib[c] = (uint32_t)(word >> sh4) & 0xfu;
-      rank0[c] = rbase + spre[q] + (uint32_t)__popcll(word & below);
-    }
-
-    for (int i = 0; i < g.K; ++i) {
-      const float* gi = grads + (int64_t)i * g.n + pbase;
-      float* ei = e + (int64_t)i * g.n + pbase;
-      float* bi = b + (int64_t)i * pk;
-      float ga[4][4], ea[4][4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t lj = t * kTile + c * 1024 + 4 * threadIdx.x;
-        if (lj < g.n_p) {
-          load4(gi, lj, g.n_p, VEC, ga[c]);
-          load4(ei, lj, g.n_p, VEC, ea[c]);
-        }
+      for (int u = 0; u < kChunkGroup; ++u) {
+        const int c = cg + u;
+        const int q = c * 16 + (threadIdx.x >> 4);
+        const uint64_t word = sw[q];
+        nib[u] = (uint32_t)(word >> sh4) & 0xfu;
+        rank0[u] = rbase + spre[q] + (uint32_t)__popcll(word & below);
+        lj[u] = t * kTile + c * 1024 + 4 * threadIdx.x;
       }
-      const bool own = STAT && (i == owner);
-      float ma[4][4];
-      if (own) {
+      float ma[kChunkGroup][4], S[kChunkGroup][4];
+      (void)S;
+      if (STEP) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int64_t lj = t * kTile + c * 1024 + 4 * threadIdx.x;
-          if (lj < g.n_p) load4(m + pbase, lj, g.n_p, VEC, ma[c]);
-        }
+        for (int u = 0; u < kChunkGroup; ++u)
+          if (lj[u] < g.n_p) load4(m + pbase, lj[u], g.n_p, VEC, ma[u]);
       }
+      for (int i = 0; i < g.K; ++i) {
+        const float* gi = grads + (int64_t)i * g.n + pbase;
+        float* ei = e + (int64_t)i * g.n + pbase;
+        float* bi = b + (int64_t)i * pk;
+        float ga[kChunkGroup][4], ea[kChunkGroup][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t lj = t * kTile + c * 1024 + 4 * threadIdx.x;
-        if (lj >= g.n_p) continue;
-        float a[4], eo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          a[q] = ga[c][q] + ea[c][q];
-          eo[q] = ((nib[c] >> q) & 1u) ? 0.0f : a[q];
+        for (int u = 0; u < kChunkGroup; ++u) {
+          if (lj[u] < g.n_p) {
+            load4(gi, lj[u], g.n_p, VEC, ga[u]);
+            load4(ei, lj[u], g.n_p, VEC, ea[u]);
+          }
         }
-        store4(ei, lj, g.n_p, VEC, eo);
-        if (nib[c]) {
-          // ranks stay inside partition p's k entries for any mask with k
-          // bits per partition; the bound keeps a malformed mask in bounds
-          int64_t r = rank0[c];
+        const bool own = STEP && (i == owner);  // block-uniform
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if ((nib[c] >> q) & 1u) {
-              if (r < rend) bi[r] = a[q];
-              ++r;
+        for (int u = 0; u < kChunkGroup; ++u) {
+          float a[4];
+          if (lj[u] < g.n_p) {
+            float eo[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              a[q] = ga[u][q] + ea[u][q];
+              eo[q] = ((nib[u] >> q) & 1u) ? 0.0f : a[q];
             }
-        }
-        if (own) {
-          uint32_t kk[4];
+            store4(ei, lj[u], g.n_p, VEC, eo);
+            if (nib[u]) {
+              // ranks stay inside partition p's k entries for any mask with
+              // k bits per partition; the bound keeps a malformed mask in bounds
+              int64_t r = rank0[u];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) kk[q] = stat_key(ma[c][q], a[q], b1, c1);
-          store4u(keys + pbase, lj, g.n_p, VEC, kk);
+              for (int q = 0; q < 4; ++q)
+                if ((nib[u] >> q) & 1u) {
+                  if (r < rend) bi[r] = a[q];
+                  ++r;
+                  if (ADAMS) S[u][q] = (i == 0) ? a[q] : S[u][q] + a[q];
+                }
+            }
+          }
+          if (own) {  // all lanes of the wave take part in the capture
+            uint32_t kk[4];
+            bool f[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (VEC || lj + q < g.n_p) atomicAdd(&sh[kk[q] >> kL1Shift], 1u);
+            for (int q = 0; q < 4; ++q) {
+              const bool valid = lj[u] + q < g.n_p;
+              kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
+              f[q] = valid && kk[q] >= lo;
+            }
+            capture4(kk, f, lj[u], g.idx_mask, slot, &tcnt, sh);
+          }
         }
       }
+      if (ADAMS) {
+        // AdamS at the group's masked elements: gather w, then update.
+#pragma unroll
+        for (int u = 0; u < kChunkGroup; ++u) {
+          if (!nib[u]) continue;
+          float wo[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (((nib[u] >> q) & 1u) && lj[u] + q < g.n_p) wo[q] = w[pbase + lj[u] + q];
+          int64_t r = rank0[u];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (!((nib[u] >> q) & 1u) || lj[u] + q >= g.n_p) continue;
+            const float x = S[u][q] * ac.invK;
+            const float mo = ma[u][q];
+            const float mn = (ac.b1 * mo) + (ac.c1 * x);
+            const float vn = (ac.b2 * (mo * mo)) + (ac.c2 * (x * x));
+            const float mh = mn * ac.ibc1;
+            const float vh = vn * ac.ibc2;
+            const float d = sqrtf(vh) + ac.eps;
+            const float uu = mh / d;
+            const float wn = wo[q] - (ac.lr * (uu + (ac.wd * wo[q])));
+            const int64_t j = pbase + lj[u] + q;
+            m[j] = mn;
+            v[j] = vn;
+            w[j] = wn;
+            if (r < rend) mold[r] = mo;
+            ++r;
+          }
+        }
+      }
+    }
+    if (STEP) {
+      __syncthreads();
+      if (threadIdx.x == 0) cnt1[(int64_t)p * g.tpp + t] = tcnt;
     }
   }
-  if (STAT) {
+  if (STEP) {
     __syncthreads();
     hist_merge(sh, hist + (int64_t)p * kBins);
   }
 }
 
-}  // namespace
+// SRC 0: key from stat[].  SRC 1: from b1*m + c1*(g^o + e^o).  SRC 2: from
+// b1*m + c1*a^o with a^o rebuilt from the compressed state: b^o at the
+// element's rank on the mask, e'^o off it.
+// PHASE 0 (HIST): histogram of every key.  PHASE 1 (CAPTURE): capture keys
+// >= state.lo_fb.  With only_fb, partitions whose fallback flag is clear
+// are skipped.
+template <int SRC, int PHASE, bool VEC>
+__global__ void __launch_bounds__(kThreads)
+stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float* __restrict__ stat,
+            const float* __restrict__ m, const float* __restrict__ grads, const float* __restrict__ e,
+            const float* __restrict__ b, const float* __restrict__ mold, const uint64_t* __restrict__ bits,
+            const uint32_t* __restrict__ tile_off, float b1, float c1, uint64_t* __restrict__ cand,
+            uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist) {
+  __shared__ uint64_t sw[kWordsPerTile];
+  __shared__ uint32_t spre[kWordsPerTile];
+  __shared__ uint32_t sh[kBins];
+  __shared__ uint32_t tcnt;
+  const int p = blockIdx.y;
+  const PartSel st = state[p];
+  if (only_fb && !st.fb) return;  // block-uniform
+  hist_zero(sh);
+  const int64_t pbase = (int64_t)p * g.n_p;
+  const int64_t wbase = (int64_t)p * g.wpp;
+  const int64_t pk = (int64_t)g.P * g.k;
+  const int o = (int)(((int64_t)p * g.K) / g.P);
+  const float* go = grads + (int64_t)o * g.n + pbase;
+  const float* eo = e + (int64_t)o * g.n + pbase;
+  const float* bo = b + (int64_t)o * pk;
+  const uint32_t lo = st.lo_fb;
+  const int lane16 = threadIdx.x & 15;
+  const int sh4 = 4 * lane16;
+  const uint64_t below = (sh4 == 0) ? 0ull : ((1ull << sh4) - 1ull);
 
-hipError_t launch_keys_from_stat(const Geom& g, const float* stat, uint32_t* keys, uint32_t* hist,
-                                 bool vec, hipStream_t s) {
-  dim3 grid(g.G, g.P);
-  if (vec)
-    keys_kernel<0, true><<<grid, kThreads, 0, s>>>(g, stat, nullptr, nullptr, nullptr, 0.f, 0.f, keys, hist);
-  else
-    keys_kernel<0, false><<<grid, kThreads, 0, s>>>(g, stat, nullptr, nullptr, nullptr, 0.f, 0.f, keys, hist);
-  return hipGetLastError();
+  for (int64_t t = blockIdx.x; t < g.tpp; t += gridDim.x) {
+    __syncthreads();
+    if (SRC == 2) load_tile_words(bits, wbase, g.wpp, t, sw, spre);
+    if (threadIdx.x == 0) tcnt = 0;
+    __syncthreads();
+    const int64_t rbase = (SRC == 2) ? (int64_t)p * g.k + tile_off[(int64_t)p * g.tpp + t] : 0;
+    const int64_t rend = (int64_t)(p + 1) * g.k;
+    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t lj = t * kTile + c * 1024 + 4 * threadIdx.x;
+      uint32_t kk[4] = {0u, 0u, 0u, 0u};
+      if (lj < g.n_p) {
+        if (SRC == 0) {
+          float s[4];
+          load4(stat + pbase, lj, g.n_p, VEC, s);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) kk[q] = __float_as_uint(s[q]) & 0x7fffffffu;
+        } else {
+          float mm[4], a[4];
+          load4(m + pbase, lj, g.n_p, VEC, mm);
+          if (SRC == 1) {
+            float gg[4], ee[4];
+            load4(go, lj, g.n_p, VEC, gg);
+            load4(eo, lj, g.n_p, VEC, ee);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] = gg[q] + ee[q];
+          } else {
+            load4(eo, lj, g.n_p, VEC, a);
+            const int qw = c * 16 + (threadIdx.x >> 4);
+            const uint64_t word = sw[qw];
+            const uint32_t nib = (uint32_t)(word >> sh4) & 0xfu;
+            if (nib) {
+              int64_t r = rbase + spre[qw] + (uint32_t)__popcll(word & below);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if ((nib >> q) & 1u) {
+                  if (r < rend) {
+                    a[q] = bo[r];
+                    if (mold) mm[q] = mold[r];
+                  }
+                  ++r;
+                }
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) kk[q] = stat_key(mm[q], a[q], b1, c1);
+        }
+      }
+      if (PHASE == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (lj + q < g.n_p) atomicAdd(&sh[kk[q] >> kL1Shift], 1u);
+      } else {
+        bool f[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f[q] = (lj + q < g.n_p) && kk[q] >= lo;
+        capture4(kk, f, lj, g.idx_mask, slot, &tcnt, sh);
+      }
+    }
+    if (PHASE == 1) {
+      __syncthreads();
+      if (threadIdx.x == 0) cnt1[(int64_t)p * g.tpp + t] = tcnt;
+    }
+  }
+  __syncthreads();
+  hist_merge(sh, hist + (int64_t)p * kBins);
 }
 
-hipError_t launch_keys_from_state(const Geom& g, const float* m, const float* grads, const float* e,
-                                  float b1, float c1, uint32_t* keys, uint32_t* hist, bool vec,
-                                  hipStream_t s) {
+template <int SRC, int PHASE>
+void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
   dim3 grid(g.G, g.P);
   if (vec)
-    keys_kernel<1, true><<<grid, kThreads, 0, s>>>(g, nullptr, m, grads, e, b1, c1, keys, hist);
+    stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
+                                                           a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
   else
-    keys_kernel<1, false><<<grid, kThreads, 0, s>>>(g, nullptr, m, grads, e, b1, c1, keys, hist);
+    stat_kernel<SRC, PHASE, false><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
+                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
+}
+
+}  // namespace
+
+hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, bool vec, hipStream_t s) {
+  if (src == kSrcStat && phase == kPhaseHist) launch_stat_t<kSrcStat, kPhaseHist>(g, a, vec, s);
+  else if (src == kSrcStat) launch_stat_t<kSrcStat, kPhaseCapture>(g, a, vec, s);
+  else if (src == kSrcState && phase == kPhaseHist) launch_stat_t<kSrcState, kPhaseHist>(g, a, vec, s);
+  else if (src == kSrcState) launch_stat_t<kSrcState, kPhaseCapture>(g, a, vec, s);
+  else if (phase == kPhaseHist) launch_stat_t<kSrcMasked, kPhaseHist>(g, a, vec, s);
+  else launch_stat_t<kSrcMasked, kPhaseCapture>(g, a, vec, s);
   return hipGetLastError();
 }
 
 hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
-                           const uint32_t* tile_off, float* b, bool stat, const float* m, float b1,
-                           float c1, uint32_t* keys, uint32_t* hist, bool vec, hipStream_t s) {
+                           const uint32_t* tile_off, float* b, hipStream_t s, bool vec) {
   dim3 grid(g.G, g.P);
-  if (stat) {
+  AdamsC ac{};
+  if (vec)
+    compress_kernel<false, false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
+                                                                  nullptr, nullptr, ac, nullptr, nullptr, nullptr,
+                                                                  nullptr);
+  else
+    compress_kernel<false, false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr,
+                                                                   nullptr, nullptr, nullptr, ac, nullptr, nullptr,
+                                                                   nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s) {
+  dim3 grid(g.G, g.P);
+  AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
+  if (a.w != nullptr) {  // with AdamS fused
     if (vec)
-      compress_kernel<true, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, m, b1, c1, keys, hist);
+      compress_kernel<true, true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
+                                                                  a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1,
+                                                                  a.hist);
     else
-      compress_kernel<true, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, m, b1, c1, keys, hist);
+      compress_kernel<true, true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
+                                                                   a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1,
+                                                                   a.hist);
   } else {
     if (vec)
-      compress_kernel<false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, 0.f, 0.f, nullptr, nullptr);
+      compress_kernel<true, false, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
+                                                                   nullptr, nullptr, nullptr, ac, a.lo, a.cand,
+                                                                   a.cnt1, a.hist);
     else
-      compress_kernel<false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, 0.f, 0.f, nullptr, nullptr);
+      compress_kernel<true, false, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b,
+                                                                    a.m, nullptr, nullptr, nullptr, ac, a.lo,
+                                                                    a.cand, a.cnt1, a.hist);
   }
   return hipGetLastError();
 }

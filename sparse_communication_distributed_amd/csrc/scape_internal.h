@@ -18,9 +18,25 @@ constexpr int kBins = 1 << kDigitBits;
 constexpr int kL1Shift = 19;
 // Target number of blocks for streaming passes (>> 256 CUs).
 constexpr int kTargetBlocks = 4096;
-// Blocks per partition for the passes over candidate lists.
-constexpr int kRefineBlocks = 16;
+// Blocks per partition for the passes over compacted candidate lists (one
+// wave per group of 64 tiles), at most this many.
+constexpr int kRefineBlocks = 64;
+// Tiles each wave of the candidate select pass walks.
+constexpr int kSelectTilesPerWave = 8;
 constexpr int kThreads = 256;
+
+// Statistic sources and phases of stat_kernel.
+constexpr int kSrcStat = 0;    // key of a given array
+constexpr int kSrcState = 1;   // b1*m + c1*(g^o + e^o), before compression
+constexpr int kSrcMasked = 2;  // b1*m + c1*a^o, a^o rebuilt from e' and b^o
+constexpr int kPhaseHist = 0;
+constexpr int kPhaseCapture = 1;
+
+// Modes of the level scan.
+constexpr int kScanLevel = 0;  // a later level, on candidates
+constexpr int kScanCheck = 1;  // level 1 on captured keys; flags a fallback if fewer than k
+constexpr int kScanBound = 2;  // fallback: level 1 on all keys -> capture bound
+constexpr int kScanFinal = 3;  // fallback: level 1 on the recaptured keys
 
 // Per-partition state of the threshold search.  The search runs on the
 // 64-bit composite  c = (key << 32) | (idx_mask - local_index),  unique per
@@ -30,12 +46,23 @@ constexpr int kThreads = 256;
 // once the search ends.
 struct PartSel {
   uint64_t prefix;
-  uint64_t mask;    // bits of prefix that are determined
-  uint32_t r;       // rank still needed among composites matching prefix
-  uint32_t done;    // 1: every composite matching prefix is selected
-  uint32_t bin1;    // level-1 digit of the threshold
-  uint32_t fault;   // 1: rank not found (internal invariant broken)
+  uint64_t mask;   // bits of prefix that are determined
+  uint32_t r;      // rank still needed among composites matching prefix
+  uint32_t done;   // 1: every composite matching prefix is selected
+  uint32_t bin1;   // level-1 digit of the threshold
+  uint32_t fault;  // bit 0: rank not found; bit 1: emitted count != k
+  uint32_t fb;     // 1: the captured candidates cannot hold the top k
+  uint32_t lo_fb;  // capture bound of the fallback (lowest key of bin1)
+  uint32_t kth;      // smallest selected key (the k-th largest key)
+  uint32_t c1;       // captured keys in the level-1 threshold bin
+  uint32_t lo_next;  // capture bound proposed for the next step
+  uint32_t pad;
 };
+
+// The next step's capture bound sits where this step counted
+// kCaptureMargin * k keys at or above it (first on the level-1 digit, then
+// refined inside the threshold bin on the level-2 digit).
+constexpr double kCaptureMargin = 1.25;
 
 struct Level {
   int shift;  // bit position of the digit in the composite
@@ -48,43 +75,81 @@ struct Geom {
   int64_t wpp;        // mask words per partition
   int64_t tpp;        // tiles per partition
   int G;              // blocks per partition of the streaming passes
-  int64_t seg_tiles;  // tiles handled by one streaming block (upper bound)
-  int64_t seg_cap;    // candidate capacity of one block segment
   int R;              // blocks per partition over candidate lists
   int idx_bits;       // bits of (n_p - 1), >= 1
   uint32_t idx_mask;  // (1 << idx_bits) - 1
-  int nlevels;        // levels after level 1
+  int nlevels;        // levels after level 1 (level 2 first)
   Level levels[8];
   // mask slot: offsets inside one slot, slot size
-  size_t off_bits, off_idx, off_toff, slot_bytes;
+  size_t off_bits, off_idx, off_toff, off_meta, slot_bytes;
   // workspace offsets and total
-  size_t ws_keys, ws_b, ws_hist, ws_segcnt, ws_cand, ws_state, ws_tilecnt, ws_total;
+  size_t ws_b, ws_mold, ws_hist, ws_cand, ws_cnt1, ws_cnt2, ws_state, ws_tilecnt, ws_total;
 };
 
 // Returns false if dims/k are outside the limits.
 bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g);
 
+struct StatArgs {
+  const PartSel* state;
+  int only_fb;
+  const float* stat;
+  const float* m;
+  const float* grads;
+  const float* e;
+  const float* b;
+  const float* mold;  // m_{t-1} of the masked elements, by rank (SRC masked)
+  const uint64_t* bits;
+  const uint32_t* tile_off;
+  float b1, c1;
+  uint64_t* cand;
+  uint32_t* cnt1;
+  uint32_t* hist;
+};
+
+// Buffers of the selection pipeline (workspace views).
+struct SelectBufs {
+  uint32_t* hist;
+  uint64_t* cand;
+  uint32_t* cnt1;
+  uint32_t* cnt2;
+  PartSel* state;
+  uint32_t* tilecnt;
+};
+
 // ---- launch wrappers (each returns hipGetLastError() of its launches) ----
 
-// Keys + level-1 histogram from a statistic array: key = bits(stat) & 0x7fffffff.
-hipError_t launch_keys_from_stat(const Geom& g, const float* stat, uint32_t* keys, uint32_t* hist,
-                                 bool vec, hipStream_t s);
-// Keys + level-1 histogram from the statistic b1*m + c1*(g^o + e^o) (step-1 bootstrap).
-hipError_t launch_keys_from_state(const Geom& g, const float* m, const float* grads, const float* e,
-                                  float b1, float c1, uint32_t* keys, uint32_t* hist, bool vec,
-                                  hipStream_t s);
-// Error-feedback compression at a mask; optionally fused owner statistic.
-hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
-                           const uint32_t* tile_off, float* b, bool stat, const float* m, float b1,
-                           float c1, uint32_t* keys, uint32_t* hist, bool vec, hipStream_t s);
+// Arguments of the fused step pass.
+struct StepArgs {
+  const float* grads;
+  float* e;
+  const uint64_t* bits;      // M_t
+  const uint32_t* tile_off;  // M_t
+  float* b;                  // [K][P*k] sparse buffers
+  float *m, *v, *w;           // w == nullptr: no AdamS in this pass
+  float* mold;               // [P*k] pre-update m of the masked elements
+  float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr;
+  const uint32_t* lo;        // [P] capture bounds
+  uint64_t* cand;
+  uint32_t* cnt1;
+  uint32_t* hist;
+};
 
-// Selection pipeline: level-1 threshold from hist, select pass, candidate
-// levels, marking and emission of idx / tile_off.  hist must hold the
-// level-1 histogram of keys; it is left zeroed.
-hipError_t launch_select(const Geom& g, const uint32_t* keys, uint32_t* hist, uint32_t* segcnt,
-                         uint64_t* cand, PartSel* state, uint32_t* tilecnt, uint64_t* bits,
-                         uint32_t* idx, uint32_t* tile_off, hipStream_t s,
-                         void (*mark)(void*, int), void* mark_ctx);
+hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, bool vec, hipStream_t s);
+// Error-feedback compression at a mask (the component call).
+hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
+                           const uint32_t* tile_off, float* b, hipStream_t s, bool vec);
+// The fused step pass: compression, owner statistic with candidate capture,
+// worker-sum reduction and AdamS at M_t.
+hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s);
+
+hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
+hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s);
+// From level-1 digits to the mask: candidate select pass (writes every mask
+// word), the later levels, marking, tile counts, offsets, index list and the
+// slot's threshold record.
+hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits, uint32_t* idx,
+                              uint32_t* tile_off, uint32_t* meta_out, hipStream_t s,
+                              void (*mark)(void*, int), void* mark_ctx);
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s);
 

@@ -5,24 +5,23 @@
 // Method: radix select on the unique 64-bit composite
 //     c = (key << 32) | (idx_mask - local_index)
 // so that "the k largest composites" is exactly "the k largest keys, ties to
-// the lower index".  Level 1 (key bits 30..19) is histogrammed by the
-// streaming pass that produces the keys.  The select pass then reads every
-// key once: keys above the level-1 threshold digit are selected outright and
-// written as mask words (one ballot per 64 elements), keys equal to it are
-// compacted as composites into per-block candidate segments (no global
-// atomics).  The remaining levels (key bits 18..7, 6..0, then the index
-// bits) run on the candidates only; the last step sets the candidates'
-// bits.  Emission turns the words into the ascending index list.
+// the lower index".  The streaming pass that produces the keys captures,
+// per tile, every key at or above a bound `lo` together with a level-1
+// histogram (key bits 30..19) of the captured keys.  If a partition captured
+// at least k keys, its top k lie among the captures; otherwise an exact
+// fallback recounts all its keys to find the level-1 digit and recaptures
+// from there.  The candidate select pass then reads only the captures:
+// digits above the threshold digit are selected and written as whole mask
+// words, the threshold digit's captures are compacted in place and
+// histogrammed on the next digit.  The remaining levels (key bits 6..0, then
+// the index bits) run on those few; marking sets their bits; emission turns
+// the words into the ascending index list and per-tile offsets.
 #include "scape_internal.h"
 
 namespace scape {
 namespace {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
-
-__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 // Exclusive scan over a block of kThreads (4 waves); `wtot` is LDS [4].
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
@@ -46,30 +45,62 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, 
   return off + x - v;
 }
 
+__device__ __forceinline__ PartSel fresh_sel(uint32_t k) {
+  PartSel s;
+  s.prefix = 0; s.mask = 0; s.r = k; s.done = 0; s.bin1 = 0; s.fault = 0; s.fb = 0; s.lo_fb = 0;
+  s.kth = 0xffffffffu; s.c1 = 0; s.lo_next = 0; s.pad = 0;
+  return s;
+}
+
+// Block-wide minimum folded into *dst with one atomic per block.
+__device__ __forceinline__ void block_min_into(uint32_t v, uint32_t* smin, uint32_t* dst) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t y = __shfl_xor(v, d, 64);
+    v = y < v ? y : v;
+  }
+  if ((threadIdx.x & 63) == 0) atomicMin(smin, v);
+  __syncthreads();
+  if (threadIdx.x == 0 && *smin != 0xffffffffu) atomicMin(dst, *smin);
+}
+
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0u;
 }
 
+__global__ void init_state_kernel(PartSel* state, int P, uint32_t k) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < P) {
+    PartSel s = fresh_sel(k);
+    s.fb = 1;
+    state[p] = s;
+  }
+}
+
 // One level of the threshold search for partition blockIdx.x: find the
 // digit d (scanning from the largest) whose bin holds the r-th largest
-// composite among those matching the current prefix; narrow the prefix.
-// Level 1 starts from r = k and an empty prefix.  Leaves the bins zeroed.
+// composite among those matching the current prefix, and narrow the prefix.
+// Level-1 modes start from r = k and an empty prefix (see kScan*).  Always
+// leaves the partition's bins zeroed.
 __global__ void __launch_bounds__(kThreads)
 level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, int shift,
-                  int nbits, int first) {
+                  int nbits, int mode, uint32_t target) {
   __shared__ uint32_t wtot[kThreads / 64];
   __shared__ int found;
+  __shared__ uint32_t s_lo;
+  __shared__ int s_dmin;
   const int p = blockIdx.x;
   uint32_t* h = hist + (int64_t)p * kBins;
   const int nb = 1 << nbits;
-  PartSel st;
-  if (first) {
-    st.prefix = 0; st.mask = 0; st.r = (uint32_t)g.k; st.done = 0; st.bin1 = 0; st.fault = 0;
-  } else {
-    st = state[p];
-  }
-  if (!st.done) {
+  const PartSel cur = state[p];
+  bool active;
+  if (mode == kScanCheck) active = true;
+  else if (mode == kScanLevel) active = !cur.done && !cur.fb;
+  else active = cur.fb != 0;
+  const bool first = mode != kScanLevel;
+  const PartSel st = first ? fresh_sel((uint32_t)g.k) : cur;
+  if (active) {
     const int per = (nb + kThreads - 1) / kThreads;
     // thread t owns descending positions [t*per, (t+1)*per): bin = nb-1-pos
     uint32_t s = 0;
@@ -79,9 +110,59 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
     }
     uint32_t tot;
     const uint32_t above = block_excl_scan(s, wtot, &tot);
-    if (threadIdx.x == 0) found = 0;
+    if (threadIdx.x == 0) {
+      found = 0;
+      s_lo = 0xffffffffu;
+      s_dmin = nb;
+    }
     __syncthreads();
-    if (above < st.r && st.r <= above + s) {
+    // Capture bound for the next step: the digit at which the count of keys
+    // from the top reaches `need` (level 1: target; level 2: the part of the
+    // target that falls inside the threshold bin).
+    const bool bound_l1 = (mode == kScanCheck || mode == kScanFinal);
+    const bool bound_l2 = (mode == kScanLevel && shift == g.levels[0].shift);
+    int64_t need = -1;
+    if (bound_l1) need = (tot >= target) ? (int64_t)target : -2;
+    if (bound_l2) {
+      const int64_t above_bin = (int64_t)g.k - (int64_t)cur.r;  // selected above the threshold bin
+      const int64_t in_bin = (int64_t)target - above_bin;
+      if (in_bin > 0 && in_bin <= (int64_t)tot) need = in_bin;
+    }
+    if (need >= 1 && above < (uint64_t)need && (uint64_t)need <= (uint64_t)above + s) {
+      uint32_t acc = above;
+      for (int q = 0; q < per; ++q) {
+        const int pos = threadIdx.x * per + q;
+        if (pos >= nb) break;
+        const int d = nb - 1 - pos;
+        acc += h[d];
+        if (acc >= (uint32_t)need) {
+          s_lo = (uint32_t)(((st.prefix & ~(((1ull << nbits) - 1ull) << shift)) | ((uint64_t)d << shift)) >> 32);
+          break;
+        }
+      }
+    }
+    if (bound_l1 && need == -2) {
+      // fewer keys than the target were captured: one bin below the lowest
+      // captured digit
+      for (int q = per - 1; q >= 0; --q) {
+        const int pos = threadIdx.x * per + q;
+        if (pos < nb && h[nb - 1 - pos]) {
+          atomicMin(&s_dmin, nb - 1 - pos);
+          break;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) s_lo = (uint32_t)(s_dmin >= 1 && s_dmin < nb ? s_dmin - 1 : 0) << kL1Shift;
+    }
+    __syncthreads();
+    if (mode == kScanCheck && tot < st.r) {
+      if (threadIdx.x == 0) {
+        PartSel o = st;
+        o.fb = 1;
+        state[p] = o;
+        found = 1;
+      }
+    } else if (above < st.r && st.r <= above + s) {
       uint32_t acc = above;
       for (int q = 0; q < per; ++q) {
         const int pos = threadIdx.x * per + q;
@@ -89,15 +170,25 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
         const int d = nb - 1 - pos;
         const uint32_t c = h[d];
         if (acc + c >= st.r) {
-          PartSel o = st;
-          o.r = st.r - acc;
-          o.prefix = st.prefix | ((uint64_t)d << shift);
-          uint64_t dm = ((1ull << nbits) - 1ull) << shift;
-          if (first) dm |= (1ull << 63);  // bit 63 of every composite is zero
-          o.mask = st.mask | dm;
-          o.done = (c == o.r) ? 1u : 0u;
-          if (first) o.bin1 = (uint32_t)d;
-          state[p] = o;
+          if (mode == kScanBound) {
+            PartSel o = cur;
+            o.lo_fb = (uint32_t)d << kL1Shift;
+            state[p] = o;
+          } else {
+            PartSel o = st;
+            o.r = st.r - acc;
+            o.prefix = st.prefix | ((uint64_t)d << shift);
+            uint64_t dm = ((1ull << nbits) - 1ull) << shift;
+            if (first) dm |= (1ull << 63);  // bit 63 of every composite is zero
+            o.mask = st.mask | dm;
+            o.done = (c == o.r) ? 1u : 0u;
+            if (first) {
+              o.bin1 = (uint32_t)d;
+              o.c1 = c;
+            }
+            o.fb = 0;
+            state[p] = o;
+          }
           found = 1;
           break;
         }
@@ -106,91 +197,142 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
     }
     __syncthreads();
     if (threadIdx.x == 0 && !found) {
-      st.fault = 1;
-      st.done = 1;
-      state[p] = st;
+      PartSel o = cur;
+      o.fault |= 1u;
+      o.done = 1;
+      o.fb = 0;
+      state[p] = o;
+    }
+    __syncthreads();
+    // record the bound (level 1 sets it; level 2 may raise it inside the bin)
+    if (threadIdx.x == 0 && (bound_l1 || bound_l2) && mode != kScanBound) {
+      if (bound_l1) state[p].lo_next = (s_lo == 0xffffffffu) ? 0u : s_lo;
+      else if (s_lo != 0xffffffffu && s_lo > state[p].lo_next) state[p].lo_next = s_lo;
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0u;
 }
 
-// Reads every key of the partition once.  Words of definite selections are
-// written whole; threshold-digit keys go to the block's candidate segment.
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Orders this wave's LDS accesses before its next ones.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave per tile: reads the tile's captured candidates 64 at a time;
+// selects the digits above the level-1 threshold digit into the tile's 64
+// mask words (written whole, so every word of the partition is written);
+// compacts the threshold digit's candidates in place, in order (a write
+// position never passes the chunk being read), and histograms their
+// level-2 digit.
 __global__ void __launch_bounds__(kThreads)
-select_pass_kernel(Geom g, const uint32_t* __restrict__ keys, const PartSel* __restrict__ state,
-                   uint64_t* __restrict__ bits, uint64_t* __restrict__ cand,
-                   uint32_t* __restrict__ segcnt) {
-  __shared__ uint32_t fill;
+cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ cand,
+                   const uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2,
+                   uint32_t* __restrict__ hist, uint64_t* __restrict__ bits) {
+  __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
+  __shared__ uint32_t sh[kBins];
+  __shared__ uint32_t smin;
   const int p = blockIdx.y;
-  const int b = blockIdx.x;
-  if (threadIdx.x == 0) fill = 0;
-  __syncthreads();
   const PartSel st = state[p];
   const uint32_t B1 = st.bin1;
   const bool done = st.done != 0;
+  const int l2shift = g.levels[0].shift;
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  const int64_t pbase = (int64_t)p * g.n_p;
-  uint64_t* seg = cand + ((int64_t)p * g.G + b) * g.seg_cap;
-
-  for (int64_t t = b; t < g.tpp; t += g.G) {
-    const int64_t w0 = t * kWordsPerTile + 16 * wave;
-    uint32_t kv[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int64_t j = (w0 + q) * 64 + lane;
-      kv[q] = (j < g.n_p) ? keys[pbase + j] : 0u;
-    }
-    uint64_t myword = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int64_t j = (w0 + q) * 64 + lane;
-      const bool valid = j < g.n_p;
-      const uint32_t bin = kv[q] >> kL1Shift;
-      const bool def = valid && (bin > B1 || (done && bin == B1));
-      const bool cnd = valid && !done && bin == B1;
-      const uint64_t wb = __ballot(def);
-      if (lane == (uint32_t)q) myword = wb;
-      const uint64_t cb = __ballot(cnd);
-      if (cb) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&fill, (uint32_t)__popcll(cb));
-        base = __shfl(base, 0, 64);
-        if (cnd) {
-          const uint64_t c = ((uint64_t)kv[q] << 32) | (uint64_t)(g.idx_mask - (uint32_t)j);
-          seg[base + mbcnt(cb)] = c;
+  unsigned long long* wd = words[wave];
+  uint32_t kmin = 0xffffffffu;  // smallest key selected whole from the threshold digit
+  for (int i = threadIdx.x; i < kBins; i += kThreads) sh[i] = 0;
+  if (threadIdx.x == 0) smin = 0xffffffffu;
+  __syncthreads();
+  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < g.tpp; t += nw) {
+    wd[lane] = 0ull;
+    wave_lds_sync();
+    uint32_t n1 = cnt1[(int64_t)p * g.tpp + t];
+    if (n1 > (uint32_t)kTile) n1 = (uint32_t)kTile;  // a slot holds at most one tile
+    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    const uint32_t tile_lo = (uint32_t)(t * kTile);
+    uint32_t n2 = 0;
+    for (uint32_t base = 0; base < n1; base += 64) {
+      const uint32_t i = base + lane;
+      const bool valid = i < n1;
+      const uint64_t c = valid ? slot[i] : 0ull;
+      const uint32_t d1 = (uint32_t)(c >> (32 + kL1Shift)) & (kBins - 1);
+      const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
+      const bool ok = valid && jl < (uint32_t)kTile;  // false only for a corrupted slot
+      const bool sel = ok && (d1 > B1 || (done && d1 == B1));
+      const bool keep = ok && !done && d1 == B1;
+      if (sel) {
+        atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+        if (d1 == B1) {
+          const uint32_t key = (uint32_t)(c >> 32);
+          kmin = key < kmin ? key : kmin;
         }
       }
+      const uint64_t kb = __ballot(keep);
+      if (keep) {
+        slot[n2 + mbcnt(kb)] = c;
+        atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
+      }
+      n2 += (uint32_t)__popcll(kb);
     }
-    if (lane < 16) {
-      const int64_t w = w0 + lane;
-      if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = myword;
-    }
+    wave_lds_sync();
+    const int64_t w = t * kWordsPerTile + lane;
+    if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = wd[lane];
+    if (lane == 0) cnt2[(int64_t)p * g.tpp + t] = n2;
+    wave_lds_sync();
   }
   __syncthreads();
-  if (threadIdx.x == 0) segcnt[(int64_t)p * g.G + b] = fill;
+  uint32_t* h = hist + (int64_t)p * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kThreads) {
+    const uint32_t c = sh[i];
+    if (c) atomicAdd(h + i, c);
+  }
+  if (done) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
 
-// Histogram of one digit over the candidates that match the prefix.
+// The compacted candidate lists are walked by wave per group of 64 tiles:
+// lane l reads tile (64*group + l)'s count, then the wave visits the
+// non-empty tiles of the group, its lanes striding over the candidates.
+template <typename F>
+__device__ __forceinline__ void for_each_compacted(const Geom& g, int p, const uint64_t* __restrict__ cand,
+                                                   const uint32_t* __restrict__ cnt2, F&& f) {
+  const uint32_t lane = lane_id();
+  const int64_t ngroups = (g.tpp + 63) / 64;
+  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); grp < ngroups; grp += nw) {
+    const int64_t t = grp * 64 + lane;
+    const uint32_t cnt = (t < g.tpp) ? cnt2[(int64_t)p * g.tpp + t] : 0u;
+    uint64_t nz = __ballot(cnt != 0);
+    while (nz) {
+      const int l = __builtin_ctzll(nz);
+      nz &= nz - 1ull;
+      const uint32_t ct = __shfl(cnt, l, 64);
+      const uint64_t* slot = cand + ((int64_t)p * g.tpp + grp * 64 + l) * kTile;
+      for (uint32_t i = lane; i < ct; i += 64) f(slot[i]);
+    }
+  }
+}
+
+// Histogram of one digit over the compacted candidates matching the prefix.
 __global__ void __launch_bounds__(kThreads)
-cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ segcnt,
-                 const PartSel* __restrict__ state, uint32_t* __restrict__ hist, int shift,
-                 int nbits) {
+cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
+                 const PartSel* __restrict__ state, uint32_t* __restrict__ hist, int shift, int nbits) {
   __shared__ uint32_t sh[kBins];
   const int p = blockIdx.y;
   const PartSel st = state[p];
-  if (st.done) return;
+  if (st.done || st.fb) return;
   const int nb = 1 << nbits;
   for (int i = threadIdx.x; i < nb; i += kThreads) sh[i] = 0;
   __syncthreads();
-  for (int s = blockIdx.x; s < g.G; s += gridDim.x) {
-    const uint32_t cnt = segcnt[(int64_t)p * g.G + s];
-    const uint64_t* seg = cand + ((int64_t)p * g.G + s) * g.seg_cap;
-    for (uint32_t i = threadIdx.x; i < cnt; i += kThreads) {
-      const uint64_t c = seg[i];
-      if ((c & st.mask) == st.prefix) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
-  }
+  for_each_compacted(g, p, cand, cnt2, [&](uint64_t c) {
+    if ((c & st.mask) == st.prefix) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+  });
   __syncthreads();
   uint32_t* h = hist + (int64_t)p * kBins;
   for (int i = threadIdx.x; i < nb; i += kThreads) {
@@ -199,24 +341,55 @@ cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __re
   }
 }
 
-// Sets the bits of the candidates at or above the threshold composite.
+// Sets the bits of the compacted candidates at or above the threshold: one
+// wave per tile with candidates assembles the tile's words in LDS and ORs
+// each non-zero word into the mask (the wave is the only writer of its
+// tile's words here, so a plain read-modify-write suffices).
 __global__ void __launch_bounds__(kThreads)
-mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ segcnt,
-            const PartSel* __restrict__ state, uint64_t* __restrict__ bits) {
+mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
+            PartSel* __restrict__ state, uint64_t* __restrict__ bits) {
+  __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
+  __shared__ uint32_t smin;
   const int p = blockIdx.y;
   const uint64_t T = state[p].prefix;
   uint64_t* wb = bits + (int64_t)p * g.wpp;
-  for (int s = blockIdx.x; s < g.G; s += gridDim.x) {
-    const uint32_t cnt = segcnt[(int64_t)p * g.G + s];
-    const uint64_t* seg = cand + ((int64_t)p * g.G + s) * g.seg_cap;
-    for (uint32_t i = threadIdx.x; i < cnt; i += kThreads) {
-      const uint64_t c = seg[i];
-      if (c >= T) {
-        const uint32_t j = g.idx_mask - (uint32_t)c;
-        atomicOr(reinterpret_cast<unsigned long long*>(wb + (j >> 6)), 1ull << (j & 63));
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  unsigned long long* wd = words[wave];
+  uint32_t kmin = 0xffffffffu;
+  if (threadIdx.x == 0) smin = 0xffffffffu;
+  const int64_t ngroups = (g.tpp + 63) / 64;
+  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + wave; grp < ngroups; grp += nw) {
+    const int64_t t0 = grp * 64 + lane;
+    const uint32_t cnt = (t0 < g.tpp) ? cnt2[(int64_t)p * g.tpp + t0] : 0u;
+    uint64_t nz = __ballot(cnt != 0);
+    while (nz) {
+      const int l = __builtin_ctzll(nz);
+      nz &= nz - 1ull;
+      const uint32_t ct = __shfl(cnt, l, 64);
+      const int64_t t = grp * 64 + l;
+      const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+      const uint32_t tile_lo = (uint32_t)(t * kTile);
+      wd[lane] = 0ull;
+      wave_lds_sync();
+      for (uint32_t i = lane; i < ct; i += 64) {
+        const uint64_t c = slot[i];
+        const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
+        if (c >= T && jl < (uint32_t)kTile) {
+          atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+          const uint32_t key = (uint32_t)(c >> 32);
+          kmin = key < kmin ? key : kmin;
+        }
       }
+      wave_lds_sync();
+      const unsigned long long word = wd[lane];
+      const int64_t w = t * kWordsPerTile + lane;
+      if (word && w < g.wpp) wb[w] |= word;
+      wave_lds_sync();
     }
   }
+  __syncthreads();
+  block_min_into(kmin, &smin, &state[p].kth);
 }
 
 // One wave per tile: number of selected elements in the tile.
@@ -233,10 +406,12 @@ tile_count_kernel(Geom g, const uint64_t* __restrict__ bits, uint32_t* __restric
   if (lane == 0) tilecnt[(int64_t)p * g.tpp + t] = c;
 }
 
-// Exclusive scan of the tile counts of partition blockIdx.x -> tile_off.
+// Exclusive scan of the tile counts of partition blockIdx.x -> tile_off;
+// then the slot's threshold record: the k-th key and the capture bound
+// proposed by the level scans for the next step.
 __global__ void __launch_bounds__(kThreads)
 scan_tiles_kernel(Geom g, const uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ tile_off,
-                  PartSel* __restrict__ state) {
+                  PartSel* __restrict__ state, uint32_t* __restrict__ meta_out) {
   __shared__ uint32_t wtot[kThreads / 64];
   const int p = blockIdx.x;
   const int64_t per = (g.tpp + kThreads - 1) / kThreads;
@@ -252,7 +427,13 @@ scan_tiles_kernel(Geom g, const uint32_t* __restrict__ tilecnt, uint32_t* __rest
     to[t] = run;
     run += tc[t];
   }
-  if (threadIdx.x == 0 && tot != (uint32_t)g.k) state[p].fault |= 2u;
+  if (threadIdx.x == 0) {
+    if (tot != (uint32_t)g.k) state[p].fault |= 2u;
+    if (meta_out) {
+      meta_out[p] = state[p].kth;
+      meta_out[g.P + p] = state[p].lo_next;
+    }
+  }
 }
 
 // One wave per tile: write the tile's selected global indices in order.
@@ -295,6 +476,13 @@ overlap_kernel(const uint64_t* __restrict__ a, const uint64_t* __restrict__ b, i
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
 
+// kCaptureMargin * k, at most n_p.
+uint32_t capture_target(const Geom& g) {
+  double t = kCaptureMargin * (double)g.k;
+  if (t > (double)g.n_p) t = (double)g.n_p;
+  return (uint32_t)(t + 0.5);
+}
+
 }  // namespace
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
@@ -305,23 +493,36 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_select(const Geom& g, const uint32_t* keys, uint32_t* hist, uint32_t* segcnt,
-                         uint64_t* cand, PartSel* state, uint32_t* tilecnt, uint64_t* bits,
-                         uint32_t* idx, uint32_t* tile_off, hipStream_t s,
-                         void (*mark)(void*, int), void* ctx) {
-  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, hist, state, 32 + kL1Shift, kDigitBits, 1);
-  select_pass_kernel<<<dim3(g.G, g.P), kThreads, 0, s>>>(g, keys, state, bits, cand, segcnt);
+hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s) {
+  init_state_kernel<<<(g.P + kThreads - 1) / kThreads, kThreads, 0, s>>>(state, g.P, (uint32_t)g.k);
+  return hipGetLastError();
+}
+
+hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s) {
+  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, 32 + kL1Shift, kDigitBits, mode,
+                                             capture_target(g));
+  return hipGetLastError();
+}
+
+hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits, uint32_t* idx,
+                              uint32_t* tile_off, uint32_t* meta_out, hipStream_t s,
+                              void (*mark)(void*, int), void* ctx) {
+  const unsigned sblocks = (unsigned)((g.tpp + 4 * kSelectTilesPerWave - 1) / (4 * kSelectTilesPerWave));
+  cand_select_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits);
   if (mark) mark(ctx, 1);
-  for (int l = 0; l < g.nlevels; ++l) {
-    cand_hist_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, cand, segcnt, state, hist,
-                                                         g.levels[l].shift, g.levels[l].nbits);
-    level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, hist, state, g.levels[l].shift, g.levels[l].nbits, 0);
+  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[0].shift, g.levels[0].nbits,
+                                             kScanLevel, capture_target(g));
+  for (int l = 1; l < g.nlevels; ++l) {
+    cand_hist_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, w.hist, g.levels[l].shift,
+                                                         g.levels[l].nbits);
+    level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[l].shift, g.levels[l].nbits,
+                                               kScanLevel, capture_target(g));
   }
-  mark_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, cand, segcnt, state, bits);
+  mark_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, bits);
   if (mark) mark(ctx, 2);
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
-  tile_count_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tilecnt);
-  scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, tilecnt, tile_off, state);
+  tile_count_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, w.tilecnt);
+  scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, w.tilecnt, tile_off, w.state, meta_out);
   write_idx_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
   return hipGetLastError();
 }

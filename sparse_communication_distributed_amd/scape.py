@@ -13,7 +13,8 @@ import os
 from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libscape.so")
+# SCAPE_LIB may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("SCAPE_LIB") or os.path.join(_PKG, "libscape.so")
 
 c_int64, c_int32, c_int, c_size_t = ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
 c_float, c_void_p, c_char_p = ctypes.c_float, ctypes.c_void_p, ctypes.c_char_p
@@ -30,7 +31,7 @@ class Betas(ctypes.Structure):
 
 
 class MaskView(ctypes.Structure):
-    _fields_ = [("bits", c_void_p), ("idx", c_void_p), ("tile_off", c_void_p)]
+    _fields_ = [("bits", c_void_p), ("idx", c_void_p), ("tile_off", c_void_p), ("meta", c_void_p)]
 
 
 class ScapeError(RuntimeError):
@@ -145,8 +146,17 @@ def mask_slot_tensors(d: Dims, k: int, blob, slot: int):
             sub(mv.tile_off, P * T, torch.int32, 4))
 
 
-def view_from_tensors(bits=None, idx=None, tile_off=None) -> MaskView:
-    return MaskView(_ptr(bits) or None, _ptr(idx) or None, _ptr(tile_off) or None)
+def mask_slot_meta(d: Dims, k: int, blob, slot: int):
+    """The slot's threshold record as an int32 view [2P] (k-th keys, then
+    the next capture bounds)."""
+    import torch
+    mv = mask_slot(d, k, blob, slot)
+    off = mv.meta - blob.data_ptr()
+    return blob[off:off + 2 * d.num_partitions * 4].view(torch.int32)
+
+
+def view_from_tensors(bits=None, idx=None, tile_off=None, meta=None) -> MaskView:
+    return MaskView(_ptr(bits) or None, _ptr(idx) or None, _ptr(tile_off) or None, _ptr(meta) or None)
 
 
 # --------------------------------------------------------------- components

@@ -190,7 +190,7 @@ def test_mask_overlap(S):
 # --------------------------------------------------------------- full step
 
 
-def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=None):
+def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=None, before_step=None):
     """Runs the fused GPU step and the oracle side by side from the same
     inputs; compares the next mask and all state after every step."""
     n, P, K, k, n_p = cfg.n, cfg.P, cfg.K, cfg.k, cfg.n_p
@@ -201,6 +201,8 @@ def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=N
     for t in range(1, steps + 1):
         g = W.grads(cfg, t, seed) if grad_fn is None else grad_fn(t)
         print(f"[lockstep] {cfg.name} n={n} P={P} K={K} k={k} step {t}", flush=True)
+        if before_step is not None:
+            before_step(opt, t)
         opt.step(dev(g))
         outs = ora.step(g)
         torch.cuda.synchronize()
@@ -270,3 +272,55 @@ def test_step_rejects_bad_arguments_on_device(S):
         S.step(d, t, torch.zeros(2, 4096, device=DEV), t, t, torch.zeros(2, 4096, device=DEV),
                torch.zeros(S.mask_bytes(d, 10), dtype=torch.uint8, device=DEV), 10, S.betas(), 1e-3, 1,
                torch.empty(16, dtype=torch.uint8, device=DEV))
+
+
+def _poison_bounds(S, value_fn):
+    """Overwrites the capture bounds in the threshold record of the slot the
+    next step reads (any value is legal: it may only change speed)."""
+    def hook(opt, t):
+        if t < 2:
+            return
+        meta = S.mask_slot_meta(opt.d, opt.k, opt.mask, (t - 1) & 1)
+        P = opt.P
+        vals = torch.tensor([value_fn(p) for p in range(P)], dtype=torch.int64).to(torch.int32)
+        meta[P:2 * P].copy_(vals.to(DEV))
+    return hook
+
+
+@pytest.mark.parametrize("mode", ["nothing", "everything", "mixed"])
+def test_step_capture_bound_fallback(S, mode):
+    """A bound that captures fewer than k keys (here: none) sends the
+    partition through the exact recount; a zero bound captures every key.
+    Both give the oracle's result bit for bit."""
+    cfg = W.flat_config("fallback", 5 * 30_000, 5, 2, "0.99", steps=4)
+    inf_bits = 0x7F800000
+    fn = {"nothing": lambda p: inf_bits, "everything": lambda p: 0,
+          "mixed": lambda p: (inf_bits, 0, 1 << 30, 0x3A800000, inf_bits)[p]}[mode]
+    run_lockstep(S, cfg, cfg.steps, before_step=_poison_bounds(S, fn))
+
+
+def test_threshold_record(S):
+    """mask_topk records the k-th largest key of every partition, and a
+    capture bound at or below it that 1.25*k keys reach, placed on the
+    coarsest digit boundary that still keeps that count (level-2 digits of
+    2^7 key units inside the threshold bin, level-1 digits of 2^19 below it)."""
+    P, n_p, k = 3, 20_000, 777
+    target = int(1.25 * k + 0.5)
+    stat = _stat_case("normal", P, n_p, 5)
+    d = S.dims(P * n_p, P, 1)
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+    S.mask_topk(d, k, dev(stat), S.mask_slot(d, k, blob, 0), ws)
+    torch.cuda.synchronize()
+    meta = host(S.mask_slot_meta(d, k, blob, 0)).view(np.uint32)
+    keys = O.magnitude_keys(stat).astype(np.int64)
+    for p in range(P):
+        kp = keys[p * n_p:(p + 1) * n_p]
+        kth = np.sort(kp)[::-1][k - 1]
+        assert meta[p] == kth
+        lo = int(meta[P + p])
+        assert lo <= kth
+        assert np.count_nonzero(kp >= lo) >= target
+        step = (1 << 7) if (lo >> 19) == (kth >> 19) else (1 << 19)
+        assert lo % step == 0
+        assert np.count_nonzero(kp >= lo + step) < target

@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-parts", type=int, default=1, help="partitions timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="report |M_t ∩ M_{t+1}| / (P k) per step (untimed; on by default for the stress workload)")
     ap.add_argument("--calib", action="store_true",
                     help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
     args = ap.parse_args()
@@ -114,6 +116,7 @@ def main():
     from sparse_communication_distributed_amd import workload as W
 
     cfg = W.CONFIGS[args.config]
+    args.overlap = args.overlap or cfg.grad_law == "stress_t3"
     n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -167,8 +170,13 @@ def main():
     # per-stage durations of the same steps, recorded with HIP events on the
     # stream the kernels run on (a second, profiled pass of --steps steps)
     S.profile_enable(True)
+    overlaps = []
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
     for _ in range(args.steps):
         one_step()
+        if args.overlap:  # |M_t ∩ M_{t+1}| / (P k), outside the timed region
+            S.mask_overlap(d, k, S.mask_slot(d, k, mask, (t - 1) & 1), S.mask_slot(d, k, mask, t & 1), cnt, stream)
+            overlaps.append(cnt.item() / (P * k))
     stages = S.profile_collect()
     S.profile_enable(False)
     stage_ms = {name: tot / cnt for name, (tot, cnt) in stages.items() if cnt}
@@ -182,8 +190,11 @@ def main():
     traffic = None
     prof_path = os.path.join(ROOT, "profiles", f"step_pass_{cfg.name}_counters.json")
     if os.path.exists(prof_path):
+        from sparse_communication_distributed_amd.prof_summary import step_pass_source_hash
         with open(prof_path) as f:
-            traffic = json.load(f).get("hbm_bytes_per_launch")
+            doc = json.load(f)
+        if doc.get("source_hash") == step_pass_source_hash():  # counters of this very kernel
+            traffic = doc.get("hbm_bytes_per_launch")
 
     out = {
         "metric": METRIC,
@@ -212,6 +223,8 @@ def main():
     }
     if calib is not None:
         out["stream_calibration"] = calib
+    if overlaps:
+        out["mask_overlap"] = overlaps
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, pool[0], w_init, args.seed, args.cpu_parts, log)
     print(json.dumps(out), flush=True)

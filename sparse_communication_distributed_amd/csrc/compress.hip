@@ -120,6 +120,17 @@ __device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], 
   }
 }
 
+// Grid of the streaming passes: G blocks per partition.  With
+// kPartitionFastest the partition is blockIdx.x, so the blocks resident at
+// any moment cover every partition; otherwise blockIdx.y, so the dispatcher
+// fills the device partition by partition.
+constexpr bool kPartitionFastest = false;
+
+__device__ __forceinline__ int block_part() { return kPartitionFastest ? blockIdx.x : blockIdx.y; }
+__device__ __forceinline__ int block_in_part() { return kPartitionFastest ? blockIdx.y : blockIdx.x; }
+__device__ __forceinline__ int blocks_per_part() { return kPartitionFastest ? gridDim.y : gridDim.x; }
+inline dim3 stream_grid(const Geom& g) { return kPartitionFastest ? dim3(g.P, g.G) : dim3(g.G, g.P); }
+
 struct AdamsC {
   float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, invK;
 };
@@ -154,7 +165,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
   __shared__ uint32_t sh[STEP ? kBins : 1];
   __shared__ uint32_t tcnt;
   if (STEP) hist_zero(sh);
-  const int p = blockIdx.y;
+  const int p = block_part();
   const int64_t pbase = (int64_t)p * g.n_p;
   const int64_t wbase = (int64_t)p * g.wpp;
   const int64_t pk = (int64_t)g.P * g.k;
@@ -164,7 +175,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
   const int sh4 = 4 * lane16;
   const uint64_t below = (sh4 == 0) ? 0ull : ((1ull << sh4) - 1ull);
 
-  for (int64_t t = blockIdx.x; t < g.tpp; t += gridDim.x) {
+  for (int64_t t = block_in_part(); t < g.tpp; t += blocks_per_part()) {
     __syncthreads();  // previous tile's LDS words and counter no longer in use
     load_tile_words(bits, wbase, g.wpp, t, sw, spre);
     if (threadIdx.x == 0) tcnt = 0;
@@ -302,7 +313,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[kBins];
   __shared__ uint32_t tcnt;
-  const int p = blockIdx.y;
+  const int p = block_part();
   const PartSel st = state[p];
   if (only_fb && !st.fb) return;  // block-uniform
   hist_zero(sh);
@@ -318,7 +329,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
   const int sh4 = 4 * lane16;
   const uint64_t below = (sh4 == 0) ? 0ull : ((1ull << sh4) - 1ull);
 
-  for (int64_t t = blockIdx.x; t < g.tpp; t += gridDim.x) {
+  for (int64_t t = block_in_part(); t < g.tpp; t += blocks_per_part()) {
     __syncthreads();
     if (SRC == 2) load_tile_words(bits, wbase, g.wpp, t, sw, spre);
     if (threadIdx.x == 0) tcnt = 0;
@@ -389,7 +400,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
 
 template <int SRC, int PHASE>
 void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
-  dim3 grid(g.G, g.P);
+  const dim3 grid = stream_grid(g);
   if (vec)
     stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
@@ -412,7 +423,7 @@ hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, boo
 
 hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
                            const uint32_t* tile_off, float* b, hipStream_t s, bool vec) {
-  dim3 grid(g.G, g.P);
+  const dim3 grid = stream_grid(g);
   AdamsC ac{};
   if (vec)
     compress_kernel<false, false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
@@ -426,7 +437,7 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
 }
 
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s) {
-  dim3 grid(g.G, g.P);
+  const dim3 grid = stream_grid(g);
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
   if (a.w != nullptr) {  // with AdamS fused
     if (vec)

@@ -16,8 +16,10 @@ constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
 // Level-1 digit: key bits [30:19] (bit 31 of a key is always zero).
 constexpr int kL1Shift = 19;
-// Target number of blocks for streaming passes (>> 256 CUs).
-constexpr int kTargetBlocks = 4096;
+// Target number of blocks for the streaming passes: short blocks (about a
+// dozen tiles each) let the dispatcher balance tiles of uneven cost (dense
+// mask or capture regions) across the 256 CUs.
+constexpr int kTargetBlocks = 32768;
 // Blocks per partition for the passes over compacted candidate lists (one
 // wave per group of 64 tiles), at most this many.
 constexpr int kRefineBlocks = 64;

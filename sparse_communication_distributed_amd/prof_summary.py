@@ -1,0 +1,96 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m sparse_communication_distributed_amd.prof_summary \
+        --stats <dir>/run_kernel_stats.csv --fetch <dir>/run_counter_collection.csv \
+        --write <dir>/run_counter_collection.csv --workload llama1.8b --out profiles/step_pass_llama1.8b
+
+writes <out>.md (kernel table and HBM bytes) and <out>_counters.json (the
+step pass's HBM bytes per launch, read by bench.py).  The HBM counters are
+scaled by what they read for the 1 GiB calibration copy that bench.py --calib
+runs (reads 1 GiB, writes 1 GiB).  The JSON records a hash of the step
+pass's sources; bench.py ignores it once the sources change.
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+STEP_KERNEL = "compress_kernel"
+CALIB_KERNEL = "__amd_rocclr_copyBuffer"
+GIB_KIB = float(1 << 20)
+
+
+def step_pass_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("compress.hip", "scape_internal.h"):
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter(path, counter):
+    per = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", default="")
+    ap.add_argument("--step-launches-skip", type=int, default=1,
+                    help="step-pass launches to drop from the counter average (the first step)")
+    a = ap.parse_args()
+
+    rows = list(csv.DictReader(open(a.stats)))
+    fetch = read_counter(a.fetch, "FETCH_SIZE")
+    write = read_counter(a.write, "WRITE_SIZE")
+    f_scale = GIB_KIB / (sum(fetch[CALIB_KERNEL]) / len(fetch[CALIB_KERNEL]))
+    w_scale = GIB_KIB / (sum(write[CALIB_KERNEL]) / len(write[CALIB_KERNEL]))
+
+    lines = [f"# Kernel profile — {a.workload}", ""]
+    if a.command:
+        lines += ["Commands (repository root on the GPU box):", "", "```", a.command.strip(), "```", ""]
+    lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
+    lines += ["", "## HBM bytes (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"Calibration copy of 1 GiB: FETCH_SIZE scale {f_scale:.3f}, WRITE_SIZE scale {w_scale:.3f}.", "",
+              "| kernel | launches | read GB / launch (scaled) | write GB / launch (scaled) |", "|---|---|---|---|"]
+    out = {}
+    for k in sorted(set(fetch) | set(write)):
+        fv, wv = fetch.get(k, []), write.get(k, [])
+        if k == STEP_KERNEL:
+            fv, wv = fv[a.step_launches_skip:], wv[a.step_launches_skip:]
+        if not fv or not wv:
+            continue
+        rd = sum(fv) / len(fv) * 1024 * f_scale / 1e9
+        wr = sum(wv) / len(wv) * 1024 * w_scale / 1e9
+        out[k] = (rd, wr)
+        if rd + wr > 0.05:
+            lines.append(f"| {k} | {len(fv)} | {rd:.3f} | {wr:.3f} |")
+    with open(a.out + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rd, wr = out[STEP_KERNEL]
+    doc = {"workload": a.workload, "kernel": STEP_KERNEL, "source_hash": step_pass_source_hash(),
+           "hbm_read_bytes_per_launch": rd * 1e9, "hbm_write_bytes_per_launch": wr * 1e9,
+           "hbm_bytes_per_launch": (rd + wr) * 1e9, "fetch_scale": f_scale, "write_scale": w_scale}
+    with open(a.out + "_counters.json", "w") as f:
+        json.dump(doc, f, indent=1)
+    print(json.dumps(doc, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -38,6 +38,9 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   if (G > r.tpp) G = r.tpp;
   if (G < 1) G = 1;
   r.G = (int)G;
+  int64_t Gs = (kStatBlocks + P - 1) / P;
+  if (Gs > r.tpp) Gs = r.tpp;
+  r.Gs = (int)(Gs < 1 ? 1 : Gs);
   const int64_t groups = (r.tpp + 63) / 64;
   int64_t R = (groups + 3) / 4;
   if (R > kRefineBlocks) R = kRefineBlocks;

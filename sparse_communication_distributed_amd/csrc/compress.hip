@@ -129,7 +129,7 @@ constexpr bool kPartitionFastest = false;
 __device__ __forceinline__ int block_part() { return kPartitionFastest ? blockIdx.x : blockIdx.y; }
 __device__ __forceinline__ int block_in_part() { return kPartitionFastest ? blockIdx.y : blockIdx.x; }
 __device__ __forceinline__ int blocks_per_part() { return kPartitionFastest ? gridDim.y : gridDim.x; }
-inline dim3 stream_grid(const Geom& g) { return kPartitionFastest ? dim3(g.P, g.G) : dim3(g.G, g.P); }
+inline dim3 stream_grid(const Geom& g, int G) { return kPartitionFastest ? dim3(g.P, G) : dim3(G, g.P); }
 
 struct AdamsC {
   float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, invK;
@@ -400,7 +400,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
 
 template <int SRC, int PHASE>
 void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
-  const dim3 grid = stream_grid(g);
+  const dim3 grid = stream_grid(g, g.Gs);
   if (vec)
     stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
@@ -423,7 +423,7 @@ hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, boo
 
 hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
                            const uint32_t* tile_off, float* b, hipStream_t s, bool vec) {
-  const dim3 grid = stream_grid(g);
+  const dim3 grid = stream_grid(g, g.G);
   AdamsC ac{};
   if (vec)
     compress_kernel<false, false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
@@ -437,7 +437,7 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
 }
 
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s) {
-  const dim3 grid = stream_grid(g);
+  const dim3 grid = stream_grid(g, g.G);
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
   if (a.w != nullptr) {  // with AdamS fused
     if (vec)

@@ -23,6 +23,9 @@ constexpr int kTargetBlocks = 32768;
 // Blocks per partition for the passes over compacted candidate lists (one
 // wave per group of 64 tiles), at most this many.
 constexpr int kRefineBlocks = 64;
+// Target number of blocks of the statistic passes (the bootstrap and the
+// fallback, which usually has nothing to do and should cost little).
+constexpr int kStatBlocks = 2048;
 // Tiles each wave of the candidate select pass walks.
 constexpr int kSelectTilesPerWave = 8;
 constexpr int kThreads = 256;
@@ -76,7 +79,8 @@ struct Geom {
   int P, K;
   int64_t wpp;        // mask words per partition
   int64_t tpp;        // tiles per partition
-  int G;              // blocks per partition of the streaming passes
+  int G;              // blocks per partition of the streaming step pass
+  int Gs;             // blocks per partition of the statistic passes
   int R;              // blocks per partition over candidate lists
   int idx_bits;       // bits of (n_p - 1), >= 1
   uint32_t idx_mask;  // (1 << idx_bits) - 1

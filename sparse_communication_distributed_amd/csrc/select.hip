@@ -234,7 +234,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 __global__ void __launch_bounds__(kThreads)
 cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ cand,
                    const uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2,
-                   uint32_t* __restrict__ hist, uint64_t* __restrict__ bits) {
+                   uint32_t* __restrict__ hist, uint64_t* __restrict__ bits,
+                   uint32_t* __restrict__ tilecnt) {
   __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
   __shared__ uint32_t sh[kBins];
   __shared__ uint32_t smin;
@@ -283,8 +284,15 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
     }
     wave_lds_sync();
     const int64_t w = t * kWordsPerTile + lane;
-    if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = wd[lane];
-    if (lane == 0) cnt2[(int64_t)p * g.tpp + t] = n2;
+    const unsigned long long word = wd[lane];
+    if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = word;
+    uint32_t pc = (uint32_t)__popcll(word);
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
+    if (lane == 0) {
+      cnt2[(int64_t)p * g.tpp + t] = n2;
+      tilecnt[(int64_t)p * g.tpp + t] = pc;
+    }
     wave_lds_sync();
   }
   __syncthreads();
@@ -347,7 +355,7 @@ cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __re
 // tile's words here, so a plain read-modify-write suffices).
 __global__ void __launch_bounds__(kThreads)
 mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
-            PartSel* __restrict__ state, uint64_t* __restrict__ bits) {
+            PartSel* __restrict__ state, uint64_t* __restrict__ bits, uint32_t* __restrict__ tilecnt) {
   __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
   __shared__ uint32_t smin;
   const int p = blockIdx.y;
@@ -385,25 +393,17 @@ mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restric
       const unsigned long long word = wd[lane];
       const int64_t w = t * kWordsPerTile + lane;
       if (word && w < g.wpp) wb[w] |= word;
+      // these elements were not selected by the candidate select pass, so
+      // the tile's count grows by exactly their number
+      uint32_t pc = (uint32_t)__popcll(word);
+#pragma unroll
+      for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
+      if (lane == 0 && pc) tilecnt[(int64_t)p * g.tpp + t] += pc;
       wave_lds_sync();
     }
   }
   __syncthreads();
   block_min_into(kmin, &smin, &state[p].kth);
-}
-
-// One wave per tile: number of selected elements in the tile.
-__global__ void __launch_bounds__(kThreads)
-tile_count_kernel(Geom g, const uint64_t* __restrict__ bits, uint32_t* __restrict__ tilecnt) {
-  const int p = blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (t >= g.tpp) return;
-  const uint32_t lane = lane_id();
-  const int64_t w = t * kWordsPerTile + lane;
-  uint32_t c = (w < g.wpp) ? (uint32_t)__popcll(bits[(int64_t)p * g.wpp + w]) : 0u;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-  if (lane == 0) tilecnt[(int64_t)p * g.tpp + t] = c;
 }
 
 // Exclusive scan of the tile counts of partition blockIdx.x -> tile_off;
@@ -508,7 +508,8 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
                               uint32_t* tile_off, uint32_t* meta_out, hipStream_t s,
                               void (*mark)(void*, int), void* ctx) {
   const unsigned sblocks = (unsigned)((g.tpp + 4 * kSelectTilesPerWave - 1) / (4 * kSelectTilesPerWave));
-  cand_select_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits);
+  cand_select_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits,
+                                                              w.tilecnt);
   if (mark) mark(ctx, 1);
   level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[0].shift, g.levels[0].nbits,
                                              kScanLevel, capture_target(g));
@@ -518,10 +519,9 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
     level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[l].shift, g.levels[l].nbits,
                                                kScanLevel, capture_target(g));
   }
-  mark_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, bits);
+  mark_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, bits, w.tilecnt);
   if (mark) mark(ctx, 2);
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
-  tile_count_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, w.tilecnt);
   scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, w.tilecnt, tile_off, w.state, meta_out);
   write_idx_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
   return hipGetLastError();

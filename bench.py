@@ -205,6 +205,17 @@ def main():
     stage_ms = {name: tot / cnt for name, (tot, cnt) in stages.items() if cnt}
     log("stage ms: " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in stage_ms.items()))
 
+    # the pages' comparison point: dense AdamS on the worker mean, same
+    # tensors, same number of steps (after the SCAPE measurements)
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for s_ in range(args.steps):
+        S.dense_adams_step(d, params, pool[s_ % len(pool)], m, v, bt, cfg.lr, t + 1 + s_, stream)
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = ev2.elapsed_time(ev3) / args.steps
+    log(f"dense AdamS: {dense_ms:.3f} ms/step")
+
     b_step = alg_bytes_step(n, P, K, k)
     b_comp = alg_bytes_step_pass(n, P, K, k)
     gbps = b_step / (ms * 1e-3) / 1e9
@@ -244,6 +255,11 @@ def main():
                      "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms},
         "cpu_baseline": None,
     }
+    b_dense = (4 * K + 20) * n
+    out["dense_adams"] = {"ms_per_step": dense_ms, "params_per_s": n / (dense_ms * 1e-3),
+                          "hbm_gbps_alg": b_dense / (dense_ms * 1e-3) / 1e9,
+                          "bytes_alg_per_step": b_dense,
+                          "note": "local cost only: no collective runs on one GPU"}
     if calib is not None:
         out["stream_calibration"] = calib
     if overlaps:

@@ -188,6 +188,17 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
                         int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dense AdamS on the worker mean: the baseline the pages compare SCAPE's
+ * per-step time with ([P] abstract; [S] §4).  For every element j:
+ *   x = (((grads[0][j] + grads[1][j]) + ...) + grads[K-1][j]) * fp32(1/K)
+ *   then the AdamS update of scape_adams_update at j ([P] §II-C eq. (2)).
+ * params, m, v [n] in/out; grads [K][n] read-only.  No error feedback, no
+ * mask, no workspace.  dims->num_partitions only has to divide n.
+ */
+scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const float* grads, float* m,
+                                   float* v, scape_betas betas, float lr, int64_t step, hipStream_t stream);
+
+/*
  * Overlap of two masks: *count_out (device u64) = |A ∩ B| summed over all
  * partitions (the consecutive-step mask stability the [P] §I insight
  * rests on; divide by P*k for the fraction).  Reads a.bits and b.bits.

@@ -2,6 +2,6 @@
 
 from .scape_oracle import (  # noqa: F401
     Hyper, OracleOptimizer, PartitionState, accumulate, adams_update, bias_reciprocal,
-    compress, magnitude_keys, mask_overlap, owner, reduce_mean, statistic_keys,
+    compress, dense_adams_step, magnitude_keys, mask_overlap, owner, reduce_mean, statistic_keys,
     step_partition, topk_indices,
 )

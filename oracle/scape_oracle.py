@@ -170,6 +170,14 @@ def adams_update(w: np.ndarray, m: np.ndarray, v: np.ndarray, idx: np.ndarray,
     w[idx] = wn
 
 
+def dense_adams_step(w: np.ndarray, m: np.ndarray, v: np.ndarray, g: np.ndarray, hp: Hyper, t: int) -> None:
+    """Dense AdamS on the worker mean, in place: the baseline the pages
+    measure SCAPE against ([P] abstract; [S] §4, per-step speedup over dense
+    AdamS).  x = O5's mean of the K gradients, then O6 at every index."""
+    x = reduce_mean([g[i] for i in range(g.shape[0])])
+    adams_update(w, m, v, np.arange(w.shape[0]), x, hp, t)
+
+
 def mask_overlap(prev: Sequence[np.ndarray], nxt: Sequence[np.ndarray], k: int) -> float:
     """O8: |M_t ∩ M_{t+1}| / (P*k) over per-partition index lists."""
     common = sum(np.intersect1d(a, b, assume_unique=True).size for a, b in zip(prev, nxt))

@@ -108,6 +108,69 @@ reduce_adams_kernel(const float* __restrict__ b, int K, float invK, const uint32
   }
 }
 
+// Dense AdamS on the worker mean (the baseline the SCAPE step is compared
+// with): one streaming pass, x = ((g0 + g1) + ...) * fp32(1/K), AdamS at
+// every element.  4 elements per thread per iteration, non-temporal.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads)
+dense_adams_kernel(const float* __restrict__ g, int K, int64_t n, float invK, float* __restrict__ w,
+                   float* __restrict__ m, float* __restrict__ v, AdamsK c) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
+  for (int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4; j0 < n; j0 += stride) {
+    float x[4], mo[4], wo[4];
+    if (VEC) {
+      v4f s = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(g + j0));
+      for (int i = 1; i < K; ++i) s = s + __builtin_nontemporal_load(reinterpret_cast<const v4f*>(g + (int64_t)i * n + j0));
+      const v4f mv = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(m + j0));
+      const v4f wv = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(w + j0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] = s[q] * invK;
+        mo[q] = mv[q];
+        wo[q] = wv[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t j = j0 + q;
+        if (j >= n) break;
+        float s = g[j];
+        for (int i = 1; i < K; ++i) s = s + g[(int64_t)i * n + j];
+        x[q] = s * invK;
+        mo[q] = m[j];
+        wo[q] = w[j];
+      }
+    }
+    float mn[4], vn[4], wn[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mn[q] = (c.b1 * mo[q]) + (c.c1 * x[q]);
+      vn[q] = (c.b2 * (mo[q] * mo[q])) + (c.c2 * (x[q] * x[q]));
+      const float mh = mn[q] * c.ibc1;
+      const float vh = vn[q] * c.ibc2;
+      const float d = sqrtf(vh) + c.eps;
+      const float u = mh / d;
+      wn[q] = wo[q] - (c.lr * (u + (c.wd * wo[q])));
+    }
+    if (VEC) {
+      __builtin_nontemporal_store((v4f){mn[0], mn[1], mn[2], mn[3]}, reinterpret_cast<v4f*>(m + j0));
+      __builtin_nontemporal_store((v4f){vn[0], vn[1], vn[2], vn[3]}, reinterpret_cast<v4f*>(v + j0));
+      __builtin_nontemporal_store((v4f){wn[0], wn[1], wn[2], wn[3]}, reinterpret_cast<v4f*>(w + j0));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t j = j0 + q;
+        if (j >= n) break;
+        m[j] = mn[q];
+        v[j] = vn[q];
+        w[j] = wn[q];
+      }
+    }
+  }
+}
+
 unsigned grid_for(int64_t count) {
   int64_t blocks = (count + kThreads - 1) / kThreads;
   if (blocks > 16384) blocks = 16384;
@@ -130,6 +193,21 @@ hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, f
   const int64_t pk = (int64_t)g.P * g.k;
   AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
   adams_kernel<<<grid_for(pk), kThreads, 0, s>>>(bbar, idx, pk, w, m, v, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float* m, float* v, float b1,
+                              float b2, float c1, float c2, float ibc1, float ibc2, float eps, float wd,
+                              float lr, bool vec, hipStream_t s) {
+  const float invK = (float)(1.0 / (double)g.K);
+  AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
+  int64_t blocks = (g.n / 4 + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (vec)
+    dense_adams_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(grads, g.K, g.n, invK, w, m, v, c);
+  else
+    dense_adams_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(grads, g.K, g.n, invK, w, m, v, c);
   return hipGetLastError();
 }
 

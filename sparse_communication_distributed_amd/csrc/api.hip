@@ -41,10 +41,6 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   int64_t Gs = (kStatBlocks + P - 1) / P;
   if (Gs > r.tpp) Gs = r.tpp;
   r.Gs = (int)(Gs < 1 ? 1 : Gs);
-  const int64_t groups = (r.tpp + 63) / 64;
-  int64_t R = (groups + 3) / 4;
-  if (R > kRefineBlocks) R = kRefineBlocks;
-  r.R = (int)(R < 1 ? 1 : R);
   r.idx_bits = bit_width_u64((uint64_t)(n_p - 1));
   if (r.idx_bits < 1) r.idx_bits = 1;
   r.idx_mask = (uint32_t)((uint64_t(1) << r.idx_bits) - 1);
@@ -396,6 +392,22 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   }
   g_prof.end();
   return st;
+}
+
+scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const float* grads, float* m,
+                                   float* v, scape_betas betas, float lr, int64_t step, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, 1, &g);
+  if (st) return st;
+  if (!params || !grads || !m || !v) return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = check_betas(betas, lr))) return st;
+  if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  const float b1 = betas.beta1, b2 = betas.beta2;
+  const bool vec = (g.n % 4 == 0) && aligned16(params) && aligned16(grads) && aligned16(m) && aligned16(v);
+  return hip_check(launch_dense_adams(g, grads, params, m, v, b1, b2, 1.0f - b1, 1.0f - b2,
+                                      bias_reciprocal(b1, step), bias_reciprocal(b2, step), betas.eps,
+                                      betas.weight_decay, lr, vec, stream),
+                   "dense adams");
 }
 
 scape_status scape_mask_overlap(const scape_dims* dims, int64_t k, scape_mask_view a,

@@ -20,13 +20,10 @@ constexpr int kL1Shift = 19;
 // dozen tiles each) let the dispatcher balance tiles of uneven cost (dense
 // mask or capture regions) across the 256 CUs.
 constexpr int kTargetBlocks = 32768;
-// Blocks per partition for the passes over compacted candidate lists (one
-// wave per group of 64 tiles), at most this many.
-constexpr int kRefineBlocks = 64;
 // Target number of blocks of the statistic passes (the bootstrap and the
 // fallback, which usually has nothing to do and should cost little).
 constexpr int kStatBlocks = 2048;
-// Tiles each wave of the candidate select pass walks.
+// Tiles each wave of the passes over candidate slots walks.
 constexpr int kSelectTilesPerWave = 8;
 constexpr int kThreads = 256;
 
@@ -81,7 +78,6 @@ struct Geom {
   int64_t tpp;        // tiles per partition
   int G;              // blocks per partition of the streaming step pass
   int Gs;             // blocks per partition of the statistic passes
-  int R;              // blocks per partition over candidate lists
   int idx_bits;       // bits of (n_p - 1), >= 1
   uint32_t idx_mask;  // (1 << idx_bits) - 1
   int nlevels;        // levels after level 1 (level 2 first)
@@ -163,6 +159,9 @@ hipError_t launch_reduce(const Geom& g, const float* b, float* bbar, hipStream_t
 hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, float* w, float* m,
                         float* v, float b1, float b2, float c1, float c2, float ibc1, float ibc2,
                         float eps, float wd, float lr, hipStream_t s);
+hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float* m, float* v, float b1,
+                              float b2, float c1, float c2, float ibc1, float ibc2, float eps, float wd,
+                              float lr, bool vec, hipStream_t s);
 hipError_t launch_reduce_adams(const Geom& g, const float* b, const uint32_t* idx, float* w,
                                float* m, float* v, float b1, float b2, float c1, float c2,
                                float ibc1, float ibc2, float eps, float wd, float lr,

@@ -304,26 +304,17 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   if (done) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
 
-// The compacted candidate lists are walked by wave per group of 64 tiles:
-// lane l reads tile (64*group + l)'s count, then the wave visits the
-// non-empty tiles of the group, its lanes striding over the candidates.
+// The compacted candidate lists are walked one wave per tile (each wave
+// takes tiles wave_id, wave_id + nwaves, ...), the lanes striding over the
+// tile's candidates.
 template <typename F>
-__device__ __forceinline__ void for_each_compacted(const Geom& g, int p, const uint64_t* __restrict__ cand,
-                                                   const uint32_t* __restrict__ cnt2, F&& f) {
-  const uint32_t lane = lane_id();
-  const int64_t ngroups = (g.tpp + 63) / 64;
+__device__ __forceinline__ void for_each_tile(const Geom& g, int p, const uint32_t* __restrict__ cnt2,
+                                              F&& f) {
   const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
-  for (int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); grp < ngroups; grp += nw) {
-    const int64_t t = grp * 64 + lane;
-    const uint32_t cnt = (t < g.tpp) ? cnt2[(int64_t)p * g.tpp + t] : 0u;
-    uint64_t nz = __ballot(cnt != 0);
-    while (nz) {
-      const int l = __builtin_ctzll(nz);
-      nz &= nz - 1ull;
-      const uint32_t ct = __shfl(cnt, l, 64);
-      const uint64_t* slot = cand + ((int64_t)p * g.tpp + grp * 64 + l) * kTile;
-      for (uint32_t i = lane; i < ct; i += 64) f(slot[i]);
-    }
+  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); t < g.tpp; t += nw) {
+    uint32_t ct = cnt2[(int64_t)p * g.tpp + t];
+    if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
+    if (ct) f(t, ct);  // wave-uniform
   }
 }
 
@@ -338,8 +329,13 @@ cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __re
   const int nb = 1 << nbits;
   for (int i = threadIdx.x; i < nb; i += kThreads) sh[i] = 0;
   __syncthreads();
-  for_each_compacted(g, p, cand, cnt2, [&](uint64_t c) {
-    if ((c & st.mask) == st.prefix) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+  const uint32_t lane = lane_id();
+  for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
+    const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    for (uint32_t i = lane; i < ct; i += 64) {
+      const uint64_t c = slot[i];
+      if ((c & st.mask) == st.prefix) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
   });
   __syncthreads();
   uint32_t* h = hist + (int64_t)p * kBins;
@@ -349,10 +345,10 @@ cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __re
   }
 }
 
-// Sets the bits of the compacted candidates at or above the threshold: one
-// wave per tile with candidates assembles the tile's words in LDS and ORs
-// each non-zero word into the mask (the wave is the only writer of its
-// tile's words here, so a plain read-modify-write suffices).
+// Sets the bits of the compacted candidates at or above the threshold: the
+// wave of a tile assembles the tile's words in LDS and ORs each non-zero
+// word into the mask (it is the only writer of its tile's words here, so a
+// plain read-modify-write suffices), and adds their count to the tile's.
 __global__ void __launch_bounds__(kThreads)
 mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
             PartSel* __restrict__ state, uint64_t* __restrict__ bits, uint32_t* __restrict__ tilecnt) {
@@ -365,43 +361,32 @@ mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restric
   unsigned long long* wd = words[wave];
   uint32_t kmin = 0xffffffffu;
   if (threadIdx.x == 0) smin = 0xffffffffu;
-  const int64_t ngroups = (g.tpp + 63) / 64;
-  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
-  for (int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + wave; grp < ngroups; grp += nw) {
-    const int64_t t0 = grp * 64 + lane;
-    const uint32_t cnt = (t0 < g.tpp) ? cnt2[(int64_t)p * g.tpp + t0] : 0u;
-    uint64_t nz = __ballot(cnt != 0);
-    while (nz) {
-      const int l = __builtin_ctzll(nz);
-      nz &= nz - 1ull;
-      const uint32_t ct = __shfl(cnt, l, 64);
-      const int64_t t = grp * 64 + l;
-      const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-      const uint32_t tile_lo = (uint32_t)(t * kTile);
-      wd[lane] = 0ull;
-      wave_lds_sync();
-      for (uint32_t i = lane; i < ct; i += 64) {
-        const uint64_t c = slot[i];
-        const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
-        if (c >= T && jl < (uint32_t)kTile) {
-          atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
-          const uint32_t key = (uint32_t)(c >> 32);
-          kmin = key < kmin ? key : kmin;
-        }
+  for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
+    const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    const uint32_t tile_lo = (uint32_t)(t * kTile);
+    wd[lane] = 0ull;
+    wave_lds_sync();
+    for (uint32_t i = lane; i < ct; i += 64) {
+      const uint64_t c = slot[i];
+      const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
+      if (c >= T && jl < (uint32_t)kTile) {
+        atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+        const uint32_t key = (uint32_t)(c >> 32);
+        kmin = key < kmin ? key : kmin;
       }
-      wave_lds_sync();
-      const unsigned long long word = wd[lane];
-      const int64_t w = t * kWordsPerTile + lane;
-      if (word && w < g.wpp) wb[w] |= word;
-      // these elements were not selected by the candidate select pass, so
-      // the tile's count grows by exactly their number
-      uint32_t pc = (uint32_t)__popcll(word);
-#pragma unroll
-      for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
-      if (lane == 0 && pc) tilecnt[(int64_t)p * g.tpp + t] += pc;
-      wave_lds_sync();
     }
-  }
+    wave_lds_sync();
+    const unsigned long long word = wd[lane];
+    const int64_t w = t * kWordsPerTile + lane;
+    if (word && w < g.wpp) wb[w] |= word;
+    // these elements were not selected by the candidate select pass, so the
+    // tile's count grows by exactly their number
+    uint32_t pc = (uint32_t)__popcll(word);
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
+    if (lane == 0 && pc) tilecnt[(int64_t)p * g.tpp + t] += pc;
+    wave_lds_sync();
+  });
   __syncthreads();
   block_min_into(kmin, &smin, &state[p].kth);
 }
@@ -514,12 +499,12 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
   level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[0].shift, g.levels[0].nbits,
                                              kScanLevel, capture_target(g));
   for (int l = 1; l < g.nlevels; ++l) {
-    cand_hist_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, w.hist, g.levels[l].shift,
-                                                         g.levels[l].nbits);
+    cand_hist_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, w.hist,
+                                                             g.levels[l].shift, g.levels[l].nbits);
     level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[l].shift, g.levels[l].nbits,
                                                kScanLevel, capture_target(g));
   }
-  mark_kernel<<<dim3(g.R, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, bits, w.tilecnt);
+  mark_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, bits, w.tilecnt);
   if (mark) mark(ctx, 2);
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
   scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, w.tilecnt, tile_off, w.state, meta_out);

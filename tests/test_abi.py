@@ -122,6 +122,11 @@ def test_component_validation():
     assert L.scape_adams_update(ctypes.byref(d), 10, FAKE, FAKE, FAKE, FAKE, mv, S.betas(beta2=1.0), 1e-3, 1,
                                 None) == 1
     assert L.scape_mask_overlap(ctypes.byref(d), 10, mv, mv, None, None) == 1
+    assert L.scape_dense_adams_step(ctypes.byref(d), FAKE, None, FAKE, FAKE, S.betas(), 1e-3, 1, None) == 1
+    assert L.scape_dense_adams_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, S.betas(eps=-1.0), 1e-3, 1, None) == 1
+    assert L.scape_dense_adams_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, S.betas(), 1e-3, 0, None) == 1
+    assert L.scape_dense_adams_step(ctypes.byref(S.dims(4097, 2, 1)), FAKE, FAKE, FAKE, FAKE, S.betas(), 1e-3, 1,
+                                    None) == 2
     assert L.scape_mask_topk(None, 10, FAKE, mv, FAKE, ws, None) == 1
 
 

@@ -172,6 +172,25 @@ def test_adams_update(S, t, wd):
         assert eq == n, f"{name}: {n - eq} entries not bitwise equal"
 
 
+@pytest.mark.parametrize("n,P,K", [(4 * 50_000, 4, 4), (30_001, 1, 3), (8, 2, 1), (4096 * 3 + 4, 2, 8)])
+def test_dense_adams_step(S, n, P, K):
+    """Dense AdamS on the worker mean (the pages' baseline) against the
+    oracle, four steps, bit for bit."""
+    rng = np.random.default_rng(n + K)
+    hp = O.Hyper.make(0.9, 0.95, 1e-8, 0.01, 1e-3)
+    w = (rng.standard_normal(n) * 0.02).astype(F32)
+    m, v = np.zeros(n, F32), np.zeros(n, F32)
+    w_t, m_t, v_t = dev(w), dev(m), dev(v)
+    for t in range(1, 5):
+        g = (rng.standard_normal((K, n)) * 10.0 ** rng.integers(-5, -1, (K, n))).astype(F32)
+        g_t = dev(g)
+        S.dense_adams_step(S.dims(n, P, K), w_t, g_t, m_t, v_t, S.betas(0.9, 0.95, 1e-8, 0.01), 1e-3, t)
+        O.dense_adams_step(w, m, v, g, hp, t)
+        torch.cuda.synchronize()
+        for name, got, want in (("w", w_t, w), ("m", m_t, m), ("v", v_t, v)):
+            assert np.array_equal(host(got).view(np.uint32), want.view(np.uint32)), f"step {t} {name}"
+
+
 def test_mask_overlap(S):
     P, n_p, k = 3, 9_000, 700
     rng = np.random.default_rng(9)

@@ -324,3 +324,21 @@ def test_mask_overlap_worked_example():
     prev = [np.array([0, 2, 4]), np.array([1, 3, 5])]
     nxt = [np.array([0, 2, 6]), np.array([7, 8, 9])]
     assert O.mask_overlap(prev, nxt, 3) == pytest.approx(2 / 6)
+
+
+def test_dense_adams_equals_scape_at_sparsity_zero():
+    """Dense AdamS on the worker mean equals the SCAPE step with every index
+    selected (e stays 0, so a = g), bit for bit, over several steps."""
+    P, K, n_p, T = 3, 4, 500, 5
+    rng = np.random.default_rng(11)
+    w0 = rng.standard_normal(P * n_p).astype(F32)
+    hp = O.Hyper.make(weight_decay=0.02)
+    opt = O.OracleOptimizer(w0, P, K, n_p, hp)
+    w, m, v = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
+    for t in range(1, T + 1):
+        g = (rng.standard_normal((K, P * n_p)) * 1e-2).astype(F32)
+        g[g == 0] = F32(1e-9)  # no signed zeros: g + (+0) is g bitwise
+        opt.step(g)
+        O.dense_adams_step(w, m, v, g, hp, t)
+        for name, a in (("w", w), ("m", m), ("v", v)):
+            assert np.array_equal(opt.gather(name).view(np.uint32), a.view(np.uint32)), name

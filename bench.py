@@ -110,6 +110,45 @@ def stream_calibration(torch, dev, log_fn):
             "ms": ms, "GBps": gbps}
 
 
+def fillin_study(S, W, cfg, seed, steps, log_fn):
+    """Fill-in of per-worker top-k: after `steps` SCAPE steps, each worker i
+    selects its own top-k of |g^i + e^i| per partition (the per-worker
+    selection the pages contrast with the shared partitioned mask); the
+    union of the first K' workers' masks is the global mask such a scheme
+    must synchronise.  Reports |union| / (P k) for K' = 1..K; SCAPE's shared
+    mask is exactly 1 by construction.  (The elementwise g + e for the study
+    is a torch add: it is analysis glue, not the optimizer path.)"""
+    import torch
+    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
+    dev = torch.device("cuda:0")
+    params = torch.empty(n, dtype=torch.float32, device=dev)
+    W.device_init_params(cfg, seed, params)
+    opt = S.ScapeOptimizer(params, P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    sigma = W.device_sigma(cfg, seed, dev)
+    g = torch.empty((K, n), dtype=torch.float32, device=dev)
+    for t in range(1, steps + 1):
+        W.device_grads(cfg, t, seed, sigma, g)
+        opt.step(g)
+    W.device_grads(cfg, steps + 1, seed, sigma, g)
+    d = opt.d
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
+    mv = S.mask_slot(d, k, blob, 0)
+    acc = torch.zeros_like(S.mask_slot_tensors(d, k, blob, 0)[0])
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    stat = torch.empty(n, dtype=torch.float32, device=dev)
+    dens = []
+    for i in range(K):
+        torch.add(g[i], opt.e[i], out=stat)
+        S.mask_topk(d, k, stat, mv, opt.ws)
+        S.mask_union(d, k, acc, mv, cnt)
+        dens.append(cnt.item() / (P * k))
+        log_fn(f"fill-in: workers 1..{i + 1}: union density {dens[-1]:.3f} x (P k)")
+    return {"metric": "fill-in of per-worker top-k masks: |union of K' workers' masks| / (P k)",
+            "workload": cfg.name, "after_steps": steps, "union_density": dens,
+            "shared_partitioned_mask_density": 1.0,
+            "data": "synthetic: independent gradients per worker (the no-correlation case)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +162,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap", action="store_true",
                     help="report |M_t ∩ M_{t+1}| / (P k) per step (untimed; on by default for the stress workload)")
+    ap.add_argument("--study", choices=["fillin"], default=None,
+                    help="run a study instead of the step benchmark")
     ap.add_argument("--calib", action="store_true",
                     help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
     args = ap.parse_args()
@@ -136,6 +177,10 @@ def main():
     from sparse_communication_distributed_amd import workload as W
 
     cfg = W.CONFIGS[args.config]
+    if args.study == "fillin":
+        S.lib()
+        print(json.dumps(fillin_study(S, W, cfg, args.seed, args.warmup + args.steps, log)), flush=True)
+        return
     args.overlap = args.overlap or cfg.grad_law == "stress_t3"
     cpu = None
     if not args.no_cpu_baseline:

@@ -206,6 +206,16 @@ scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const
 scape_status scape_mask_overlap(const scape_dims* dims, int64_t k, scape_mask_view a,
                                 scape_mask_view b, uint64_t* count_out, hipStream_t stream);
 
+/*
+ * Union of masks, for the fill-in effect of per-worker top-k ([P] §II-B:
+ * when each worker keeps its own top-k indices, the synchronised global mask
+ * is their union and fills in as workers are added; [S] §2, partitioned
+ * mask synchronisation avoids it): acc_bits (device, words laid out like a
+ * mask's bits) |= m.bits, then *count_out (device u64) = popcount(acc_bits).
+ */
+scape_status scape_mask_union(const scape_dims* dims, int64_t k, uint64_t* acc_bits, scape_mask_view m,
+                              uint64_t* count_out, hipStream_t stream);
+
 /* -------------------------------------------------------------- utility */
 
 const char* scape_status_string(scape_status s);

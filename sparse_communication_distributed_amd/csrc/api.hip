@@ -419,6 +419,15 @@ scape_status scape_mask_overlap(const scape_dims* dims, int64_t k, scape_mask_vi
   return hip_check(launch_overlap(g, a.bits, b.bits, count_out, stream), "overlap");
 }
 
+scape_status scape_mask_union(const scape_dims* dims, int64_t k, uint64_t* acc_bits, scape_mask_view m,
+                              uint64_t* count_out, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!acc_bits || !m.bits || !count_out) return fail(SCAPE_EINVAL, "null pointer argument");
+  return hip_check(launch_union(g, acc_bits, m.bits, count_out, stream), "union");
+}
+
 const char* scape_status_string(scape_status s) {
   switch (s) {
     case SCAPE_OK: return "ok";

@@ -166,6 +166,7 @@ hipError_t launch_reduce_adams(const Geom& g, const float* b, const uint32_t* id
                                float* m, float* v, float b1, float b2, float c1, float c2,
                                float ibc1, float ibc2, float eps, float wd, float lr,
                                hipStream_t s);
+hipError_t launch_union(const Geom& g, uint64_t* acc, const uint64_t* m, uint64_t* out, hipStream_t s);
 hipError_t launch_overlap(const Geom& g, const uint64_t* a, const uint64_t* b, uint64_t* out,
                           hipStream_t s);
 

@@ -461,6 +461,21 @@ overlap_kernel(const uint64_t* __restrict__ a, const uint64_t* __restrict__ b, i
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
 
+// acc |= m over all mask words; *out += popcount of the result.
+__global__ void __launch_bounds__(kThreads)
+union_kernel(uint64_t* __restrict__ acc, const uint64_t* __restrict__ m, int64_t nwords,
+             unsigned long long* __restrict__ out) {
+  uint64_t c = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * kThreads) {
+    const uint64_t u = acc[i] | m[i];
+    acc[i] = u;
+    c += (uint64_t)__popcll(u);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+  if (lane_id() == 0 && c) atomicAdd(out, (unsigned long long)c);
+}
+
 // kCaptureMargin * k, at most n_p.
 uint32_t capture_target(const Geom& g) {
   double t = kCaptureMargin * (double)g.k;
@@ -509,6 +524,16 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
   scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, w.tilecnt, tile_off, w.state, meta_out);
   write_idx_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const Geom& g, uint64_t* acc, const uint64_t* m, uint64_t* out, hipStream_t s) {
+  zero_u64_kernel<<<1, 1, 0, s>>>(reinterpret_cast<unsigned long long*>(out));
+  const int64_t nwords = (int64_t)g.P * g.wpp;
+  int64_t blocks = (nwords + kThreads - 1) / kThreads;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  union_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(acc, m, nwords, reinterpret_cast<unsigned long long*>(out));
   return hipGetLastError();
 }
 

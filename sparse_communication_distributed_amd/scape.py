@@ -54,6 +54,7 @@ _SIGS = {
     "scape_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p]),
     "scape_mask_overlap": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, MaskView, c_void_p, c_void_p]),
+    "scape_mask_union": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, MaskView, c_void_p, c_void_p]),
     "scape_dense_adams_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, Betas, c_float,
                                        c_int64, c_void_p]),
     "scape_status_string": (c_char_p, [c_int]),
@@ -188,6 +189,10 @@ def step(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: floa
     _check(lib().scape_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
                             _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mask_union(d: Dims, k: int, acc_bits, m: MaskView, count_out, stream=None) -> None:
+    _check(lib().scape_mask_union(ctypes.byref(d), k, _ptr(acc_bits), m, _ptr(count_out), _stream(stream)))
 
 
 def dense_adams_step(d: Dims, params, grads, m, v, bt: Betas, lr: float, step_no: int, stream=None) -> None:

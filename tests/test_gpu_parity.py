@@ -191,6 +191,31 @@ def test_dense_adams_step(S, n, P, K):
             assert np.array_equal(host(got).view(np.uint32), want.view(np.uint32)), f"step {t} {name}"
 
 
+def test_mask_union_fill_in(S):
+    """Union of per-worker top-k masks (the fill-in of per-worker
+    selection) against the oracle's per-worker top-k."""
+    P, K, n_p, k = 3, 4, 7_000, 350
+    rng = np.random.default_rng(21)
+    a = (rng.standard_normal((K, P * n_p)) * 1e-3).astype(F32)
+    d = S.dims(P * n_p, P, K)
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+    mv = S.mask_slot(d, k, blob, 0)
+    acc = torch.zeros_like(S.mask_slot_tensors(d, k, blob, 0)[0])
+    cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    union = [set() for _ in range(P)]
+    for i in range(K):
+        ai = dev(a[i])
+        S.mask_topk(d, k, ai, mv, ws)
+        S.mask_union(d, k, acc, mv, cnt)
+        torch.cuda.synchronize()
+        for p, sel in enumerate(oracle_topk_local(a[i], P, n_p, k)):
+            union[p] |= set(sel.tolist())
+        assert int(cnt.item()) == sum(len(u) for u in union)
+    want = pack_mask([np.array(sorted(u)) for u in union], n_p)[0]
+    assert np.array_equal(host(acc).view(np.uint64), want)
+
+
 def test_mask_overlap(S):
     P, n_p, k = 3, 9_000, 700
     rng = np.random.default_rng(9)

@@ -149,6 +149,60 @@ def fillin_study(S, W, cfg, seed, steps, log_fn):
             "data": "synthetic: independent gradients per worker (the no-correlation case)"}
 
 
+def offload_bench(S, W, cfg, args, log_fn):
+    """The step with the error-feedback buffers in pinned host memory,
+    staged through the device in chunks of partitions (two copy streams,
+    double buffered).  Timed like the main benchmark."""
+    import torch
+    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
+    dev = torch.device("cuda:0")
+    d = S.dims(n, P, K)
+    bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
+    params = torch.empty(n, dtype=torch.float32, device=dev)
+    W.device_init_params(cfg, args.seed, params)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    log_fn(f"pinning {K * n * 4 / 1e9:.1f} GB of host memory for e")
+    e_host = torch.zeros((K, n), dtype=torch.float32, pin_memory=True)
+    mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+    stage = torch.empty(S.offload_stage_bytes(d, k, args.offload), dtype=torch.uint8, device=dev)
+    sigma = W.device_sigma(cfg, args.seed, dev)
+    pool = []
+    for s_ in range(args.pool):
+        gset = torch.empty((K, n), dtype=torch.float32, device=dev)
+        W.device_grads(cfg, s_ + 1, args.seed, sigma, gset)
+        pool.append(gset)
+    del sigma
+    stream = torch.cuda.current_stream()
+    cin, cout = torch.cuda.Stream(), torch.cuda.Stream()
+    t = 0
+
+    def one_step():
+        nonlocal t
+        t += 1
+        S.step_offload(d, params, pool[(t - 1) % len(pool)], m, v, e_host, mask, k, bt, cfg.lr, t, ws, stage,
+                       args.offload, stream, cin, cout)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    link = 2 * K * n * 4 / (ms * 1e-3) / 1e9
+    log_fn(f"offload ({args.offload} partitions per chunk): {ms:.2f} ms/step, {link:.1f} GB/s over the host link")
+    return {"metric": "optimizer-step params/s with e offloaded to pinned host memory",
+            "value": n / (ms * 1e-3), "unit": "params/s", "ms_per_step": ms, "steps": args.steps,
+            "warmup": args.warmup, "chunk_parts": args.offload, "host_link_gbps_both_directions": link,
+            "bytes_over_link_per_step": 2 * K * n * 4, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": cfg.name, "n_params": n, "partitions": P, "workers": K, "k_per_partition": k}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +216,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap", action="store_true",
                     help="report |M_t ∩ M_{t+1}| / (P k) per step (untimed; on by default for the stress workload)")
+    ap.add_argument("--offload", type=int, default=0, metavar="CHUNK_PARTS",
+                    help="keep e in pinned host memory, staged in chunks of this many partitions")
     ap.add_argument("--study", choices=["fillin"], default=None,
                     help="run a study instead of the step benchmark")
     ap.add_argument("--calib", action="store_true",
@@ -180,6 +236,10 @@ def main():
     if args.study == "fillin":
         S.lib()
         print(json.dumps(fillin_study(S, W, cfg, args.seed, args.warmup + args.steps, log)), flush=True)
+        return
+    if args.offload:
+        S.lib()
+        print(json.dumps(offload_bench(S, W, cfg, args, log)), flush=True)
         return
     args.overlap = args.overlap or cfg.grad_law == "stress_t3"
     cpu = None

@@ -199,6 +199,29 @@ scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const
                                    float* v, scape_betas betas, float lr, int64_t step, hipStream_t stream);
 
 /*
+ * Error-feedback buffers offloaded to pinned host memory, with double
+ * buffering ([P] §I: the EF buffers live in CPU memory, moved over the
+ * CPU-GPU link; [S] §2 "Ottimizzazione della Memoria": CPU offload with
+ * double buffering).  Same step and results as scape_step, except that
+ * e_host ([K][n] fp32) is pinned host memory (hipHostMalloc, device
+ * accessible).  The pass over e runs on chunks of chunk_parts partitions:
+ * chunk c+1 is copied in on copy_in and chunk c-1 copied out on copy_out
+ * while chunk c is processed on `stream`, through `stage`, a device buffer
+ * of scape_offload_stage_bytes() bytes (two chunks).  The step-1 bootstrap
+ * and the exact recount of the selection read e_host directly.  The three
+ * streams must be distinct; `stream` waits for the last copy-out before
+ * the call's selection work, so later work on `stream` sees the new e_host.
+ * Uses a process-wide set of HIP events (not thread-safe across concurrent
+ * offload calls).
+ */
+size_t scape_offload_stage_bytes(const scape_dims* dims, int64_t k, int32_t chunk_parts);
+scape_status scape_step_offload(const scape_dims* dims, float* params, const float* grads, float* m,
+                                float* v, float* e_host, void* mask_blob, int64_t k, scape_betas betas,
+                                float lr, int64_t step, void* workspace, size_t workspace_bytes, void* stage,
+                                size_t stage_bytes, int32_t chunk_parts, hipStream_t stream,
+                                hipStream_t copy_in, hipStream_t copy_out);
+
+/*
  * Overlap of two masks: *count_out (device u64) = |A ∩ B| summed over all
  * partitions (the consecutive-step mask stability the [P] §I insight
  * rests on; divide by P*k for the fraction).  Reads a.bits and b.bits.

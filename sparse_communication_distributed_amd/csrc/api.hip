@@ -316,12 +316,29 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
                    "adams");
 }
 
-scape_status scape_step(const scape_dims* dims, float* params, const float* grads, float* m,
+}  // extern "C"
+
+namespace {
+
+// Everything of one step except the pass over the error-feedback buffers:
+// validation, the step-1 bootstrap, and (after the pass) level 1, the exact
+// fallback and the selection of M_{t+1}.  `e` is where the fallback and the
+// bootstrap read the error-feedback rows ([K][n]).
+struct StepCtx {
+  Geom g;
+  Ws w;
+  scape_mask_view cur, nxt;
+  StatArgs a;
+  StepArgs sa;
+  bool vec;
+};
+
+scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const float* grads, float* m,
                         float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
                         int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Geom g;
-  scape_status st = check_dims(dims, k, &g);
+  scape_status st = check_dims(dims, k, &c.g);
   if (st) return st;
+  const Geom& g = c.g;
   if (!params || !grads || !m || !v || !e || !mask_blob || !workspace)
     return fail(SCAPE_EINVAL, "null pointer argument");
   if ((st = check_betas(betas, lr))) return st;
@@ -329,42 +346,34 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   if (workspace_bytes < g.ws_total)
     return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
 
-  Ws w = ws_view(g, workspace);
-  const scape_mask_view cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
-  const scape_mask_view nxt = slot_view(g, mask_blob, (int)(step & 1));
-  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m);
+  c.w = ws_view(g, workspace);
+  c.cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
+  c.nxt = slot_view(g, mask_blob, (int)(step & 1));
+  c.vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m);
   const float b1 = betas.beta1, b2 = betas.beta2;
   const float c1 = 1.0f - b1, c2 = 1.0f - b2;
-  const bool prof = g_prof.on;
-  StatArgs a{};
+  StatArgs& a = c.a;
+  a = StatArgs{};
   a.m = m;
   a.grads = grads;
   a.e = e;
-  a.b = w.b;
-  a.mold = kFuseAdams ? w.mold : nullptr;  // m is updated before the selection only when fused
-  a.bits = cur.bits;
-  a.tile_off = cur.tile_off;
+  a.b = c.w.b;
+  a.mold = kFuseAdams ? c.w.mold : nullptr;  // m is updated before the selection only when fused
+  a.bits = c.cur.bits;
+  a.tile_off = c.cur.tile_off;
   a.b1 = b1;
   a.c1 = c1;
-
-  if (step == 1) {  // bootstrap: M_1 = top-k of the step-1 statistic
-    g_prof.begin(ST_BOOT, stream);
-    StatArgs boot = a;
-    boot.mold = nullptr;
-    if ((st = run_fresh_select(g, w, kSrcState, boot, vec, cur, stream))) return st;
-  }
-  g_prof.begin(ST_PASS, stream);
-  if ((st = hip_check(launch_zero_u32(w.sel.hist, (int64_t)g.P * kBins, stream), "zero"))) return st;
-  StepArgs sa{};
+  StepArgs& sa = c.sa;
+  sa = StepArgs{};
   sa.grads = grads;
   sa.e = e;
-  sa.bits = cur.bits;
-  sa.tile_off = cur.tile_off;
-  sa.b = w.b;
+  sa.bits = c.cur.bits;
+  sa.tile_off = c.cur.tile_off;
+  sa.b = c.w.b;
   sa.m = m;
   sa.v = kFuseAdams ? v : nullptr;
   sa.w = kFuseAdams ? params : nullptr;
-  sa.mold = kFuseAdams ? w.mold : nullptr;
+  sa.mold = kFuseAdams ? c.w.mold : nullptr;
   sa.b1 = b1;
   sa.b2 = b2;
   sa.c1 = c1;
@@ -374,24 +383,148 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   sa.eps = betas.eps;
   sa.wd = betas.weight_decay;
   sa.lr = lr;
-  sa.lo = cur.meta + g.P;
-  sa.cand = w.sel.cand;
-  sa.cnt1 = w.sel.cnt1;
-  sa.hist = w.sel.hist;
-  if ((st = hip_check(launch_step_pass(g, sa, vec && aligned16(params) && aligned16(v), stream), "step pass")))
-    return st;
+  sa.lo = c.cur.meta + g.P;
+  sa.cand = c.w.sel.cand;
+  sa.cnt1 = c.w.sel.cnt1;
+  sa.hist = c.w.sel.hist;
+  sa.p0 = 0;
+  sa.nparts = g.P;
+  sa.e_stride = g.n;
+
+  if (step == 1) {  // bootstrap: M_1 = top-k of the step-1 statistic
+    g_prof.begin(ST_BOOT, stream);
+    StatArgs boot = a;
+    boot.mold = nullptr;
+    if ((st = run_fresh_select(g, c.w, kSrcState, boot, c.vec, c.cur, stream))) return st;
+  }
+  g_prof.begin(ST_PASS, stream);
+  return hip_check(launch_zero_u32(c.w.sel.hist, (int64_t)g.P * kBins, stream), "zero");
+}
+
+scape_status step_end(StepCtx& c, float* params, float* m, float* v, scape_betas betas, float lr,
+                      hipStream_t stream) {
+  const Geom& g = c.g;
+  scape_status st;
   g_prof.begin(ST_SELECT, stream);
-  if ((st = hip_check(launch_level1(g, w.sel, kScanCheck, stream), "level 1"))) return st;
-  if ((st = run_fallback(g, w, kSrcMasked, a, vec, stream))) return st;
-  if ((st = run_tail(g, w, nxt, stream, prof))) return st;
+  if ((st = hip_check(launch_level1(g, c.w.sel, kScanCheck, stream), "level 1"))) return st;
+  if ((st = run_fallback(g, c.w, kSrcMasked, c.a, c.vec, stream))) return st;
+  if ((st = run_tail(g, c.w, c.nxt, stream, g_prof.on))) return st;
   if (!kFuseAdams) {
     g_prof.begin(ST_ADAMS, stream);
-    st = hip_check(launch_reduce_adams(g, w.b, cur.idx, params, m, v, b1, b2, c1, c2, sa.ibc1, sa.ibc2,
-                                       betas.eps, betas.weight_decay, lr, stream),
+    st = hip_check(launch_reduce_adams(g, c.w.b, c.cur.idx, params, m, v, c.sa.b1, c.sa.b2, c.sa.c1, c.sa.c2,
+                                       c.sa.ibc1, c.sa.ibc2, betas.eps, betas.weight_decay, lr, stream),
                    "reduce_adams");
   }
   g_prof.end();
   return st;
+}
+
+// Events of the offload pipeline, created once per process: per stage
+// buffer, "copied in", "pass done" and "copied out", plus the call's start.
+struct OffloadEvents {
+  bool ready = false;
+  hipEvent_t in[2], pass[2], out[2], start;
+};
+OffloadEvents g_oev;
+
+scape_status offload_events() {
+  if (g_oev.ready) return SCAPE_OK;
+  hipEvent_t* all[7] = {&g_oev.in[0], &g_oev.in[1], &g_oev.pass[0], &g_oev.pass[1],
+                        &g_oev.out[0], &g_oev.out[1], &g_oev.start};
+  for (hipEvent_t* e : all) {
+    scape_status st = hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "offload events");
+    if (st) return st;
+  }
+  g_oev.ready = true;
+  return SCAPE_OK;
+}
+
+int64_t chunk_parts_of(const Geom& g, int32_t chunk_parts) {
+  return chunk_parts < 1 ? 0 : (chunk_parts > g.P ? g.P : chunk_parts);
+}
+
+}  // namespace
+
+extern "C" {
+
+scape_status scape_step(const scape_dims* dims, float* params, const float* grads, float* m,
+                        float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
+                        int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  StepCtx c;
+  scape_status st = step_begin(c, dims, params, grads, m, v, e, mask_blob, k, betas, lr, step, workspace,
+                               workspace_bytes, stream);
+  if (st) return st;
+  const bool vec = c.vec && aligned16(params) && aligned16(v);
+  if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, stream), "step pass"))) return st;
+  return step_end(c, params, m, v, betas, lr, stream);
+}
+
+size_t scape_offload_stage_bytes(const scape_dims* dims, int64_t k, int32_t chunk_parts) {
+  Geom g;
+  if (!dims || !make_geom(dims->n, dims->num_partitions, dims->num_workers, k, &g)) return 0;
+  const int64_t cp = chunk_parts_of(g, chunk_parts);
+  return cp ? 2 * (size_t)g.K * (size_t)cp * (size_t)g.n_p * 4 : 0;
+}
+
+scape_status scape_step_offload(const scape_dims* dims, float* params, const float* grads, float* m,
+                                float* v, float* e_host, void* mask_blob, int64_t k, scape_betas betas,
+                                float lr, int64_t step, void* workspace, size_t workspace_bytes, void* stage,
+                                size_t stage_bytes, int32_t chunk_parts, hipStream_t stream,
+                                hipStream_t copy_in, hipStream_t copy_out) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  const int64_t cp = chunk_parts_of(g, chunk_parts);
+  if (cp == 0) return fail(SCAPE_EINVAL, "chunk_parts must be >= 1");
+  if (!stage) return fail(SCAPE_EINVAL, "null pointer argument");
+  const size_t need = scape_offload_stage_bytes(dims, k, chunk_parts);
+  if (stage_bytes < need) return fail(SCAPE_EWORKSPACE, "stage has %zu bytes, needs %zu", stage_bytes, need);
+  StepCtx c;
+  if ((st = step_begin(c, dims, params, grads, m, v, e_host, mask_blob, k, betas, lr, step, workspace,
+                       workspace_bytes, stream)))
+    return st;
+  if ((st = offload_events())) return st;
+  const int64_t n_p = g.n_p, chunk = cp * n_p;
+  float* sbuf[2] = {static_cast<float*>(stage), static_cast<float*>(stage) + (size_t)g.K * chunk};
+  const bool vec = c.vec && aligned16(params) && aligned16(v) && aligned16(stage) && (chunk % 4 == 0);
+  // the copies of this call follow everything already on the compute stream
+  if ((st = hip_check(hipEventRecord(g_oev.start, stream), "offload record"))) return st;
+  if ((st = hip_check(hipStreamWaitEvent(copy_in, g_oev.start, 0), "offload wait"))) return st;
+  const int64_t nchunks = (g.P + cp - 1) / cp;
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const int b = (int)(ci & 1);
+    const int64_t p0 = ci * cp;
+    const int64_t np = (p0 + cp <= g.P) ? cp : g.P - p0;
+    // stage buffer b is free once the copy-out of chunk ci - 2 is done
+    if (ci >= 2 && (st = hip_check(hipStreamWaitEvent(copy_in, g_oev.out[b], 0), "offload wait"))) return st;
+    for (int i = 0; i < g.K; ++i) {
+      st = hip_check(hipMemcpyAsync(sbuf[b] + (size_t)i * chunk, e_host + (size_t)i * g.n + (size_t)p0 * n_p,
+                                    (size_t)np * n_p * 4, hipMemcpyHostToDevice, copy_in),
+                     "offload copy in");
+      if (st) return st;
+    }
+    if ((st = hip_check(hipEventRecord(g_oev.in[b], copy_in), "offload record"))) return st;
+    if ((st = hip_check(hipStreamWaitEvent(stream, g_oev.in[b], 0), "offload wait"))) return st;
+    StepArgs sa = c.sa;
+    sa.e = sbuf[b];
+    sa.p0 = (int)p0;
+    sa.nparts = (int)np;
+    sa.e_stride = chunk;
+    if ((st = hip_check(launch_step_pass(g, sa, vec, stream), "step pass"))) return st;
+    if ((st = hip_check(hipEventRecord(g_oev.pass[b], stream), "offload record"))) return st;
+    if ((st = hip_check(hipStreamWaitEvent(copy_out, g_oev.pass[b], 0), "offload wait"))) return st;
+    for (int i = 0; i < g.K; ++i) {
+      st = hip_check(hipMemcpyAsync(e_host + (size_t)i * g.n + (size_t)p0 * n_p, sbuf[b] + (size_t)i * chunk,
+                                    (size_t)np * n_p * 4, hipMemcpyDeviceToHost, copy_out),
+                     "offload copy out");
+      if (st) return st;
+    }
+    if ((st = hip_check(hipEventRecord(g_oev.out[b], copy_out), "offload record"))) return st;
+  }
+  // the selection's fallback reads e_host: wait for every copy-out
+  for (int b = 0; b < 2 && b < nchunks; ++b)
+    if ((st = hip_check(hipStreamWaitEvent(stream, g_oev.out[b], 0), "offload wait"))) return st;
+  return step_end(c, params, m, v, betas, lr, stream);
 }
 
 scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const float* grads, float* m,

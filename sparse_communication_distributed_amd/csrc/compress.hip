@@ -129,7 +129,7 @@ constexpr bool kPartitionFastest = false;
 __device__ __forceinline__ int block_part() { return kPartitionFastest ? blockIdx.x : blockIdx.y; }
 __device__ __forceinline__ int block_in_part() { return kPartitionFastest ? blockIdx.y : blockIdx.x; }
 __device__ __forceinline__ int blocks_per_part() { return kPartitionFastest ? gridDim.y : gridDim.x; }
-inline dim3 stream_grid(const Geom& g, int G) { return kPartitionFastest ? dim3(g.P, G) : dim3(G, g.P); }
+inline dim3 stream_grid(int nparts, int G) { return kPartitionFastest ? dim3(nparts, G) : dim3(G, nparts); }
 
 struct AdamsC {
   float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, invK;
@@ -159,13 +159,16 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 float* __restrict__ b, float* __restrict__ m, float* __restrict__ v,
                 float* __restrict__ w, float* __restrict__ mold, AdamsC ac,
                 const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
-                uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist) {
+                uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int p0, int64_t e_stride) {
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[STEP ? kBins : 1];
   __shared__ uint32_t tcnt;
   if (STEP) hist_zero(sh);
-  const int p = block_part();
+  // partitions p0 .. p0 + nparts - 1; e holds their rows [K][nparts * n_p]
+  // with rows e_stride apart (e_stride = n and p0 = 0 for the resident buffer)
+  const int p = p0 + block_part();
+  const int64_t ebase = (int64_t)(p - p0) * g.n_p;
   const int64_t pbase = (int64_t)p * g.n_p;
   const int64_t wbase = (int64_t)p * g.wpp;
   const int64_t pk = (int64_t)g.P * g.k;
@@ -205,7 +208,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
       }
       for (int i = 0; i < g.K; ++i) {
         const float* gi = grads + (int64_t)i * g.n + pbase;
-        float* ei = e + (int64_t)i * g.n + pbase;
+        float* ei = e + (int64_t)i * e_stride + ebase;
         float* bi = b + (int64_t)i * pk;
         float ga[kChunkGroup][4], ea[kChunkGroup][4];
 #pragma unroll
@@ -400,7 +403,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
 
 template <int SRC, int PHASE>
 void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
-  const dim3 grid = stream_grid(g, g.Gs);
+  const dim3 grid = stream_grid(g.P, g.Gs);
   if (vec)
     stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
@@ -423,40 +426,40 @@ hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, boo
 
 hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
                            const uint32_t* tile_off, float* b, hipStream_t s, bool vec) {
-  const dim3 grid = stream_grid(g, g.G);
+  const dim3 grid = stream_grid(g.P, g.G);
   AdamsC ac{};
   if (vec)
     compress_kernel<false, false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
                                                                   nullptr, nullptr, ac, nullptr, nullptr, nullptr,
-                                                                  nullptr);
+                                                                  nullptr, 0, g.n);
   else
     compress_kernel<false, false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr,
                                                                    nullptr, nullptr, nullptr, ac, nullptr, nullptr,
-                                                                   nullptr, nullptr);
+                                                                   nullptr, nullptr, 0, g.n);
   return hipGetLastError();
 }
 
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s) {
-  const dim3 grid = stream_grid(g, g.G);
+  const dim3 grid = stream_grid(a.nparts, g.G);
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
   if (a.w != nullptr) {  // with AdamS fused
     if (vec)
       compress_kernel<true, true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
                                                                   a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1,
-                                                                  a.hist);
+                                                                  a.hist, a.p0, a.e_stride);
     else
       compress_kernel<true, true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
                                                                    a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1,
-                                                                   a.hist);
+                                                                   a.hist, a.p0, a.e_stride);
   } else {
     if (vec)
       compress_kernel<true, false, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
                                                                    nullptr, nullptr, nullptr, ac, a.lo, a.cand,
-                                                                   a.cnt1, a.hist);
+                                                                   a.cnt1, a.hist, a.p0, a.e_stride);
     else
       compress_kernel<true, false, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b,
                                                                     a.m, nullptr, nullptr, nullptr, ac, a.lo,
-                                                                    a.cand, a.cnt1, a.hist);
+                                                                    a.cand, a.cnt1, a.hist, a.p0, a.e_stride);
   }
   return hipGetLastError();
 }

@@ -134,6 +134,8 @@ struct StepArgs {
   uint64_t* cand;
   uint32_t* cnt1;
   uint32_t* hist;
+  int p0, nparts;            // partitions of this launch
+  int64_t e_stride;          // elements between the worker rows of e
 };
 
 hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, bool vec, hipStream_t s);

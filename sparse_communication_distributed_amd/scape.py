@@ -54,6 +54,10 @@ _SIGS = {
     "scape_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p]),
     "scape_mask_overlap": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, MaskView, c_void_p, c_void_p]),
+    "scape_offload_stage_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64, c_int32]),
+    "scape_step_offload": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p, c_size_t, c_int32,
+                                   c_void_p, c_void_p, c_void_p]),
     "scape_mask_union": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, MaskView, c_void_p, c_void_p]),
     "scape_dense_adams_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, Betas, c_float,
                                        c_int64, c_void_p]),
@@ -189,6 +193,21 @@ def step(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: floa
     _check(lib().scape_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
                             _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def offload_stage_bytes(d: Dims, k: int, chunk_parts: int) -> int:
+    return int(lib().scape_offload_stage_bytes(ctypes.byref(d), k, chunk_parts))
+
+
+def step_offload(d: Dims, params, grads, m, v, e_host, mask_blob, k: int, bt: Betas, lr: float, step_no: int,
+                 workspace, stage, chunk_parts: int, stream=None, copy_in=None, copy_out=None) -> None:
+    """scape_step with e_host ([K][n] fp32, pinned host memory) staged
+    through `stage` in chunks of chunk_parts partitions on two copy streams."""
+    _check(lib().scape_step_offload(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e_host),
+                                    _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(stage),
+                                    stage.numel() * stage.element_size(), chunk_parts, _stream(stream),
+                                    _stream(copy_in), _stream(copy_out)))
 
 
 def mask_union(d: Dims, k: int, acc_bits, m: MaskView, count_out, stream=None) -> None:

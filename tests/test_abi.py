@@ -130,6 +130,23 @@ def test_component_validation():
     assert L.scape_mask_topk(None, 10, FAKE, mv, FAKE, ws, None) == 1
 
 
+def test_offload_validation():
+    L = S.lib()
+    d = S.dims(4096, 4, 2)
+    assert S.offload_stage_bytes(d, 10, 0) == 0
+    assert S.offload_stage_bytes(d, 10, 3) == 2 * 2 * 3 * 1024 * 4
+    assert S.offload_stage_bytes(d, 10, 9) == 2 * 2 * 4 * 1024 * 4   # at most P partitions per chunk
+    wsb = S.workspace_bytes(d, 10)
+    sb = S.offload_stage_bytes(d, 10, 2)
+    def call(chunk=2, stage=FAKE, stage_bytes=sb, e=FAKE):
+        return L.scape_step_offload(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, e, FAKE, 10, S.betas(), 1e-3, 1, FAKE,
+                                    wsb, stage, stage_bytes, chunk, None, None, None)
+    assert call(chunk=0) == 1
+    assert call(stage=None) == 1
+    assert call(stage_bytes=sb - 1) == 3
+    assert call(e=None) == 1
+
+
 def test_status_strings_and_profile_names():
     L = S.lib()
     assert L.scape_status_string(0) == b"ok"

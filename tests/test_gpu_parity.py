@@ -368,3 +368,39 @@ def test_threshold_record(S):
         step = (1 << 7) if (lo >> 19) == (kth >> 19) else (1 << 19)
         assert lo % step == 0
         assert np.count_nonzero(kp >= lo + step) < target
+
+
+@pytest.mark.parametrize("chunk_parts,poison", [(1, False), (2, False), (3, False), (5, False), (2, True)])
+def test_step_offload_matches_oracle(S, chunk_parts, poison):
+    """Error-feedback buffers in pinned host memory, staged in chunks of
+    partitions through two copy streams: the same result as the oracle, bit
+    for bit (5 partitions: ragged last chunks for 2 and 3; with the capture
+    bounds poisoned, the exact recount reads the host buffers)."""
+    cfg = W.flat_config("offload", 5 * 12_000, 5, 3, "0.99", steps=4)
+    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
+    w0 = W.init_params(cfg)
+    hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    ora = O.OracleOptimizer(w0, P, K, k, hp)
+    d = S.dims(n, P, K)
+    params = dev(w0)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    e_host = torch.zeros((K, n), dtype=torch.float32, pin_memory=True)
+    mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+    stage = torch.empty(S.offload_stage_bytes(d, k, chunk_parts), dtype=torch.uint8, device=DEV)
+    cin, cout = torch.cuda.Stream(), torch.cuda.Stream()
+    for t in range(1, cfg.steps + 1):
+        g = W.grads(cfg, t)
+        if poison and t >= 2:
+            meta = S.mask_slot_meta(d, k, mask, (t - 1) & 1)
+            meta[P:].fill_(0x7F800000)
+        S.step_offload(d, params, dev(g), m, v, e_host, mask, k, S.betas(), cfg.lr, t, ws, stage, chunk_parts,
+                       copy_in=cin, copy_out=cout)
+        outs = ora.step(g)
+        torch.cuda.synchronize()
+        bits, idx, toff = S.mask_slot_tensors(d, k, mask, t & 1)
+        check_mask(bits, idx, toff, [o["nxt"] for o in outs], cfg.n_p)
+        for name, got, want in (("w", params, ora.gather("w")), ("m", m, ora.gather("m")),
+                                ("v", v, ora.gather("v")), ("e", e_host, ora.gather("e"))):
+            assert np.array_equal(host(got).view(np.uint32), want.view(np.uint32)), f"step {t} {name}"

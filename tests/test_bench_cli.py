@@ -1,0 +1,63 @@
+"""bench.py's command line and the profile summarizer, on the CPU."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_formula():
+    sys.path.insert(0, ROOT)
+    import bench
+    # Llama-1.8B layout, 99% sparsity: 94.49 GB per step
+    n, P, K, k = 1_775_372_288, 32, 4, 554_803
+    assert abs(bench.alg_bytes_step(n, P, K, k) / 1e9 - 94.494) < 0.01
+    # the step pass moves everything except the emitted index list and the read-back of b
+    assert bench.alg_bytes_step_pass(n, P, K, k) < bench.alg_bytes_step(n, P, K, k)
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_prof_summary_scales_counters_by_the_copy(tmp_path):
+    stats = tmp_path / "stats.csv"
+    _write_csv(stats, ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+               [["compress_kernel", 3, 60e6, 20e6, 90.0, 19e6, 21e6, 1.0]])
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    # the calibration copy reads 1 GiB but its FETCH_SIZE counter shows half of it
+    _write_csv(fetch, hdr, [["__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288],
+                            ["compress_kernel", "FETCH_SIZE", 999], ["compress_kernel", "FETCH_SIZE", 1000],
+                            ["compress_kernel", "FETCH_SIZE", 1000]])
+    _write_csv(write, hdr, [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576],
+                            ["compress_kernel", "WRITE_SIZE", 7], ["compress_kernel", "WRITE_SIZE", 500],
+                            ["compress_kernel", "WRITE_SIZE", 500]])
+    out = tmp_path / "prof"
+    r = subprocess.run([sys.executable, "-m", "sparse_communication_distributed_amd.prof_summary", "--stats", str(stats),
+                        "--fetch", str(fetch), "--write", str(write), "--workload", "x", "--out", str(out)],
+                       cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    doc = json.load(open(str(out) + "_counters.json"))
+    assert doc["fetch_scale"] == pytest.approx(2.0)
+    assert doc["write_scale"] == pytest.approx(1.0)
+    # first launch skipped; KiB -> bytes, scaled
+    assert doc["hbm_read_bytes_per_launch"] == pytest.approx(1000 * 1024 * 2.0)
+    assert doc["hbm_write_bytes_per_launch"] == pytest.approx(500 * 1024)
+    assert "compress_kernel" in open(str(out) + ".md").read()

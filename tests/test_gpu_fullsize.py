@@ -56,8 +56,8 @@ def check_all_partitions(S, opt, cfg):
     assert torch.equal(toff.view(P, T).to(torch.int64), want), "tile offsets differ"
 
 
-def run_fullsize(S, name, steps, parts, seed=0):
-    cfg = W.CONFIGS[name]
+def run_fullsize(S, name, steps, parts, seed=0, cfg=None):
+    cfg = W.CONFIGS[name] if cfg is None else cfg
     n, P, K, k, n_p = cfg.n, cfg.P, cfg.K, cfg.k, cfg.n_p
     print(f"[fullsize] {name}: n={n} P={P} K={K} k={k} steps={steps} parts={parts}", flush=True)
     params = torch.empty(n, dtype=torch.float32, device=DEV)
@@ -109,4 +109,15 @@ def run_fullsize(S, name, steps, parts, seed=0):
 ])
 def test_fullsize_parity(S, name, steps, parts):
     run_fullsize(S, name, steps, parts)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_maximum_size_u32_indices(S):
+    """n just under 2^32 (the largest the 32-bit index list allows), one
+    worker, 64 partitions: the last partition's global indices come within
+    256 of 2^32.  Sampled partitions replayed on the oracle, bit for bit."""
+    n = (1 << 32) - 256
+    cfg = W.flat_config("maxsize", n, 64, 1, "0.99", steps=2, config_id=7)
+    run_fullsize(S, "maxsize", 2, (0, 63), cfg=cfg)
     torch.cuda.empty_cache()

@@ -273,6 +273,8 @@ def test_step_tiny_20_steps(S):
     (20_000, 4, 2, "0.999", "stress_t3"),      # duplicate magnitudes -> exact ties
     (4096, 6, 4, "0.5", "partition_scale"),
     (64, 3, 5, "0.9", "tensor_sigma"),         # K > P: some workers own nothing
+    (37, 20_000, 3, "0.9", "tensor_sigma"),    # 20000 ragged one-tile partitions (grid y = 20000)
+    (100, 7, 16, "0.95", "tensor_sigma"),      # 16 workers
 ])
 def test_step_small_shapes(S, n_p, P, K, sp, law):
     cfg = W.flat_config("small", P * n_p, P, K, sp, steps=4, grad_law=law, weight_decay=0.01)

@@ -57,57 +57,6 @@ adams_kernel(const float* __restrict__ bbar, const uint32_t* __restrict__ idx, i
     adams_one(idx[r], bbar[r], w, m, v, c);
 }
 
-// Each thread takes 4 consecutive entries and issues every gather (the
-// index, the K buffer values, then m[j] and w[j]) before any arithmetic, so
-// that the scattered 64-byte reads of m and w overlap.
-constexpr int kAdamsUnroll = 4;
-
-__global__ void __launch_bounds__(kThreads)
-reduce_adams_kernel(const float* __restrict__ b, int K, float invK, const uint32_t* __restrict__ idx,
-                    int64_t pk, float* __restrict__ w, float* __restrict__ m, float* __restrict__ v,
-                    AdamsK c) {
-  const int64_t step = (int64_t)gridDim.x * kThreads * kAdamsUnroll;
-  for (int64_t r0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kAdamsUnroll; r0 < pk; r0 += step) {
-    int64_t j[kAdamsUnroll];
-    float x[kAdamsUnroll], mo[kAdamsUnroll], wo[kAdamsUnroll];
-#pragma unroll
-    for (int u = 0; u < kAdamsUnroll; ++u) {
-      const int64_t r = r0 + u;
-      j[u] = (r < pk) ? (int64_t)idx[r] : c.n;
-      x[u] = (r < pk) ? b[r] : 0.0f;
-    }
-    for (int i = 1; i < K; ++i) {
-#pragma unroll
-      for (int u = 0; u < kAdamsUnroll; ++u) {
-        const int64_t r = r0 + u;
-        if (r < pk) x[u] = x[u] + b[(int64_t)i * pk + r];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kAdamsUnroll; ++u) {
-      if (j[u] < c.n) {
-        mo[u] = m[j[u]];
-        wo[u] = w[j[u]];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kAdamsUnroll; ++u) {
-      if (j[u] >= c.n) continue;  // past the end, or an index from a malformed mask
-      const float xm = x[u] * invK;
-      const float mn = (c.b1 * mo[u]) + (c.c1 * xm);
-      const float vn = (c.b2 * (mo[u] * mo[u])) + (c.c2 * (xm * xm));
-      const float mh = mn * c.ibc1;
-      const float vh = vn * c.ibc2;
-      const float d = sqrtf(vh) + c.eps;
-      const float uu = mh / d;
-      const float wn = wo[u] - (c.lr * (uu + (c.wd * wo[u])));
-      m[j[u]] = mn;
-      v[j[u]] = vn;
-      w[j[u]] = wn;
-    }
-  }
-}
-
 // Dense AdamS on the worker mean (the baseline the SCAPE step is compared
 // with): one streaming pass, x = ((g0 + g1) + ...) * fp32(1/K), AdamS at
 // every element.  4 elements per thread per iteration, non-temporal.
@@ -208,18 +157,6 @@ hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float
     dense_adams_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(grads, g.K, g.n, invK, w, m, v, c);
   else
     dense_adams_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(grads, g.K, g.n, invK, w, m, v, c);
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce_adams(const Geom& g, const float* b, const uint32_t* idx, float* w,
-                               float* m, float* v, float b1, float b2, float c1, float c2,
-                               float ibc1, float ibc2, float eps, float wd, float lr,
-                               hipStream_t s) {
-  const int64_t pk = (int64_t)g.P * g.k;
-  const float invK = (float)(1.0 / (double)g.K);
-  AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
-  reduce_adams_kernel<<<grid_for((pk + kAdamsUnroll - 1) / kAdamsUnroll), kThreads, 0, s>>>(b, g.K, invK, idx,
-                                                                                             pk, w, m, v, c);
   return hipGetLastError();
 }
 

@@ -151,12 +151,8 @@ Ws ws_view(const Geom& g, void* ws) {
 
 // ------------------------------------------------------------- profiling
 
-// AdamS inside the step pass (true) or as its own pass after the selection.
-constexpr bool kFuseAdams = true;
-
-enum Stage { ST_BOOT = 0, ST_PASS, ST_SELECT, ST_REFINE, ST_EMIT, ST_ADAMS, ST_COUNT };
-const char* kStageNames[ST_COUNT] = {"bootstrap_select", "step_pass", "select_pass", "refine", "emit",
-                                     "adams"};
+enum Stage { ST_BOOT = 0, ST_PASS, ST_SELECT, ST_REFINE, ST_EMIT, ST_COUNT };
+const char* kStageNames[ST_COUNT] = {"bootstrap_select", "step_pass", "select_pass", "refine", "emit"};
 
 struct Rec {
   int stage;
@@ -358,7 +354,7 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   a.grads = grads;
   a.e = e;
   a.b = c.w.b;
-  a.mold = kFuseAdams ? c.w.mold : nullptr;  // m is updated before the selection only when fused
+  a.mold = c.w.mold;  // the step pass updates m at M_t before the selection runs
   a.bits = c.cur.bits;
   a.tile_off = c.cur.tile_off;
   a.b1 = b1;
@@ -371,9 +367,9 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   sa.tile_off = c.cur.tile_off;
   sa.b = c.w.b;
   sa.m = m;
-  sa.v = kFuseAdams ? v : nullptr;
-  sa.w = kFuseAdams ? params : nullptr;
-  sa.mold = kFuseAdams ? c.w.mold : nullptr;
+  sa.v = v;
+  sa.w = params;
+  sa.mold = c.w.mold;
   sa.b1 = b1;
   sa.b2 = b2;
   sa.c1 = c1;
@@ -401,20 +397,13 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   return hip_check(launch_zero_u32(c.w.sel.hist, (int64_t)g.P * kBins, stream), "zero");
 }
 
-scape_status step_end(StepCtx& c, float* params, float* m, float* v, scape_betas betas, float lr,
-                      hipStream_t stream) {
+scape_status step_end(StepCtx& c, hipStream_t stream) {
   const Geom& g = c.g;
   scape_status st;
   g_prof.begin(ST_SELECT, stream);
   if ((st = hip_check(launch_level1(g, c.w.sel, kScanCheck, stream), "level 1"))) return st;
   if ((st = run_fallback(g, c.w, kSrcMasked, c.a, c.vec, stream))) return st;
-  if ((st = run_tail(g, c.w, c.nxt, stream, g_prof.on))) return st;
-  if (!kFuseAdams) {
-    g_prof.begin(ST_ADAMS, stream);
-    st = hip_check(launch_reduce_adams(g, c.w.b, c.cur.idx, params, m, v, c.sa.b1, c.sa.b2, c.sa.c1, c.sa.c2,
-                                       c.sa.ibc1, c.sa.ibc2, betas.eps, betas.weight_decay, lr, stream),
-                   "reduce_adams");
-  }
+  st = run_tail(g, c.w, c.nxt, stream, g_prof.on);
   g_prof.end();
   return st;
 }
@@ -456,7 +445,7 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   if (st) return st;
   const bool vec = c.vec && aligned16(params) && aligned16(v);
   if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, stream), "step pass"))) return st;
-  return step_end(c, params, m, v, betas, lr, stream);
+  return step_end(c, stream);
 }
 
 size_t scape_offload_stage_bytes(const scape_dims* dims, int64_t k, int32_t chunk_parts) {
@@ -524,7 +513,7 @@ scape_status scape_step_offload(const scape_dims* dims, float* params, const flo
   // the selection's fallback reads e_host: wait for every copy-out
   for (int b = 0; b < 2 && b < nchunks; ++b)
     if ((st = hip_check(hipStreamWaitEvent(stream, g_oev.out[b], 0), "offload wait"))) return st;
-  return step_end(c, params, m, v, betas, lr, stream);
+  return step_end(c, stream);
 }
 
 scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const float* grads, float* m,

@@ -120,16 +120,12 @@ __device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], 
   }
 }
 
-// Grid of the streaming passes: G blocks per partition.  With
-// kPartitionFastest the partition is blockIdx.x, so the blocks resident at
-// any moment cover every partition; otherwise blockIdx.y, so the dispatcher
-// fills the device partition by partition.
-constexpr bool kPartitionFastest = false;
-
-__device__ __forceinline__ int block_part() { return kPartitionFastest ? blockIdx.x : blockIdx.y; }
-__device__ __forceinline__ int block_in_part() { return kPartitionFastest ? blockIdx.y : blockIdx.x; }
-__device__ __forceinline__ int blocks_per_part() { return kPartitionFastest ? gridDim.y : gridDim.x; }
-inline dim3 stream_grid(int nparts, int G) { return kPartitionFastest ? dim3(nparts, G) : dim3(G, nparts); }
+// Grid of the streaming passes: (G, partitions); the dispatcher fills the
+// device partition by partition, G blocks each.
+__device__ __forceinline__ int block_part() { return blockIdx.y; }
+__device__ __forceinline__ int block_in_part() { return blockIdx.x; }
+__device__ __forceinline__ int blocks_per_part() { return gridDim.x; }
+inline dim3 stream_grid(int nparts, int G) { return dim3(G, nparts); }
 
 struct AdamsC {
   float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, invK;
@@ -152,7 +148,7 @@ constexpr int kChunkGroup = 2;
 // 128, which the chunk group of 2 fits without spilling).
 constexpr int kStepMinWaves = 4;
 
-template <bool STEP, bool ADAMS, bool VEC>
+template <bool STEP, bool VEC>
 __global__ void __launch_bounds__(kThreads, kStepMinWaves)
 compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
@@ -239,7 +235,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 if ((nib[u] >> q) & 1u) {
                   if (r < rend) bi[r] = a[q];
                   ++r;
-                  if (ADAMS) S[u][q] = (i == 0) ? a[q] : S[u][q] + a[q];
+                  if (STEP) S[u][q] = (i == 0) ? a[q] : S[u][q] + a[q];
                 }
             }
           }
@@ -256,7 +252,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
           }
         }
       }
-      if (ADAMS) {
+      if (STEP) {
         // AdamS at the group's masked elements: gather w, then update.
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {
@@ -429,38 +425,26 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
   const dim3 grid = stream_grid(g.P, g.G);
   AdamsC ac{};
   if (vec)
-    compress_kernel<false, false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
-                                                                  nullptr, nullptr, ac, nullptr, nullptr, nullptr,
-                                                                  nullptr, 0, g.n);
+    compress_kernel<false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr,
+                                                           nullptr, ac, nullptr, nullptr, nullptr, nullptr, 0, g.n);
   else
-    compress_kernel<false, false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr,
-                                                                   nullptr, nullptr, nullptr, ac, nullptr, nullptr,
-                                                                   nullptr, nullptr, 0, g.n);
+    compress_kernel<false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
+                                                            nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
+                                                            0, g.n);
   return hipGetLastError();
 }
 
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s) {
   const dim3 grid = stream_grid(a.nparts, g.G);
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
-  if (a.w != nullptr) {  // with AdamS fused
-    if (vec)
-      compress_kernel<true, true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
-                                                                  a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1,
-                                                                  a.hist, a.p0, a.e_stride);
-    else
-      compress_kernel<true, true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
-                                                                   a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1,
-                                                                   a.hist, a.p0, a.e_stride);
-  } else {
-    if (vec)
-      compress_kernel<true, false, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
-                                                                   nullptr, nullptr, nullptr, ac, a.lo, a.cand,
-                                                                   a.cnt1, a.hist, a.p0, a.e_stride);
-    else
-      compress_kernel<true, false, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b,
-                                                                    a.m, nullptr, nullptr, nullptr, ac, a.lo,
-                                                                    a.cand, a.cnt1, a.hist, a.p0, a.e_stride);
-  }
+  if (vec)
+    compress_kernel<true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v, a.w,
+                                                          a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
+                                                          a.e_stride);
+  else
+    compress_kernel<true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
+                                                           a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
+                                                           a.e_stride);
   return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ struct StepArgs {
   const uint64_t* bits;      // M_t
   const uint32_t* tile_off;  // M_t
   float* b;                  // [K][P*k] sparse buffers
-  float *m, *v, *w;           // w == nullptr: no AdamS in this pass
+  float *m, *v, *w;
   float* mold;               // [P*k] pre-update m of the masked elements
   float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr;
   const uint32_t* lo;        // [P] capture bounds
@@ -164,10 +164,6 @@ hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, f
 hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float* m, float* v, float b1,
                               float b2, float c1, float c2, float ibc1, float ibc2, float eps, float wd,
                               float lr, bool vec, hipStream_t s);
-hipError_t launch_reduce_adams(const Geom& g, const float* b, const uint32_t* idx, float* w,
-                               float* m, float* v, float b1, float b2, float c1, float c2,
-                               float ibc1, float ibc2, float eps, float wd, float lr,
-                               hipStream_t s);
 hipError_t launch_union(const Geom& g, uint64_t* acc, const uint64_t* m, uint64_t* out, hipStream_t s);
 hipError_t launch_overlap(const Geom& g, const uint64_t* a, const uint64_t* b, uint64_t* out,
                           hipStream_t s);

@@ -152,7 +152,7 @@ def test_status_strings_and_profile_names():
     assert L.scape_status_string(0) == b"ok"
     assert L.scape_status_string(3) == b"workspace too small"
     names = S.profile_stage_names()
-    assert names == ["bootstrap_select", "step_pass", "select_pass", "refine", "emit", "adams"]
+    assert names == ["bootstrap_select", "step_pass", "select_pass", "refine", "emit"]
     assert L.scape_profile_collect(None, None) == 1
 
 

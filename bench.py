@@ -88,6 +88,27 @@ def cpu_baseline(cfg, seed, workers, log_fn):
                       f"{wall:.1f} s wall (per-process {min(t for _, t in times):.1f}-{max(t for _, t in times):.1f} s)"}
 
 
+def cpu_tiny_single_core(seed, log_fn, steps=3):
+    """The whole tiny workload (n = 2^20, P = 4, K = 2) stepped by the oracle
+    in this one process: median ms per step over steps 1..steps, inputs
+    generated before each timed step."""
+    from oracle import scape_oracle as O
+    from sparse_communication_distributed_amd import workload as W
+    cfg = W.CONFIGS["tiny"]
+    hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    opt = O.OracleOptimizer(W.init_params(cfg, seed), cfg.P, cfg.K, cfg.k, hp)
+    times = []
+    for t in range(1, steps + 1):
+        g = W.grads(cfg, t, seed)
+        t0 = time.perf_counter()
+        opt.step(g)
+        times.append((time.perf_counter() - t0) * 1e3)
+    ms = float(np.median(times))
+    log_fn(f"cpu baseline: tiny workload on one core {ms:.1f} ms/step")
+    return {"workload": "tiny", "n_params": cfg.n, "ms_per_step": ms, "params_per_s": cfg.n / (ms * 1e-3),
+            "cores": 1, "steps": steps}
+
+
 def stream_calibration(torch, dev, log_fn):
     """A plain copy of 1 GiB (read 1 GiB, write 1 GiB), five times: the
     known-size kernel that scales the HBM byte counters, and the streaming
@@ -246,6 +267,7 @@ def main():
     if not args.no_cpu_baseline:
         workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
         cpu = cpu_baseline(cfg, args.seed, workers, log)
+        cpu["tiny_single_core"] = cpu_tiny_single_core(args.seed, log)
     n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -300,15 +322,22 @@ def main():
     S.profile_enable(True)
     overlaps = []
     cnt = torch.zeros(1, dtype=torch.int64, device=dev)
-    for _ in range(args.steps):
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    step_ms = []
+    for i in range(args.steps):
+        step_ev[i].record(stream)
         one_step()
+        step_ev[i + 1].record(stream)
         if args.overlap:  # |M_t ∩ M_{t+1}| / (P k), outside the timed region
             S.mask_overlap(d, k, S.mask_slot(d, k, mask, (t - 1) & 1), S.mask_slot(d, k, mask, t & 1), cnt, stream)
             overlaps.append(cnt.item() / (P * k))
+    torch.cuda.synchronize()
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     stages = S.profile_collect()
     S.profile_enable(False)
     stage_ms = {name: tot / cnt for name, (tot, cnt) in stages.items() if cnt}
     log("stage ms: " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in stage_ms.items()))
+    log("profiled steps ms: " + ", ".join(f"{x:.3f}" for x in step_ms))
 
     # the pages' comparison point: dense AdamS on the worker mean, same
     # tensors, same number of steps (after the SCAPE measurements)
@@ -320,6 +349,19 @@ def main():
     torch.cuda.synchronize()
     dense_ms = ev2.elapsed_time(ev3) / args.steps
     log(f"dense AdamS: {dense_ms:.3f} ms/step")
+
+    # a step-1 call (the bootstrap: statistic pass and fresh select of M_1
+    # before the step pass), timed warm on the same tensors after everything
+    # else, since its state afterwards is no longer used
+    S.profile_enable(True)
+    ev2.record(stream)
+    S.step(d, params, pool[0], m, v, e, mask, k, bt, cfg.lr, 1, ws, stream)
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    boot_ms = ev2.elapsed_time(ev3)
+    boot_stages = {name: tot for name, (tot, c) in S.profile_collect().items() if c}
+    S.profile_enable(False)
+    log(f"bootstrap step (t = 1): {boot_ms:.3f} ms")
 
     b_step = alg_bytes_step(n, P, K, k)
     b_comp = alg_bytes_step_pass(n, P, K, k)
@@ -355,6 +397,8 @@ def main():
         "hbm_frac_alg": gbps / HBM_PEAK_GBPS,
         "bytes_alg_per_step": b_step,
         "stage_ms": stage_ms,
+        "profiled_step_ms": step_ms,
+        "bootstrap_step": {"ms": boot_ms, "stage_ms": boot_stages},
         "roofline": {"bound": "hbm", "kernel": "compress_kernel (step pass)", "achieved": comp_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": comp_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms},
@@ -369,6 +413,8 @@ def main():
         out["stream_calibration"] = calib
     if overlaps:
         out["mask_overlap"] = overlaps
+    if cpu is not None:
+        cpu["gpu_over_cpu"] = out["value"] / cpu["value"]
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 

@@ -95,7 +95,7 @@ __device__ __forceinline__ void load_tile_words(const uint64_t* __restrict__ bit
 // flagged keys are appended to the tile's candidate slot at positions
 // handed out by the LDS counter `tcnt`, and counted in the LDS histogram.
 // Every lane of the wave must call this (ballots and a lane-0 broadcast).
-__device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], int64_t lj,
+__device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], uint32_t lj,
                                          uint32_t idx_mask, uint64_t* __restrict__ slot,
                                          uint32_t* tcnt, uint32_t* sh) {
   uint64_t B[4];
@@ -113,7 +113,7 @@ __device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], 
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (f[q]) {
-      const uint32_t j = (uint32_t)(lj + q);
+      const uint32_t j = lj + q;
       slot[base + pre[q] + mbcnt(B[q])] = ((uint64_t)kk[q] << 32) | (uint64_t)(idx_mask - j);
       atomicAdd(&sh[kk[q] >> kL1Shift], 1u);
     }
@@ -179,62 +179,67 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
     load_tile_words(bits, wbase, g.wpp, t, sw, spre);
     if (threadIdx.x == 0) tcnt = 0;
     __syncthreads();
+    // Addresses are a block-uniform tile base (scalar registers) plus a
+    // 32-bit lane offset: element o of the tile, rank rr of the tile's
+    // first masked element.
+    const int64_t tb = t * kTile;
+    const uint32_t tn = (uint32_t)min<int64_t>(kTile, g.n_p - tb);  // elements in this tile
     const int64_t rbase = (int64_t)p * g.k + tile_off[(int64_t)p * g.tpp + t];
-    const int64_t rend = (int64_t)(p + 1) * g.k;
+    // ranks stay inside partition p's k entries for any mask with k bits per
+    // partition; the bound keeps a malformed mask in bounds
+    const int64_t rlim = (int64_t)(p + 1) * g.k - rbase;
     uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    const float* mt = m + pbase + tb;
 
     for (int cg = 0; cg < 4; cg += kChunkGroup) {
-      uint32_t nib[kChunkGroup];
-      int64_t rank0[kChunkGroup], lj[kChunkGroup];
+      uint32_t nib[kChunkGroup], rr0[kChunkGroup], o[kChunkGroup];
 #pragma unroll
       for (int u = 0; u < kChunkGroup; ++u) {
         const int c = cg + u;
         const int q = c * 16 + (threadIdx.x >> 4);
         const uint64_t word = sw[q];
         nib[u] = (uint32_t)(word >> sh4) & 0xfu;
-        rank0[u] = rbase + spre[q] + (uint32_t)__popcll(word & below);
-        lj[u] = t * kTile + c * 1024 + 4 * threadIdx.x;
+        rr0[u] = spre[q] + (uint32_t)__popcll(word & below);
+        o[u] = c * 1024 + 4 * threadIdx.x;
       }
       float ma[kChunkGroup][4], S[kChunkGroup][4];
       (void)S;
       if (STEP) {
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u)
-          if (lj[u] < g.n_p) load4(m + pbase, lj[u], g.n_p, VEC, ma[u]);
+          if (o[u] < tn) load4(mt, o[u], tn, VEC, ma[u]);
       }
       for (int i = 0; i < g.K; ++i) {
-        const float* gi = grads + (int64_t)i * g.n + pbase;
-        float* ei = e + (int64_t)i * e_stride + ebase;
-        float* bi = b + (int64_t)i * pk;
+        const float* gt = grads + (int64_t)i * g.n + pbase + tb;
+        float* et = e + (int64_t)i * e_stride + ebase + tb;
+        float* bt = b + (int64_t)i * pk + rbase;
         float ga[kChunkGroup][4], ea[kChunkGroup][4];
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {
-          if (lj[u] < g.n_p) {
-            load4(gi, lj[u], g.n_p, VEC, ga[u]);
-            load4(ei, lj[u], g.n_p, VEC, ea[u]);
+          if (o[u] < tn) {
+            load4(gt, o[u], tn, VEC, ga[u]);
+            load4(et, o[u], tn, VEC, ea[u]);
           }
         }
         const bool own = STEP && (i == owner);  // block-uniform
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {
           float a[4];
-          if (lj[u] < g.n_p) {
+          if (o[u] < tn) {
             float eo[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               a[q] = ga[u][q] + ea[u][q];
               eo[q] = ((nib[u] >> q) & 1u) ? 0.0f : a[q];
             }
-            store4(ei, lj[u], g.n_p, VEC, eo);
+            store4(et, o[u], tn, VEC, eo);
             if (nib[u]) {
-              // ranks stay inside partition p's k entries for any mask with
-              // k bits per partition; the bound keeps a malformed mask in bounds
-              int64_t r = rank0[u];
+              uint32_t rr = rr0[u];
 #pragma unroll
               for (int q = 0; q < 4; ++q)
                 if ((nib[u] >> q) & 1u) {
-                  if (r < rend) bi[r] = a[q];
-                  ++r;
+                  if ((int64_t)rr < rlim) bt[rr] = a[q];
+                  ++rr;
                   if (STEP) S[u][q] = (i == 0) ? a[q] : S[u][q] + a[q];
                 }
             }
@@ -244,27 +249,31 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             bool f[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const bool valid = lj[u] + q < g.n_p;
+              const bool valid = o[u] + q < tn;
               kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
               f[q] = valid && kk[q] >= lo;
             }
-            capture4(kk, f, lj[u], g.idx_mask, slot, &tcnt, sh);
+            capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
           }
         }
       }
       if (STEP) {
         // AdamS at the group's masked elements: gather w, then update.
+        float* wt = w + pbase + tb;
+        float* mw = m + pbase + tb;
+        float* vt = v + pbase + tb;
+        float* ot = mold + rbase;
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {
           if (!nib[u]) continue;
           float wo[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (((nib[u] >> q) & 1u) && lj[u] + q < g.n_p) wo[q] = w[pbase + lj[u] + q];
-          int64_t r = rank0[u];
+            if (((nib[u] >> q) & 1u) && o[u] + q < tn) wo[q] = wt[o[u] + q];
+          uint32_t rr = rr0[u];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (!((nib[u] >> q) & 1u) || lj[u] + q >= g.n_p) continue;
+            if (!((nib[u] >> q) & 1u) || o[u] + q >= tn) continue;
             const float x = S[u][q] * ac.invK;
             const float mo = ma[u][q];
             const float mn = (ac.b1 * mo) + (ac.c1 * x);
@@ -274,12 +283,11 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             const float d = sqrtf(vh) + ac.eps;
             const float uu = mh / d;
             const float wn = wo[q] - (ac.lr * (uu + (ac.wd * wo[q])));
-            const int64_t j = pbase + lj[u] + q;
-            m[j] = mn;
-            v[j] = vn;
-            w[j] = wn;
-            if (r < rend) mold[r] = mo;
-            ++r;
+            mw[o[u] + q] = mn;
+            vt[o[u] + q] = vn;
+            wt[o[u] + q] = wn;
+            if ((int64_t)rr < rlim) ot[rr] = mo;
+            ++rr;
           }
         }
       }
@@ -385,7 +393,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
         bool f[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) f[q] = (lj + q < g.n_p) && kk[q] >= lo;
-        capture4(kk, f, lj, g.idx_mask, slot, &tcnt, sh);
+        capture4(kk, f, (uint32_t)lj, g.idx_mask, slot, &tcnt, sh);
       }
     }
     if (PHASE == 1) {

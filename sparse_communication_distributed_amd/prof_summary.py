@@ -5,9 +5,12 @@
         --write <dir>/run_counter_collection.csv --workload llama1.8b --out profiles/step_pass_llama1.8b
 
 writes <out>.md (kernel table and HBM bytes) and <out>_counters.json (the
-step pass's HBM bytes per launch, read by bench.py).  The HBM counters are
-scaled by what they read for the 1 GiB calibration copy that bench.py --calib
-runs (reads 1 GiB, writes 1 GiB).  The JSON records a hash of the step
+step pass's HBM bytes per launch, read by bench.py).  --stats may be given
+several times, one file per process: the first gives the kernel table, and
+every file's step-pass average is listed, since large allocations land
+differently in each process and the step pass's duration follows them.
+The HBM counters are scaled by what they read for the 1 GiB calibration
+copy that bench.py --calib runs (reads 1 GiB, writes 1 GiB).  The JSON records a hash of the step
 pass's sources; bench.py ignores it once the sources change.
 """
 
@@ -42,7 +45,7 @@ def read_counter(path, counter):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--stats", required=True, action="append")
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--workload", required=True)
@@ -52,7 +55,8 @@ def main():
                     help="step-pass launches to drop from the counter average (the first step)")
     a = ap.parse_args()
 
-    rows = list(csv.DictReader(open(a.stats)))
+    runs = [list(csv.DictReader(open(path))) for path in a.stats]
+    rows = runs[0]
     fetch = read_counter(a.fetch, "FETCH_SIZE")
     write = read_counter(a.write, "WRITE_SIZE")
     f_scale = GIB_KIB / (sum(fetch[CALIB_KERNEL]) / len(fetch[CALIB_KERNEL]))
@@ -66,6 +70,15 @@ def main():
     for r in rows:
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
+    step_ms = []
+    for run in runs:
+        for r in run:
+            if r["Name"] == STEP_KERNEL:
+                step_ms.append((float(r["AverageNs"]) / 1e6, float(r["MinNs"]) / 1e6, float(r["MaxNs"]) / 1e6))
+    if len(runs) > 1:
+        lines += ["", f"## {STEP_KERNEL} in each profiled process", "",
+                  "| process | avg ms | min ms | max ms |", "|---|---|---|---|"]
+        lines += [f"| {i + 1} | {av:.3f} | {mn:.3f} | {mx:.3f} |" for i, (av, mn, mx) in enumerate(step_ms)]
     lines += ["", "## HBM bytes (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"Calibration copy of 1 GiB: FETCH_SIZE scale {f_scale:.3f}, WRITE_SIZE scale {w_scale:.3f}.", "",
               "| kernel | launches | read GB / launch (scaled) | write GB / launch (scaled) |", "|---|---|---|---|"]
@@ -86,7 +99,8 @@ def main():
     rd, wr = out[STEP_KERNEL]
     doc = {"workload": a.workload, "kernel": STEP_KERNEL, "source_hash": step_pass_source_hash(),
            "hbm_read_bytes_per_launch": rd * 1e9, "hbm_write_bytes_per_launch": wr * 1e9,
-           "hbm_bytes_per_launch": (rd + wr) * 1e9, "fetch_scale": f_scale, "write_scale": w_scale}
+           "hbm_bytes_per_launch": (rd + wr) * 1e9, "fetch_scale": f_scale, "write_scale": w_scale,
+           "step_pass_avg_ms_per_process": [av for av, _, _ in step_ms]}
     with open(a.out + "_counters.json", "w") as f:
         json.dump(doc, f, indent=1)
     print(json.dumps(doc, indent=1))

@@ -49,8 +49,12 @@ def test_prof_summary_scales_counters_by_the_copy(tmp_path):
     _write_csv(write, hdr, [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576],
                             ["compress_kernel", "WRITE_SIZE", 7], ["compress_kernel", "WRITE_SIZE", 500],
                             ["compress_kernel", "WRITE_SIZE", 500]])
+    stats2 = tmp_path / "stats2.csv"  # a second profiled process, slower placement
+    _write_csv(stats2, ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+               [["compress_kernel", 3, 66e6, 22e6, 90.0, 21e6, 23e6, 1.0]])
     out = tmp_path / "prof"
     r = subprocess.run([sys.executable, "-m", "sparse_communication_distributed_amd.prof_summary", "--stats", str(stats),
+                        "--stats", str(stats2),
                         "--fetch", str(fetch), "--write", str(write), "--workload", "x", "--out", str(out)],
                        cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
@@ -60,4 +64,6 @@ def test_prof_summary_scales_counters_by_the_copy(tmp_path):
     # first launch skipped; KiB -> bytes, scaled
     assert doc["hbm_read_bytes_per_launch"] == pytest.approx(1000 * 1024 * 2.0)
     assert doc["hbm_write_bytes_per_launch"] == pytest.approx(500 * 1024)
-    assert "compress_kernel" in open(str(out) + ".md").read()
+    assert doc["step_pass_avg_ms_per_process"] == pytest.approx([20.0, 22.0])
+    md = open(str(out) + ".md").read()
+    assert "compress_kernel in each profiled process" in md and "| 2 | 22.000 |" in md

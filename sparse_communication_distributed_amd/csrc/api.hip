@@ -114,6 +114,10 @@ scape_status check_betas(const scape_betas& b, float lr) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// whole 64-byte segments of w, m and v per 16 elements
+bool seg_ok(const Geom& g, const void* w, const void* m, const void* v) {
+  return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0;
+}
 
 float bias_reciprocal(float beta, int64_t t) {
   double p = 1.0;
@@ -444,7 +448,8 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
                                workspace_bytes, stream);
   if (st) return st;
   const bool vec = c.vec && aligned16(params) && aligned16(v);
-  if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, stream), "step pass"))) return st;
+  const bool seg = vec && seg_ok(c.g, params, m, v);
+  if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
   return step_end(c, stream);
 }
 
@@ -476,6 +481,7 @@ scape_status scape_step_offload(const scape_dims* dims, float* params, const flo
   const int64_t n_p = g.n_p, chunk = cp * n_p;
   float* sbuf[2] = {static_cast<float*>(stage), static_cast<float*>(stage) + (size_t)g.K * chunk};
   const bool vec = c.vec && aligned16(params) && aligned16(v) && aligned16(stage) && (chunk % 4 == 0);
+  const bool seg = vec && seg_ok(g, params, m, v);
   // the copies of this call follow everything already on the compute stream
   if ((st = hip_check(hipEventRecord(g_oev.start, stream), "offload record"))) return st;
   if ((st = hip_check(hipStreamWaitEvent(copy_in, g_oev.start, 0), "offload wait"))) return st;
@@ -499,7 +505,7 @@ scape_status scape_step_offload(const scape_dims* dims, float* params, const flo
     sa.p0 = (int)p0;
     sa.nparts = (int)np;
     sa.e_stride = chunk;
-    if ((st = hip_check(launch_step_pass(g, sa, vec, stream), "step pass"))) return st;
+    if ((st = hip_check(launch_step_pass(g, sa, vec, seg, stream), "step pass"))) return st;
     if ((st = hip_check(hipEventRecord(g_oev.pass[b], stream), "offload record"))) return st;
     if ((st = hip_check(hipStreamWaitEvent(copy_out, g_oev.pass[b], 0), "offload wait"))) return st;
     for (int i = 0; i < g.K; ++i) {

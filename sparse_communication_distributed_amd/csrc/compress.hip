@@ -62,6 +62,16 @@ __device__ __forceinline__ void store4(float* p, int64_t lj, int64_t n_p, bool v
   }
 }
 
+// Ordinary (cached) 16-byte access to elements o .. o+3 of a 16-byte-aligned row.
+__device__ __forceinline__ void load4t(const float* p, uint32_t o, float out[4]) {
+  const v4f t = *reinterpret_cast<const v4f*>(p + o);
+  out[0] = t.x; out[1] = t.y; out[2] = t.z; out[3] = t.w;
+}
+
+__device__ __forceinline__ void store4t(float* p, uint32_t o, const float v[4]) {
+  *reinterpret_cast<v4f*>(p + o) = v4f{v[0], v[1], v[2], v[3]};
+}
+
 __device__ __forceinline__ void hist_zero(uint32_t* sh) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) sh[i] = 0;
 }
@@ -148,7 +158,7 @@ constexpr int kChunkGroup = 2;
 // 128, which the chunk group of 2 fits without spilling).
 constexpr int kStepMinWaves = 4;
 
-template <bool STEP, bool VEC>
+template <bool STEP, bool VEC, bool SEG>
 __global__ void __launch_bounds__(kThreads, kStepMinWaves)
 compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
@@ -258,18 +268,36 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         }
       }
       if (STEP) {
-        // AdamS at the group's masked elements: gather w, then update.
+        // AdamS at the group's masked elements.
         float* wt = w + pbase + tb;
         float* mw = m + pbase + tb;
         float* vt = v + pbase + tb;
         float* ot = mold + rbase;
+        const uint32_t lane = threadIdx.x & 63u;
+        (void)lane;
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {
-          if (!nib[u]) continue;
-          float wo[4];
+          float wo[4], vo[4], mn4[4], wn4[4];
+          if (SEG) {
+            // w, m and v are written as whole 64-byte segments (4 lanes x 4
+            // elements) wherever a segment holds a masked element, the
+            // unmasked elements with the values just read: a scattered
+            // 4-byte write costs the memory a read-modify-write of its burst.
+            const uint64_t act = __ballot(nib[u] != 0u);
+            if (!((act >> (lane & ~3u)) & 0xfull) || o[u] >= tn) continue;
+            load4t(wt, o[u], wo);
+            load4t(vt, o[u], vo);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (((nib[u] >> q) & 1u) && o[u] + q < tn) wo[q] = wt[o[u] + q];
+            for (int q = 0; q < 4; ++q) {
+              mn4[q] = ma[u][q];
+              wn4[q] = wo[q];
+            }
+          } else {
+            if (!nib[u]) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (((nib[u] >> q) & 1u) && o[u] + q < tn) wo[q] = wt[o[u] + q];
+          }
           uint32_t rr = rr0[u];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -283,11 +311,22 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             const float d = sqrtf(vh) + ac.eps;
             const float uu = mh / d;
             const float wn = wo[q] - (ac.lr * (uu + (ac.wd * wo[q])));
-            mw[o[u] + q] = mn;
-            vt[o[u] + q] = vn;
-            wt[o[u] + q] = wn;
+            if (SEG) {
+              mn4[q] = mn;
+              vo[q] = vn;
+              wn4[q] = wn;
+            } else {
+              mw[o[u] + q] = mn;
+              vt[o[u] + q] = vn;
+              wt[o[u] + q] = wn;
+            }
             if ((int64_t)rr < rlim) ot[rr] = mo;
             ++rr;
+          }
+          if (SEG) {
+            store4t(mw, o[u], mn4);
+            store4t(vt, o[u], vo);
+            store4t(wt, o[u], wn4);
           }
         }
       }
@@ -433,26 +472,30 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
   const dim3 grid = stream_grid(g.P, g.G);
   AdamsC ac{};
   if (vec)
-    compress_kernel<false, true><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr,
+    compress_kernel<false, true, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr,
                                                            nullptr, ac, nullptr, nullptr, nullptr, nullptr, 0, g.n);
   else
-    compress_kernel<false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
+    compress_kernel<false, false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
                                                             nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
                                                             0, g.n);
   return hipGetLastError();
 }
 
-hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s) {
+hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
   const dim3 grid = stream_grid(a.nparts, g.G);
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
-  if (vec)
-    compress_kernel<true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v, a.w,
-                                                          a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-                                                          a.e_stride);
+  if (vec && seg)
+    compress_kernel<true, true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
+                                                                a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
+                                                                a.e_stride);
+  else if (vec)
+    compress_kernel<true, true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
+                                                                 a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
+                                                                 a.e_stride);
   else
-    compress_kernel<true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
-                                                           a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-                                                           a.e_stride);
+    compress_kernel<true, false, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
+                                                                  a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist,
+                                                                  a.p0, a.e_stride);
   return hipGetLastError();
 }
 

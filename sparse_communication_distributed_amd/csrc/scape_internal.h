@@ -144,7 +144,8 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
                            const uint32_t* tile_off, float* b, hipStream_t s, bool vec);
 // The fused step pass: compression, owner statistic with candidate capture,
 // worker-sum reduction and AdamS at M_t.
-hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, hipStream_t s);
+// seg: w, m, v rows 64-byte aligned and n_p % 16 == 0 (whole-segment AdamS writes)
+hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
 
 hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
 hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s);

@@ -234,14 +234,26 @@ def test_mask_overlap(S):
 # --------------------------------------------------------------- full step
 
 
-def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=None, before_step=None):
+def _offset_view(x, offset):
+    """x copied into a fresh buffer at `offset` floats from its start."""
+    buf = torch.zeros(x.numel() + offset, dtype=x.dtype, device=x.device)
+    out = buf[offset:]
+    out.copy_(x)
+    return out
+
+
+def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=None, before_step=None,
+                 offset=0):
     """Runs the fused GPU step and the oracle side by side from the same
-    inputs; compares the next mask and all state after every step."""
+    inputs; compares the next mask and all state after every step.  With
+    `offset`, w, m and v live that many floats into their buffers."""
     n, P, K, k, n_p = cfg.n, cfg.P, cfg.K, cfg.k, cfg.n_p
     w0 = W.init_params(cfg, seed)
     hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
     ora = O.OracleOptimizer(w0, P, K, k, hp)
     opt = S.ScapeOptimizer(dev(w0), P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    if offset:
+        opt.params, opt.m, opt.v = (_offset_view(x, offset) for x in (opt.params, opt.m, opt.v))
     for t in range(1, steps + 1):
         g = W.grads(cfg, t, seed) if grad_fn is None else grad_fn(t)
         print(f"[lockstep] {cfg.name} n={n} P={P} K={K} k={k} step {t}", flush=True)
@@ -279,6 +291,20 @@ def test_step_tiny_20_steps(S):
 def test_step_small_shapes(S, n_p, P, K, sp, law):
     cfg = W.flat_config("small", P * n_p, P, K, sp, steps=4, grad_law=law, weight_decay=0.01)
     run_lockstep(S, cfg, cfg.steps)
+
+
+@pytest.mark.parametrize("n_p,offset", [
+    (4096 + 160, 0),    # n_p % 16 == 0, 64-byte aligned rows: whole-segment w/m/v writes
+    (4096 + 160, 4),    # 16-byte but not 64-byte aligned: per-element writes, vector streams
+    (4096 + 164, 0),    # n_p % 16 == 4: per-element writes, vector streams
+    (4096 + 160, 1),    # 4-byte aligned: scalar path
+])
+def test_step_adams_store_paths(S, n_p, offset):
+    """The step pass writes the AdamS results either as whole 64-byte
+    segments or element by element, chosen by the alignment of w, m, v and
+    n_p; every choice gives the oracle's state bit for bit."""
+    cfg = W.flat_config("align", 3 * n_p, 3, 2, "0.9", steps=3, weight_decay=0.01)
+    run_lockstep(S, cfg, cfg.steps, offset=offset)
 
 
 def test_step_deterministic_and_resumable(S):

@@ -114,9 +114,11 @@ scape_status check_betas(const scape_betas& b, float lr) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-// whole 64-byte segments of w, m and v per 16 elements
+// Whole 64-byte segments of w, m and v per 16 elements: needs aligned
+// segments, and pays only where masked elements are not too rare (at a
+// density of 0.1% the segment reads cost more than the writes save).
 bool seg_ok(const Geom& g, const void* w, const void* m, const void* v) {
-  return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0;
+  return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0 && g.k * 200 >= g.n_p;
 }
 
 float bias_reciprocal(float beta, int64_t t) {

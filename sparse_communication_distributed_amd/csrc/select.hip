@@ -23,6 +23,9 @@ namespace {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
+// Chunks of 64 candidates a wave loads per round when it walks a slot.
+constexpr int kCandChunks = 4;
+
 // Exclusive scan over a block of kThreads (4 waves); `wtot` is LDS [4].
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
@@ -250,50 +253,87 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   for (int i = threadIdx.x; i < kBins; i += kThreads) sh[i] = 0;
   if (threadIdx.x == 0) smin = 0xffffffffu;
   __syncthreads();
+  // The wave takes tiles t0, t0 + nw, ... in batches of up to 64: lane i
+  // loads the capture count of the batch's i-th tile, and the first 64
+  // captures of the next tile are loaded while a tile is processed, so that
+  // a tile costs no dependent global load of its own.
   const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
-  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < g.tpp; t += nw) {
-    wd[lane] = 0ull;
-    wave_lds_sync();
-    uint32_t n1 = cnt1[(int64_t)p * g.tpp + t];
-    if (n1 > (uint32_t)kTile) n1 = (uint32_t)kTile;  // a slot holds at most one tile
-    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-    const uint32_t tile_lo = (uint32_t)(t * kTile);
-    uint32_t n2 = 0;
-    for (uint32_t base = 0; base < n1; base += 64) {
-      const uint32_t i = base + lane;
-      const bool valid = i < n1;
-      const uint64_t c = valid ? slot[i] : 0ull;
-      const uint32_t d1 = (uint32_t)(c >> (32 + kL1Shift)) & (kBins - 1);
-      const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
-      const bool ok = valid && jl < (uint32_t)kTile;  // false only for a corrupted slot
-      const bool sel = ok && (d1 > B1 || (done && d1 == B1));
-      const bool keep = ok && !done && d1 == B1;
-      if (sel) {
-        atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
-        if (d1 == B1) {
-          const uint32_t key = (uint32_t)(c >> 32);
-          kmin = key < kmin ? key : kmin;
+  const int64_t t0 = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  const uint32_t* c1p = cnt1 + (int64_t)p * g.tpp;
+  for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
+    const int64_t tl = tb + (int64_t)lane * nw;
+    uint32_t cv = (tl < g.tpp) ? c1p[tl] : 0u;
+    if (cv > (uint32_t)kTile) cv = (uint32_t)kTile;  // a slot holds at most one tile
+    const int64_t left = (g.tpp - tb + nw - 1) / nw;
+    const int nb = left < 64 ? (int)left : 64;
+    uint64_t cnext = 0ull;
+    {
+      const uint32_t nn = (uint32_t)__shfl((int)cv, 0, 64);
+      const uint64_t* ns = cand + ((int64_t)p * g.tpp + tb) * kTile;
+      if (lane < nn) cnext = ns[lane];
+    }
+    for (int j = 0; j < nb; ++j) {
+      const int64_t t = tb + (int64_t)j * nw;
+      const uint32_t n1 = (uint32_t)__shfl((int)cv, j, 64);
+      const uint64_t c0 = cnext;
+      if (j + 1 < nb) {
+        const uint32_t nn = (uint32_t)__shfl((int)cv, j + 1, 64);
+        const uint64_t* ns = cand + ((int64_t)p * g.tpp + t + nw) * kTile;
+        cnext = (lane < nn) ? ns[lane] : 0ull;
+      }
+      wd[lane] = 0ull;
+      wave_lds_sync();
+      uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+      const uint32_t tile_lo = (uint32_t)(t * kTile);
+      uint32_t n2 = 0;
+      // rounds of kCandChunks chunks of 64, all loaded before any is used
+      for (uint32_t base = 0; base < n1; base += 64 * kCandChunks) {
+        uint64_t cc[kCandChunks];
+#pragma unroll
+        for (int u = 0; u < kCandChunks; ++u) {
+          const uint32_t i = base + 64 * u + lane;
+          cc[u] = (base == 0 && u == 0) ? c0 : ((i < n1) ? slot[i] : 0ull);
+        }
+#pragma unroll
+        for (int u = 0; u < kCandChunks; ++u) {
+          if (base + 64 * u >= n1) break;  // wave-uniform
+          const uint64_t c = cc[u];
+          const bool valid = base + 64 * u + lane < n1;
+          const uint32_t d1 = (uint32_t)(c >> (32 + kL1Shift)) & (kBins - 1);
+          const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
+          const bool ok = valid && jl < (uint32_t)kTile;  // false only for a corrupted slot
+          const bool sel = ok && (d1 > B1 || (done && d1 == B1));
+          const bool keep = ok && !done && d1 == B1;
+          if (sel) {
+            atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+            if (d1 == B1) {
+              const uint32_t key = (uint32_t)(c >> 32);
+              kmin = key < kmin ? key : kmin;
+            }
+          }
+          // in-place compaction: a write lands at a position already read
+          // (n2 never passes the candidates read so far)
+          const uint64_t kb = __ballot(keep);
+          if (keep) {
+            slot[n2 + mbcnt(kb)] = c;
+            atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
+          }
+          n2 += (uint32_t)__popcll(kb);
         }
       }
-      const uint64_t kb = __ballot(keep);
-      if (keep) {
-        slot[n2 + mbcnt(kb)] = c;
-        atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
-      }
-      n2 += (uint32_t)__popcll(kb);
-    }
-    wave_lds_sync();
-    const int64_t w = t * kWordsPerTile + lane;
-    const unsigned long long word = wd[lane];
-    if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = word;
-    uint32_t pc = (uint32_t)__popcll(word);
+      wave_lds_sync();
+      const int64_t w = t * kWordsPerTile + lane;
+      const unsigned long long word = wd[lane];
+      if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = word;
+      uint32_t pc = (uint32_t)__popcll(word);
 #pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
-    if (lane == 0) {
-      cnt2[(int64_t)p * g.tpp + t] = n2;
-      tilecnt[(int64_t)p * g.tpp + t] = pc;
+      for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
+      if (lane == 0) {
+        cnt2[(int64_t)p * g.tpp + t] = n2;
+        tilecnt[(int64_t)p * g.tpp + t] = pc;
+      }
+      wave_lds_sync();
     }
-    wave_lds_sync();
   }
   __syncthreads();
   uint32_t* h = hist + (int64_t)p * kBins;
@@ -307,14 +347,43 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
 // The compacted candidate lists are walked one wave per tile (each wave
 // takes tiles wave_id, wave_id + nwaves, ...), the lanes striding over the
 // tile's candidates.
+// Candidates 0 .. ct-1 of a slot, read by the wave in rounds of
+// kCandChunks chunks of 64 (all loaded before any is used); f(c) runs on
+// the lanes that hold a candidate.
+template <typename F>
+__device__ __forceinline__ void for_each_cand(const uint64_t* __restrict__ slot, uint32_t ct, uint32_t lane,
+                                              F&& f) {
+  for (uint32_t base = 0; base < ct; base += 64 * kCandChunks) {
+    uint64_t cc[kCandChunks];
+#pragma unroll
+    for (int u = 0; u < kCandChunks; ++u) {
+      const uint32_t i = base + 64 * u + lane;
+      cc[u] = (i < ct) ? slot[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kCandChunks; ++u)
+      if (base + 64 * u + lane < ct) f(cc[u]);
+  }
+}
+
+// The counts are loaded 64 tiles at a time (lane i: the batch's i-th tile)
+// and only tiles with candidates are visited, in ascending order.
 template <typename F>
 __device__ __forceinline__ void for_each_tile(const Geom& g, int p, const uint32_t* __restrict__ cnt2,
                                               F&& f) {
   const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
-  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); t < g.tpp; t += nw) {
-    uint32_t ct = cnt2[(int64_t)p * g.tpp + t];
+  const int64_t t0 = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t lane = lane_id();
+  for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
+    const int64_t tl = tb + (int64_t)lane * nw;
+    uint32_t ct = (tl < g.tpp) ? cnt2[(int64_t)p * g.tpp + tl] : 0u;
     if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
-    if (ct) f(t, ct);  // wave-uniform
+    uint64_t nz = __ballot(ct != 0u);
+    while (nz) {  // wave-uniform
+      const int j = __builtin_ctzll(nz);
+      nz &= nz - 1;
+      f(tb + (int64_t)j * nw, (uint32_t)__shfl((int)ct, j, 64));
+    }
   }
 }
 
@@ -332,10 +401,9 @@ cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __re
   const uint32_t lane = lane_id();
   for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
     const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-    for (uint32_t i = lane; i < ct; i += 64) {
-      const uint64_t c = slot[i];
+    for_each_cand(slot, ct, lane, [&](uint64_t c) {
       if ((c & st.mask) == st.prefix) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
+    });
   });
   __syncthreads();
   uint32_t* h = hist + (int64_t)p * kBins;
@@ -364,21 +432,21 @@ mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restric
   for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
     const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
     const uint32_t tile_lo = (uint32_t)(t * kTile);
+    const int64_t w = t * kWordsPerTile + lane;
+    const uint64_t old = (w < g.wpp) ? wb[w] : 0ull;  // in flight while the candidates are read
     wd[lane] = 0ull;
     wave_lds_sync();
-    for (uint32_t i = lane; i < ct; i += 64) {
-      const uint64_t c = slot[i];
+    for_each_cand(slot, ct, lane, [&](uint64_t c) {
       const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
       if (c >= T && jl < (uint32_t)kTile) {
         atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
         const uint32_t key = (uint32_t)(c >> 32);
         kmin = key < kmin ? key : kmin;
       }
-    }
+    });
     wave_lds_sync();
     const unsigned long long word = wd[lane];
-    const int64_t w = t * kWordsPerTile + lane;
-    if (word && w < g.wpp) wb[w] |= word;
+    if (word && w < g.wpp) wb[w] = old | word;
     // these elements were not selected by the candidate select pass, so the
     // tile's count grows by exactly their number
     uint32_t pc = (uint32_t)__popcll(word);

@@ -293,17 +293,19 @@ def test_step_small_shapes(S, n_p, P, K, sp, law):
     run_lockstep(S, cfg, cfg.steps)
 
 
-@pytest.mark.parametrize("n_p,offset", [
-    (4096 + 160, 0),    # n_p % 16 == 0, 64-byte aligned rows: whole-segment w/m/v writes
-    (4096 + 160, 4),    # 16-byte but not 64-byte aligned: per-element writes, vector streams
-    (4096 + 164, 0),    # n_p % 16 == 4: per-element writes, vector streams
-    (4096 + 160, 1),    # 4-byte aligned: scalar path
+@pytest.mark.parametrize("n_p,offset,sp", [
+    (4096 + 160, 0, "0.9"),    # n_p % 16 == 0, 64-byte aligned rows: whole-segment w/m/v writes
+    (4096 + 160, 4, "0.9"),    # 16-byte but not 64-byte aligned: per-element writes, vector streams
+    (4096 + 164, 0, "0.9"),    # n_p % 16 == 4: per-element writes, vector streams
+    (4096 + 160, 1, "0.9"),    # 4-byte aligned: scalar path
+    (4096 + 160, 0, "0.999"),  # aligned, but masked elements too rare: per-element writes
 ])
-def test_step_adams_store_paths(S, n_p, offset):
+def test_step_adams_store_paths(S, n_p, offset, sp):
     """The step pass writes the AdamS results either as whole 64-byte
-    segments or element by element, chosen by the alignment of w, m, v and
-    n_p; every choice gives the oracle's state bit for bit."""
-    cfg = W.flat_config("align", 3 * n_p, 3, 2, "0.9", steps=3, weight_decay=0.01)
+    segments or element by element, chosen by the alignment of w, m, v,
+    n_p and the mask density; every choice gives the oracle's state bit for
+    bit."""
+    cfg = W.flat_config("align", 3 * n_p, 3, 2, sp, steps=3, weight_decay=0.01)
     run_lockstep(S, cfg, cfg.steps, offset=offset)
 
 

@@ -225,13 +225,35 @@ scape_status run_tail(const Geom& g, const Ws& w, scape_mask_view out, hipStream
   return hip_check(e, "select launch");
 }
 
-// Mask from scratch (no capture bound known): every partition takes the
-// exact two-pass route of the fallback.
+// Mask from scratch (no capture bound known).  With enough tiles per
+// partition, a histogram of every kSampleStep-th tile gives each partition
+// the level-1 digit above which about kSampleMargin * k keys lie; one
+// capture pass at that bound follows and is checked as after a step pass,
+// and a partition that captured fewer than k keys takes the exact two-pass
+// route of the fallback (every partition does, without the sample).
 scape_status run_fresh_select(const Geom& g, const Ws& w, int src, const StatArgs& a, bool vec,
                               scape_mask_view out, hipStream_t s) {
   scape_status st;
   if ((st = hip_check(launch_zero_u32(w.sel.hist, (int64_t)g.P * kBins, s), "zero"))) return st;
   if ((st = hip_check(launch_init_state(g, w.sel.state, s), "init"))) return st;
+  if (g.tpp >= 4 * kSampleStep) {
+    StatArgs b = a;
+    b.state = w.sel.state;
+    b.only_fb = 1;
+    b.cand = w.sel.cand;
+    b.cnt1 = w.sel.cnt1;
+    b.hist = w.sel.hist;
+    b.tile_step = kSampleStep;
+    const int64_t sampled = (g.tpp + kSampleStep - 1) / kSampleStep;
+    const double frac = (double)(sampled * kTile) / (double)(g.tpp * kTile);
+    double tgt = std::ceil(kSampleMargin * (double)g.k * frac);
+    if (tgt < 1.0) tgt = 1.0;
+    if ((st = hip_check(launch_stat(g, src, kPhaseHist, b, vec, s), "sample count"))) return st;
+    if ((st = hip_check(launch_level1(g, w.sel, kScanSample, s, (uint32_t)tgt), "sample bound"))) return st;
+    b.tile_step = 1;
+    if ((st = hip_check(launch_stat(g, src, kPhaseCapture, b, vec, s), "first capture"))) return st;
+    if ((st = hip_check(launch_level1(g, w.sel, kScanCheck, s), "level 1"))) return st;
+  }
   if ((st = run_fallback(g, w, src, a, vec, s))) return st;
   return run_tail(g, w, out, s, false);
 }

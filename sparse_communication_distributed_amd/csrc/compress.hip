@@ -354,7 +354,7 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
             const float* __restrict__ m, const float* __restrict__ grads, const float* __restrict__ e,
             const float* __restrict__ b, const float* __restrict__ mold, const uint64_t* __restrict__ bits,
             const uint32_t* __restrict__ tile_off, float b1, float c1, uint64_t* __restrict__ cand,
-            uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist) {
+            uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int tile_step) {
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[kBins];
@@ -375,7 +375,8 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
   const int sh4 = 4 * lane16;
   const uint64_t below = (sh4 == 0) ? 0ull : ((1ull << sh4) - 1ull);
 
-  for (int64_t t = block_in_part(); t < g.tpp; t += blocks_per_part()) {
+  const int64_t tstride = (int64_t)blocks_per_part() * tile_step;
+  for (int64_t t = (int64_t)block_in_part() * tile_step; t < g.tpp; t += tstride) {
     __syncthreads();
     if (SRC == 2) load_tile_words(bits, wbase, g.wpp, t, sw, spre);
     if (threadIdx.x == 0) tcnt = 0;
@@ -449,10 +450,12 @@ void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
   const dim3 grid = stream_grid(g.P, g.Gs);
   if (vec)
     stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
-                                                           a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
+                                                           a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist,
+                                                           a.tile_step < 1 ? 1 : a.tile_step);
   else
     stat_kernel<SRC, PHASE, false><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
-                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist);
+                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist,
+                                                           a.tile_step < 1 ? 1 : a.tile_step);
 }
 
 }  // namespace

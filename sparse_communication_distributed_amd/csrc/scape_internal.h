@@ -39,6 +39,7 @@ constexpr int kScanLevel = 0;  // a later level, on candidates
 constexpr int kScanCheck = 1;  // level 1 on captured keys; flags a fallback if fewer than k
 constexpr int kScanBound = 2;  // fallback: level 1 on all keys -> capture bound
 constexpr int kScanFinal = 3;  // fallback: level 1 on the recaptured keys
+constexpr int kScanSample = 4;  // level 1 on a sample of tiles -> capture bound for a first capture
 
 // Per-partition state of the threshold search.  The search runs on the
 // 64-bit composite  c = (key << 32) | (idx_mask - local_index),  unique per
@@ -65,6 +66,10 @@ struct PartSel {
 // kCaptureMargin * k keys at or above it (first on the level-1 digit, then
 // refined inside the threshold bin on the level-2 digit).
 constexpr double kCaptureMargin = 1.25;
+// A first capture (no previous bound) estimates its bound from every
+// kSampleStep-th tile, aiming at kSampleMargin * k keys above it.
+constexpr int kSampleStep = 16;
+constexpr double kSampleMargin = 1.5;
 
 struct Level {
   int shift;  // bit position of the digit in the composite
@@ -106,6 +111,7 @@ struct StatArgs {
   uint64_t* cand;
   uint32_t* cnt1;
   uint32_t* hist;
+  int tile_step;  // visit tiles 0, tile_step, 2*tile_step, ... (a sample when > 1)
 };
 
 // Buffers of the selection pipeline (workspace views).
@@ -148,7 +154,8 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
 
 hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
-hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s);
+// target 0: the capture target of a step (kCaptureMargin * k)
+hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target = 0);
 // From level-1 digits to the mask: candidate select pass (writes every mask
 // word), the later levels, marking, tile counts, offsets, index list and the
 // slot's threshold record.

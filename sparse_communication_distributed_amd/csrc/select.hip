@@ -100,10 +100,36 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
   bool active;
   if (mode == kScanCheck) active = true;
   else if (mode == kScanLevel) active = !cur.done && !cur.fb;
-  else active = cur.fb != 0;
+  else active = cur.fb != 0;  // kScanBound, kScanFinal, kScanSample
   const bool first = mode != kScanLevel;
   const PartSel st = first ? fresh_sel((uint32_t)g.k) : cur;
-  if (active) {
+  if (active && mode == kScanSample) {
+    // The bound for a first capture: the digit at which the count of the
+    // sampled keys from the top reaches `target` (scaled to the sample), or
+    // 0 (capture every key) if the sample holds fewer.
+    const int per = (nb + kThreads - 1) / kThreads;
+    uint32_t s = 0;
+    for (int q = 0; q < per; ++q) {
+      const int pos = threadIdx.x * per + q;
+      if (pos < nb) s += h[nb - 1 - pos];
+    }
+    uint32_t tot;
+    const uint32_t above = block_excl_scan(s, wtot, &tot);
+    if (threadIdx.x == 0 && tot < target) state[p].lo_fb = 0u;
+    if (tot >= target && above < target && target <= above + s) {
+      uint32_t acc = above;
+      for (int q = 0; q < per; ++q) {
+        const int pos = threadIdx.x * per + q;
+        if (pos >= nb) break;
+        const int d = nb - 1 - pos;
+        acc += h[d];
+        if (acc >= target) {
+          state[p].lo_fb = (uint32_t)d << kL1Shift;
+          break;
+        }
+      }
+    }
+  } else if (active) {
     const int per = (nb + kThreads - 1) / kThreads;
     // thread t owns descending positions [t*per, (t+1)*per): bin = nb-1-pos
     uint32_t s = 0;
@@ -566,9 +592,9 @@ hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s) {
+hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target) {
   level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, 32 + kL1Shift, kDigitBits, mode,
-                                             capture_target(g));
+                                             target ? target : capture_target(g));
   return hipGetLastError();
 }
 

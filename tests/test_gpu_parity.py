@@ -94,6 +94,37 @@ def test_mask_topk(S, kind, P, n_p, k):
     check_mask(bits, idx, toff, oracle_topk_local(stat, P, n_p, k), n_p)
 
 
+def _sampled_tiles_large(P, n_p, seed):
+    """Keys of every 16th tile (4096 elements) of each partition 1e4 times
+    larger than the rest: the sampled bound of a first capture lies far
+    above the k-th key, so every partition needs the exact fallback."""
+    x = _stat_case("normal", P, n_p, seed).reshape(P, n_p)
+    j = np.arange(n_p)
+    x[:, (j // 4096) % 16 == 0] *= F32(1e4)
+    return x.reshape(-1)
+
+
+@pytest.mark.parametrize("kind,P,n_p,k", [
+    ("normal", 2, 80 * 4096 + 123, 3_000),    # bound from a sample of tiles, one capture pass
+    ("ties", 2, 70 * 4096, 50_000),           # 13 distinct keys: the threshold digit is one value
+    ("const", 1, 64 * 4096, 1_000),           # every key in one digit: all captured
+    ("normal", 3, 64 * 4096, 1),
+    ("sampled_large", 2, 80 * 4096, 65_536),  # sample misleads: captured < k, exact fallback
+])
+def test_mask_topk_first_capture(S, kind, P, n_p, k):
+    """Partitions of 64 or more tiles take their first capture bound from a
+    sample of tiles; the mask is exact whether or not that capture holds k
+    keys."""
+    seed = 77 + P + k
+    stat = _sampled_tiles_large(P, n_p, seed) if kind == "sampled_large" else _stat_case(kind, P, n_p, seed)
+    d = S.dims(P * n_p, P, 1)
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    ws = torch.full((S.workspace_bytes(d, k),), 0x3C, dtype=torch.uint8, device=DEV)
+    S.mask_topk(d, k, dev(stat), S.mask_slot(d, k, blob, 0), ws)
+    torch.cuda.synchronize()
+    check_mask(*S.mask_slot_tensors(d, k, blob, 0), oracle_topk_local(stat, P, n_p, k), n_p)
+
+
 def test_mask_topk_repeated_calls_reuse_workspace(S):
     """A second call on a dirty workspace gives the same (correct) mask."""
     P, n_p, k = 4, 70_000, 999

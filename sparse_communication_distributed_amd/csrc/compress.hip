@@ -273,16 +273,16 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         float* mw = m + pbase + tb;
         float* vt = v + pbase + tb;
         float* ot = mold + rbase;
-        const uint32_t lane = threadIdx.x & 63u;
-        (void)lane;
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {
           float wo[4], vo[4], mn4[4], wn4[4];
           if (SEG) {
             // w, m and v are written as whole 64-byte segments (4 lanes x 4
             // elements) wherever a segment holds a masked element, the
-            // unmasked elements with the values just read: a scattered
-            // 4-byte write costs the memory a read-modify-write of its burst.
+            // unmasked elements with the values just read.  A 4-byte write
+            // still occupies a whole memory burst; aligned whole segments
+            // measured faster than scattered element writes.
+            const uint32_t lane = threadIdx.x & 63u;
             const uint64_t act = __ballot(nib[u] != 0u);
             if (!((act >> (lane & ~3u)) & 0xfull) || o[u] >= tn) continue;
             load4t(wt, o[u], wo);

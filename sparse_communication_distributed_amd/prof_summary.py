@@ -19,6 +19,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,11 +28,20 @@ CALIB_KERNEL = "__amd_rocclr_copyBuffer"
 GIB_KIB = float(1 << 20)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed (the files
+    hashed here hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def step_pass_source_hash() -> str:
+    """Hash of the step pass's code (comments and layout ignored)."""
     h = hashlib.sha256()
     for name in ("compress.hip", "scape_internal.h"):
-        with open(os.path.join(PKG, "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(PKG, "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

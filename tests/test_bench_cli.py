@@ -67,3 +67,14 @@ def test_prof_summary_scales_counters_by_the_copy(tmp_path):
     assert doc["step_pass_avg_ms_per_process"] == pytest.approx([20.0, 22.0])
     md = open(str(out) + ".md").read()
     assert "compress_kernel in each profiled process" in md and "| 2 | 22.000 |" in md
+
+
+def test_step_pass_hash_ignores_comments_only():
+    """The counters file stays valid across comment and layout edits of the
+    step pass's sources, and not across code edits."""
+    from sparse_communication_distributed_amd.prof_summary import _code_only
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* no\n overflow */ }\n"
+    b = "int f(int x) {\n    return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }"
+    assert _code_only(a) == _code_only(b)
+    assert _code_only(a) != _code_only(c)

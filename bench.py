@@ -83,6 +83,7 @@ def cpu_baseline(cfg, seed, workers, log_fn):
     n = len(parts) * cfg.n_p
     log_fn(f"cpu baseline: {n} params in {wall:.1f} s wall")
     return {"value": n / wall, "unit": "params/s", "cores": len(parts), "kind": "oracle",
+            "ms_per_step_equiv": cfg.n / (n / wall) * 1e3,
             "sample": f"step 1 of {len(parts)} of the {cfg.P} partitions ({n} params, {cfg.K} workers), "
                       f"one single-threaded numpy process per partition, inputs from the host generator, "
                       f"{wall:.1f} s wall (per-process {min(t for _, t in times):.1f}-{max(t for _, t in times):.1f} s)"}

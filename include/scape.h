@@ -21,7 +21,9 @@
  * Common rules for every call:
  *   - Pointers are DEVICE pointers unless stated; the caller allocates and
  *     owns every buffer, including workspaces and mask blobs.  The library
- *     never allocates or frees device memory and keeps no device state.
+ *     never allocates or frees device memory and keeps no state between
+ *     calls, except the HIP events that scape_step_offload and the stage
+ *     timing create once per process.
  *   - Arguments are validated synchronously before anything is enqueued; a
  *     failed check returns a status and touches no buffer.
  *   - Work is enqueued on `stream` and the call returns without waiting.

@@ -318,9 +318,11 @@ def test_step_tiny_20_steps(S):
     (64, 3, 5, "0.9", "tensor_sigma"),         # K > P: some workers own nothing
     (37, 20_000, 3, "0.9", "tensor_sigma"),    # 20000 ragged one-tile partitions (grid y = 20000)
     (100, 7, 16, "0.95", "tensor_sigma"),      # 16 workers
+    (4, 65535, 2, "0.5", "tensor_sigma"),      # the largest partition count (grid y = 65535)
 ])
 def test_step_small_shapes(S, n_p, P, K, sp, law):
-    cfg = W.flat_config("small", P * n_p, P, K, sp, steps=4, grad_law=law, weight_decay=0.01)
+    steps = 2 if P >= 20_000 else 4  # the host generator draws per partition
+    cfg = W.flat_config("small", P * n_p, P, K, sp, steps=steps, grad_law=law, weight_decay=0.01)
     run_lockstep(S, cfg, cfg.steps)
 
 

@@ -225,6 +225,29 @@ def offload_bench(S, W, cfg, args, log_fn):
             "config": {"workload": cfg.name, "n_params": n, "partitions": P, "workers": K, "k_per_partition": k}}
 
 
+def graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, lr, steps_done, ws, steps, log_fn):
+    """Two consecutive steps recorded once into a HIP graph through
+    scape_step_graph (the step's slot and bias state on the device), then
+    replayed: ms per step over `steps` replays of two steps each."""
+    bias = S.bias_state_tensor(bt, steps_done, params.device)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        for j in range(2):
+            S.step_graph(d, params, pool[j % len(pool)], m, v, e, mask, k, bt, lr, (steps_done + j) & 1, bias, ws)
+    graph.replay()  # warm
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (2 * steps)
+    log_fn(f"graph replay: {ms:.3f} ms/step ({steps} replays of 2 steps)")
+    return {"ms_per_step": ms, "replays": steps, "steps_per_replay": 2}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +263,8 @@ def main():
                     help="report |M_t ∩ M_{t+1}| / (P k) per step (untimed; on by default for the stress workload)")
     ap.add_argument("--offload", type=int, default=0, metavar="CHUNK_PARTS",
                     help="keep e in pinned host memory, staged in chunks of this many partitions")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time two steps captured in a HIP graph (scape_step_graph) and replayed")
     ap.add_argument("--study", choices=["fillin"], default=None,
                     help="run a study instead of the step benchmark")
     ap.add_argument("--calib", action="store_true",
@@ -351,6 +376,10 @@ def main():
     dense_ms = ev2.elapsed_time(ev3) / args.steps
     log(f"dense AdamS: {dense_ms:.3f} ms/step")
 
+    graph_rec = None
+    if args.graph:  # continues the SCAPE steps: t steps done, M_{t+1} in slot t & 1
+        graph_rec = graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, cfg.lr, t, ws, args.steps, log)
+
     # a step-1 call (the bootstrap: statistic pass and fresh select of M_1
     # before the step pass), timed warm on the same tensors after everything
     # else, since its state afterwards is no longer used
@@ -414,6 +443,8 @@ def main():
         out["stream_calibration"] = calib
     if overlaps:
         out["mask_overlap"] = overlaps
+    if graph_rec is not None:
+        out["graph"] = graph_rec
     if cpu is not None:
         cpu["gpu_over_cpu"] = out["value"] / cpu["value"]
     out["cpu_baseline"] = cpu

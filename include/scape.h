@@ -190,6 +190,43 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
                         int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Bias-correction state of the graph-capturable step, in DEVICE memory
+ * (8-byte aligned): beta1_pow = beta1^t and beta2_pow = beta2^t after t
+ * steps, as binary64 products of binary64(beta) taken one step at a time
+ * (the same roundings as scape_step's host computation), and the fp32
+ * reciprocals ibc1 = 1/(1 - beta1^t), ibc2 = 1/(1 - beta2^t) that step t
+ * uses ([P] §II-C, the bias-correction remark).
+ */
+typedef struct {
+  double beta1_pow;
+  double beta2_pow;
+  float ibc1;
+  float ibc2;
+} scape_bias_state;
+
+/* The state after `steps_done` (>= 0) steps, computed on the host into *out
+ * (host memory); copy it to the device before the first scape_step_graph.
+ * For steps_done == 0 the reciprocals are 0 (unused). */
+scape_status scape_bias_state_at(scape_betas betas, int64_t steps_done, scape_bias_state* out);
+
+/*
+ * One step t >= 2 of scape_step in a form a HIP graph can capture and
+ * replay: nothing of it depends on host-side values that change from step
+ * to step.  The mask of this step, M_t, is read from slot `cur_slot` (0 or
+ * 1; scape_step's slot (t-1)&1) and M_{t+1} is written to slot 1-cur_slot.
+ * `bias` (device) holds the state after t-1 steps on entry; the call's
+ * first kernel advances it to step t, and the step uses its reciprocals.
+ * There is no step-1 bootstrap: run step 1 with scape_step, then copy
+ * scape_bias_state_at(betas, 1) to `bias`.  Stage timing records nothing
+ * for these calls.  A graph of two calls (cur_slot 1, then 0) replays
+ * steps t, t+1 for even t; the caller refills `grads` between replays.
+ * Results equal scape_step's bit for bit.
+ */
+scape_status scape_step_graph(const scape_dims* dims, float* params, const float* grads, float* m, float* v,
+                              float* e, void* mask_blob, int64_t k, scape_betas betas, float lr, int32_t cur_slot,
+                              scape_bias_state* bias, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Dense AdamS on the worker mean: the baseline the pages compare SCAPE's
  * per-step time with ([P] abstract; [S] §4).  For every element j:
  *   x = (((grads[0][j] + grads[1][j]) + ...) + grads[K-1][j]) * fp32(1/K)

@@ -127,6 +127,20 @@ unsigned grid_for(int64_t count) {
   return (unsigned)blocks;
 }
 
+// One step of the bias-correction state ([P] §II-C, the remark after
+// eq. (2)): beta^t as binary64 products, each step one more multiplication
+// by binary64(beta) in the order the host takes them, then the fp32
+// reciprocals of 1 - beta^t.  One thread.
+__global__ void bias_step_kernel(scape_bias_state* __restrict__ st, float b1, float b2) {
+  if (threadIdx.x != 0) return;
+  const double p1 = st->beta1_pow * (double)b1;
+  const double p2 = st->beta2_pow * (double)b2;
+  st->beta1_pow = p1;
+  st->beta2_pow = p2;
+  st->ibc1 = (float)(1.0 / (1.0 - p1));
+  st->ibc2 = (float)(1.0 / (1.0 - p2));
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const Geom& g, const float* b, float* bbar, hipStream_t s) {
@@ -142,6 +156,11 @@ hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, f
   const int64_t pk = (int64_t)g.P * g.k;
   AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
   adams_kernel<<<grid_for(pk), kThreads, 0, s>>>(bbar, idx, pk, w, m, v, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_step(scape_bias_state* st, float b1, float b2, hipStream_t s) {
+  bias_step_kernel<<<1, 64, 0, s>>>(st, b1, b2);
   return hipGetLastError();
 }
 

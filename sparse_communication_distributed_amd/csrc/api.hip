@@ -355,24 +355,34 @@ struct StepCtx {
   StatArgs a;
   StepArgs sa;
   bool vec;
+  bool prof;  // stage timing records this call
 };
 
+// `bias` null: step t = `step` from the host (slots (t-1)&1 -> t&1, host
+// bias reciprocals, bootstrap at t = 1).  `bias` set: the graph-capturable
+// form, M_t in slot cur_slot, the bias state advanced on the device, no
+// bootstrap and no stage timing.
 scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const float* grads, float* m,
                         float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
-                        int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        scape_bias_state* bias = nullptr, int cur_slot = 0) {
   scape_status st = check_dims(dims, k, &c.g);
   if (st) return st;
   const Geom& g = c.g;
   if (!params || !grads || !m || !v || !e || !mask_blob || !workspace)
     return fail(SCAPE_EINVAL, "null pointer argument");
   if ((st = check_betas(betas, lr))) return st;
-  if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  if (!bias && step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  if (bias && cur_slot != 0 && cur_slot != 1) return fail(SCAPE_EINVAL, "cur_slot must be 0 or 1");
+  if (bias && ((uintptr_t)bias & 7u)) return fail(SCAPE_EINVAL, "bias state must be 8-byte aligned");
   if (workspace_bytes < g.ws_total)
     return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
 
+  c.prof = g_prof.on && !bias;
   c.w = ws_view(g, workspace);
-  c.cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
-  c.nxt = slot_view(g, mask_blob, (int)(step & 1));
+  const int cs = bias ? cur_slot : (int)((step - 1) & 1);
+  c.cur = slot_view(g, mask_blob, cs);
+  c.nxt = slot_view(g, mask_blob, 1 - cs);
   c.vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m);
   const float b1 = betas.beta1, b2 = betas.beta2;
   const float c1 = 1.0f - b1, c2 = 1.0f - b2;
@@ -402,8 +412,9 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   sa.b2 = b2;
   sa.c1 = c1;
   sa.c2 = c2;
-  sa.ibc1 = bias_reciprocal(b1, step);
-  sa.ibc2 = bias_reciprocal(b2, step);
+  sa.ibc1 = bias ? 0.0f : bias_reciprocal(b1, step);
+  sa.ibc2 = bias ? 0.0f : bias_reciprocal(b2, step);
+  sa.ibc_dev = bias ? &bias->ibc1 : nullptr;  // ibc2 follows ibc1
   sa.eps = betas.eps;
   sa.wd = betas.weight_decay;
   sa.lr = lr;
@@ -415,24 +426,25 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   sa.nparts = g.P;
   sa.e_stride = g.n;
 
-  if (step == 1) {  // bootstrap: M_1 = top-k of the step-1 statistic
-    g_prof.begin(ST_BOOT, stream);
+  if (bias && (st = hip_check(launch_bias_step(bias, b1, b2, stream), "bias step"))) return st;
+  if (!bias && step == 1) {  // bootstrap: M_1 = top-k of the step-1 statistic
+    if (c.prof) g_prof.begin(ST_BOOT, stream);
     StatArgs boot = a;
     boot.mold = nullptr;
     if ((st = run_fresh_select(g, c.w, kSrcState, boot, c.vec, c.cur, stream))) return st;
   }
-  g_prof.begin(ST_PASS, stream);
+  if (c.prof) g_prof.begin(ST_PASS, stream);
   return hip_check(launch_zero_u32(c.w.sel.hist, (int64_t)g.P * kBins, stream), "zero");
 }
 
 scape_status step_end(StepCtx& c, hipStream_t stream) {
   const Geom& g = c.g;
   scape_status st;
-  g_prof.begin(ST_SELECT, stream);
+  if (c.prof) g_prof.begin(ST_SELECT, stream);
   if ((st = hip_check(launch_level1(g, c.w.sel, kScanCheck, stream), "level 1"))) return st;
   if ((st = run_fallback(g, c.w, kSrcMasked, c.a, c.vec, stream))) return st;
-  st = run_tail(g, c.w, c.nxt, stream, g_prof.on);
-  g_prof.end();
+  st = run_tail(g, c.w, c.nxt, stream, c.prof);
+  if (c.prof) g_prof.end();
   return st;
 }
 
@@ -470,6 +482,37 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   StepCtx c;
   scape_status st = step_begin(c, dims, params, grads, m, v, e, mask_blob, k, betas, lr, step, workspace,
                                workspace_bytes, stream);
+  if (st) return st;
+  const bool vec = c.vec && aligned16(params) && aligned16(v);
+  const bool seg = vec && seg_ok(c.g, params, m, v);
+  if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
+  return step_end(c, stream);
+}
+
+scape_status scape_bias_state_at(scape_betas betas, int64_t steps_done, scape_bias_state* out) {
+  scape_status st = check_betas(betas, 1.0f);
+  if (st) return st;
+  if (!out) return fail(SCAPE_EINVAL, "out is null");
+  if (steps_done < 0) return fail(SCAPE_EINVAL, "steps_done must be >= 0");
+  double p1 = 1.0, p2 = 1.0;
+  for (int64_t i = 0; i < steps_done; ++i) {
+    p1 = p1 * (double)betas.beta1;
+    p2 = p2 * (double)betas.beta2;
+  }
+  out->beta1_pow = p1;
+  out->beta2_pow = p2;
+  out->ibc1 = steps_done ? bias_reciprocal(betas.beta1, steps_done) : 0.0f;
+  out->ibc2 = steps_done ? bias_reciprocal(betas.beta2, steps_done) : 0.0f;
+  return SCAPE_OK;
+}
+
+scape_status scape_step_graph(const scape_dims* dims, float* params, const float* grads, float* m, float* v,
+                              float* e, void* mask_blob, int64_t k, scape_betas betas, float lr, int32_t cur_slot,
+                              scape_bias_state* bias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!bias) return fail(SCAPE_EINVAL, "null pointer argument");
+  StepCtx c;
+  scape_status st = step_begin(c, dims, params, grads, m, v, e, mask_blob, k, betas, lr, 2, workspace,
+                               workspace_bytes, stream, bias, cur_slot);
   if (st) return st;
   const bool vec = c.vec && aligned16(params) && aligned16(v);
   const bool seg = vec && seg_ok(c.g, params, m, v);

@@ -165,10 +165,15 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 float* __restrict__ b, float* __restrict__ m, float* __restrict__ v,
                 float* __restrict__ w, float* __restrict__ mold, AdamsC ac,
                 const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
-                uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int p0, int64_t e_stride) {
+                uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int p0, int64_t e_stride,
+                const float* __restrict__ ibc_dev) {
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[STEP ? kBins : 1];
+  // bias-correction reciprocals: kernel arguments, or the device-resident
+  // state of a graph-capturable step
+  const float ibc1 = (STEP && ibc_dev) ? ibc_dev[0] : ac.ibc1;
+  const float ibc2 = (STEP && ibc_dev) ? ibc_dev[1] : ac.ibc2;
   __shared__ uint32_t tcnt;
   if (STEP) hist_zero(sh);
   // partitions p0 .. p0 + nparts - 1; e holds their rows [K][nparts * n_p]
@@ -306,8 +311,8 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             const float mo = ma[u][q];
             const float mn = (ac.b1 * mo) + (ac.c1 * x);
             const float vn = (ac.b2 * (mo * mo)) + (ac.c2 * (x * x));
-            const float mh = mn * ac.ibc1;
-            const float vh = vn * ac.ibc2;
+            const float mh = mn * ibc1;
+            const float vh = vn * ibc2;
             const float d = sqrtf(vh) + ac.eps;
             const float uu = mh / d;
             const float wn = wo[q] - (ac.lr * (uu + (ac.wd * wo[q])));
@@ -475,12 +480,13 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
   const dim3 grid = stream_grid(g.P, g.G);
   AdamsC ac{};
   if (vec)
-    compress_kernel<false, true, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr,
-                                                           nullptr, ac, nullptr, nullptr, nullptr, nullptr, 0, g.n);
+    compress_kernel<false, true, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
+                                                                  nullptr, nullptr, ac, nullptr, nullptr, nullptr,
+                                                                  nullptr, 0, g.n, nullptr);
   else
     compress_kernel<false, false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
-                                                            nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
-                                                            0, g.n);
+                                                                   nullptr, nullptr, ac, nullptr, nullptr, nullptr,
+                                                                   nullptr, 0, g.n, nullptr);
   return hipGetLastError();
 }
 
@@ -490,15 +496,15 @@ hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg
   if (vec && seg)
     compress_kernel<true, true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
                                                                 a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-                                                                a.e_stride);
+                                                                a.e_stride, a.ibc_dev);
   else if (vec)
     compress_kernel<true, true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
                                                                  a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-                                                                 a.e_stride);
+                                                                 a.e_stride, a.ibc_dev);
   else
     compress_kernel<true, false, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
                                                                   a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist,
-                                                                  a.p0, a.e_stride);
+                                                                  a.p0, a.e_stride, a.ibc_dev);
   return hipGetLastError();
 }
 

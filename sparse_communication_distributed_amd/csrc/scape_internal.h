@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include "scape.h"
+
 namespace scape {
 
 // Compaction / work tile: 4096 elements = 64 mask words.
@@ -142,6 +144,7 @@ struct StepArgs {
   uint32_t* hist;
   int p0, nparts;            // partitions of this launch
   int64_t e_stride;          // elements between the worker rows of e
+  const float* ibc_dev;      // if set: ibc1, ibc2 read from device memory here
 };
 
 hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, bool vec, hipStream_t s);
@@ -169,6 +172,8 @@ hipError_t launch_reduce(const Geom& g, const float* b, float* bbar, hipStream_t
 hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, float* w, float* m,
                         float* v, float b1, float b2, float c1, float c2, float ibc1, float ibc2,
                         float eps, float wd, float lr, hipStream_t s);
+// Advances the device-resident bias-correction state by one step.
+hipError_t launch_bias_step(scape_bias_state* st, float b1, float b2, hipStream_t s);
 hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float* m, float* v, float b1,
                               float b2, float c1, float c2, float ibc1, float ibc2, float eps, float wd,
                               float lr, bool vec, hipStream_t s);

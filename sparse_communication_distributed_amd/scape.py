@@ -34,6 +34,11 @@ class MaskView(ctypes.Structure):
     _fields_ = [("bits", c_void_p), ("idx", c_void_p), ("tile_off", c_void_p), ("meta", c_void_p)]
 
 
+class BiasState(ctypes.Structure):
+    """scape_bias_state: beta^t products (binary64) and the fp32 reciprocals."""
+    _fields_ = [("beta1_pow", ctypes.c_double), ("beta2_pow", ctypes.c_double), ("ibc1", c_float), ("ibc2", c_float)]
+
+
 class ScapeError(RuntimeError):
     def __init__(self, status: int, detail: str):
         self.status = status
@@ -53,6 +58,9 @@ _SIGS = {
                                    MaskView, Betas, c_float, c_int64, c_void_p]),
     "scape_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p]),
+    "scape_bias_state_at": (c_int, [Betas, c_int64, ctypes.POINTER(BiasState)]),
+    "scape_step_graph": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int64, Betas, c_float, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "scape_mask_overlap": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, MaskView, c_void_p, c_void_p]),
     "scape_offload_stage_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64, c_int32]),
     "scape_step_offload": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -193,6 +201,30 @@ def step(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: floa
     _check(lib().scape_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
                             _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def bias_state_at(bt: Betas, steps_done: int) -> BiasState:
+    out = BiasState()
+    _check(lib().scape_bias_state_at(bt, steps_done, ctypes.byref(out)))
+    return out
+
+
+def bias_state_tensor(bt: Betas, steps_done: int, device):
+    """scape_bias_state after `steps_done` steps, as a 24-byte device tensor."""
+    import torch
+    st = bias_state_at(bt, steps_done)
+    host = torch.frombuffer(bytearray(bytes(st)), dtype=torch.uint8)
+    return host.to(device)
+
+
+def step_graph(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: float, cur_slot: int,
+               bias_state, workspace, stream=None) -> None:
+    """scape_step_graph: one step t >= 2 with M_t in slot cur_slot and the
+    bias state (device tensor of bias_state_tensor) advanced on the device;
+    safe to record into a graph."""
+    _check(lib().scape_step_graph(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
+                                  _ptr(mask_blob), k, bt, lr, cur_slot, _ptr(bias_state), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def offload_stage_bytes(d: Dims, k: int, chunk_parts: int) -> int:

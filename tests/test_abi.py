@@ -104,6 +104,54 @@ def test_step_rejects_step_zero_and_small_workspace():
     assert b"workspace" in S.lib().scape_last_error()
 
 
+def _step_graph(d, k, cur_slot=1, bias=FAKE, ptrs=None, bt=None, wsb=None):
+    L = S.lib()
+    p = dict(params=FAKE, grads=FAKE, m=FAKE, v=FAKE, e=FAKE, mask=FAKE, ws=FAKE)
+    p.update(ptrs or {})
+    return L.scape_step_graph(ctypes.byref(d), p["params"], p["grads"], p["m"], p["v"], p["e"], p["mask"], k,
+                              bt or S.betas(), 1e-3, cur_slot, bias, p["ws"],
+                              S.workspace_bytes(d, k) if wsb is None else wsb, None)
+
+
+def test_step_graph_validation():
+    """Rejected before anything is enqueued (no device needed)."""
+    d = S.dims(4096, 2, 2)
+    assert _step_graph(d, 10, cur_slot=2) == 1
+    assert b"cur_slot" in S.lib().scape_last_error()
+    assert _step_graph(d, 10, cur_slot=-1) == 1
+    assert _step_graph(d, 10, bias=None) == 1
+    assert _step_graph(d, 10, bias=FAKE + 4) == 1
+    assert b"aligned" in S.lib().scape_last_error()
+    assert _step_graph(d, 10, ptrs={"e": None}) == 1
+    assert _step_graph(d, 10, bt=S.betas(beta2=1.0)) == 1
+    assert _step_graph(d, 10, wsb=S.workspace_bytes(d, 10) - 1) == 3
+    assert _step_graph(S.dims(4096, 3, 2), 10) == 2
+
+
+def test_bias_state_matches_stepwise_binary64_products():
+    """beta^t is formed one multiplication per step in binary64 from the
+    fp32 beta, and the reciprocal 1/(1 - beta^t) is rounded once to fp32:
+    the values the host-side step uses ([P] §II-C, bias correction)."""
+    import numpy as np
+    bt = S.betas(0.9, 0.95, 1e-8, 0.0)
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.95))
+    for t in (0, 1, 2, 7, 1000):
+        st = S.bias_state_at(bt, t)
+        p1 = p2 = 1.0
+        for _ in range(t):
+            p1, p2 = p1 * b1, p2 * b2
+        assert st.beta1_pow == p1 and st.beta2_pow == p2
+        if t:
+            assert st.ibc1 == np.float32(1.0 / (1.0 - p1)) and st.ibc2 == np.float32(1.0 / (1.0 - p2))
+        else:
+            assert st.ibc1 == 0.0 and st.ibc2 == 0.0
+    assert S.bias_state_at(bt, 1).ibc1 == np.float32(9.999998)
+    with pytest.raises(S.ScapeError):
+        S.bias_state_at(bt, -1)
+    with pytest.raises(S.ScapeError):
+        S.bias_state_at(S.betas(beta1=1.0), 3)
+
+
 def test_component_validation():
     L = S.lib()
     d = S.dims(4096, 2, 2)

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <vector>
 
 namespace scape {
@@ -121,9 +122,37 @@ bool seg_ok(const Geom& g, const void* w, const void* m, const void* v) {
   return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0 && g.k * 200 >= g.n_p;
 }
 
+// fp32(1 / (1 - beta^t)), beta^t formed by t binary64 multiplications by
+// binary64(beta) starting from 1.  A product of a previous call with the same
+// beta and at most t steps is resumed (the same multiplications in the same
+// order), so consecutive steps cost one multiplication each.
 float bias_reciprocal(float beta, int64_t t) {
+  struct Entry {
+    uint32_t bits;
+    int64_t t;  // 0: empty
+    double p;
+  };
+  thread_local Entry cache[4] = {};
+  thread_local int next = 0;
+  uint32_t bits;
+  std::memcpy(&bits, &beta, sizeof bits);
   double p = 1.0;
-  for (int64_t i = 0; i < t; ++i) p = p * (double)beta;
+  int64_t from = 0;
+  Entry* mine = nullptr;
+  for (Entry& c : cache) {
+    if (c.t == 0 || c.bits != bits) continue;
+    mine = &c;
+    if (c.t <= t) {
+      from = c.t;
+      p = c.p;
+    }
+  }
+  for (int64_t i = from; i < t; ++i) p = p * (double)beta;
+  if (!mine) {
+    mine = &cache[next];
+    next = (next + 1) % 4;
+  }
+  *mine = Entry{bits, t, p};
   return (float)(1.0 / (1.0 - p));
 }
 
@@ -540,6 +569,8 @@ scape_status scape_step_offload(const scape_dims* dims, float* params, const flo
   if (!stage) return fail(SCAPE_EINVAL, "null pointer argument");
   const size_t need = scape_offload_stage_bytes(dims, k, chunk_parts);
   if (stage_bytes < need) return fail(SCAPE_EWORKSPACE, "stage has %zu bytes, needs %zu", stage_bytes, need);
+  if (copy_in == copy_out || copy_in == stream || copy_out == stream)
+    return fail(SCAPE_EINVAL, "stream, copy_in and copy_out must be three distinct streams");
   StepCtx c;
   if ((st = step_begin(c, dims, params, grads, m, v, e_host, mask_blob, k, betas, lr, step, workspace,
                        workspace_bytes, stream)))

@@ -135,7 +135,7 @@ def test_bias_state_matches_stepwise_binary64_products():
     import numpy as np
     bt = S.betas(0.9, 0.95, 1e-8, 0.0)
     b1, b2 = float(np.float32(0.9)), float(np.float32(0.95))
-    for t in (0, 1, 2, 7, 1000):
+    for t in (0, 1, 2, 7, 1000, 7, 1001, 2, 1):  # forward, back, forward: products are resumed only from below
         st = S.bias_state_at(bt, t)
         p1 = p2 = 1.0
         for _ in range(t):
@@ -186,13 +186,16 @@ def test_offload_validation():
     assert S.offload_stage_bytes(d, 10, 9) == 2 * 2 * 4 * 1024 * 4   # at most P partitions per chunk
     wsb = S.workspace_bytes(d, 10)
     sb = S.offload_stage_bytes(d, 10, 2)
-    def call(chunk=2, stage=FAKE, stage_bytes=sb, e=FAKE):
+    def call(chunk=2, stage=FAKE, stage_bytes=sb, e=FAKE, streams=(0x100, 0x200, 0x300)):
         return L.scape_step_offload(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, e, FAKE, 10, S.betas(), 1e-3, 1, FAKE,
-                                    wsb, stage, stage_bytes, chunk, None, None, None)
+                                    wsb, stage, stage_bytes, chunk, *streams)
     assert call(chunk=0) == 1
     assert call(stage=None) == 1
     assert call(stage_bytes=sb - 1) == 3
     assert call(e=None) == 1
+    for streams in ((None, None, None), (0x100, 0x100, 0x300), (0x100, 0x200, 0x100), (0x100, 0x300, 0x300)):
+        assert call(streams=streams) == 1
+        assert b"distinct" in L.scape_last_error()
 
 
 def test_status_strings_and_profile_names():

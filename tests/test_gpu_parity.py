@@ -309,6 +309,16 @@ def test_step_tiny_20_steps(S):
     run_lockstep(S, cfg, cfg.steps)
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_step_tiny_200_steps(S):
+    """Ten times the workload's horizon: the residuals keep accumulating, the
+    masks drift and the capture bound follows them; masks and state stay
+    bitwise equal to the oracle's at every step."""
+    cfg = W.CONFIGS["tiny"]
+    run_lockstep(S, cfg, 200, rtol_end=1e-6)
+
+
 @pytest.mark.parametrize("n_p,P,K,sp,law", [
     (10_007, 3, 2, "0.9", "tensor_sigma"),     # ragged, scalar path, P % K != 0
     (3 * 4096 + 100, 4, 4, "0.99", "tensor_sigma"),

@@ -35,10 +35,7 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   r.K = K;
   r.wpp = (n_p + 63) / 64;
   r.tpp = (n_p + kTile - 1) / kTile;
-  int64_t G = (kTargetBlocks + P - 1) / P;
-  if (G > r.tpp) G = r.tpp;
-  if (G < 1) G = 1;
-  r.G = (int)G;
+  r.G = (int)r.tpp;  // one block per tile (tpp < 2^21: n < 2^32)
   int64_t Gs = (kStatBlocks + P - 1) / P;
   if (Gs > r.tpp) Gs = r.tpp;
   r.Gs = (int)(Gs < 1 ? 1 : Gs);

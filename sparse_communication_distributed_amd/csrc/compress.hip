@@ -15,7 +15,8 @@
 //    key; phase CAPTURE captures keys at or above the partition's bound.
 //
 // Work decomposition: grid (G, P).  Block (b, p) walks tiles b, b+G, ... of
-// partition p; a tile is 4096 elements = 64 mask words; thread `tid` owns
+// partition p (the step pass has G = tiles per partition, one tile per
+// block); a tile is 4096 elements = 64 mask words; thread `tid` owns
 // elements 4*tid .. 4*tid+3 of each 1024-element chunk, so every global
 // access is a 16-byte-per-lane coalesced load or store when vector access
 // is possible (n_p % 4 == 0 and 16-byte aligned bases).

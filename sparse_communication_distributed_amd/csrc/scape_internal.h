@@ -18,13 +18,13 @@ constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
 // Level-1 digit: key bits [30:19] (bit 31 of a key is always zero).
 constexpr int kL1Shift = 19;
-// Target number of blocks for the streaming passes: short blocks (about a
-// dozen tiles each) let the dispatcher balance tiles of uneven cost (dense
-// mask or capture regions) across the 256 CUs.
-constexpr int kTargetBlocks = 32768;
-// Target number of blocks of the statistic passes (the bootstrap and the
+// The step pass and the compression run one block per tile (grid: tiles x
+// partitions): the hardware dispatcher then balances tiles of uneven cost
+// (dense mask or capture regions) across the 256 CUs, and no block holds
+// the end of the pass back by more than one tile.
+// Target number of blocks of the statistic passes (the bootstrap, and the
 // fallback, which usually has nothing to do and should cost little).
-constexpr int kStatBlocks = 2048;
+constexpr int kStatBlocks = 8192;
 // Tiles each wave of the passes over candidate slots walks.
 constexpr int kSelectTilesPerWave = 8;
 constexpr int kThreads = 256;

@@ -38,11 +38,13 @@ def alg_bytes_step(n, P, K, k):
 
 def alg_bytes_step_pass(n, P, K, k):
     """The fused step pass: K workers read g and e and write e, the owner
-    statistic reads m, the mask words are read once, the K sparse buffers
-    are written, and AdamS reads w and writes w, m, v at the P*k masked
-    elements (its m read is the statistic's).  Candidate captures and the
-    saved pre-update m are implementation traffic, not counted."""
-    return (12 * K + 4) * n + n / 8 + 4 * K * P * k + 16 * P * k
+    statistic reads m, the mask words are read once, the owner's sparse
+    buffer is written (the workers' values are summed in registers, so the
+    other K-1 buffers are not needed on one device), and AdamS reads w and
+    writes w, m, v at the P*k masked elements (its m read is the
+    statistic's).  Candidate captures and the saved pre-update m are
+    implementation traffic, not counted."""
+    return (12 * K + 4) * n + n / 8 + 4 * P * k + 16 * P * k
 
 
 def _oracle_partition(name, p, seed, barrier, results):

@@ -177,8 +177,9 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
  *   The selection of M_{t+1} reads the threshold record of slot (t-1)&1
  *   (see scape_mask_view) to bound its candidate capture, and writes the
  *   record of slot t&1.
- *   1. a^i = grads[i] + e[i]; error-feedback compression at M_t into the
- *      K sparse buffers (kept in the workspace); e updated in place.
+ *   1. a^i = grads[i] + e[i]; error-feedback compression at M_t; e updated
+ *      in place.  The K workers' sparse buffers are summed in registers;
+ *      only the owner's is kept (in the workspace), for the exact recount.
  *   2. statistic per partition p with owner o: s = b1*m + (1-b1)*a^o, using
  *      m before this step's update; M_{t+1} = per-partition top-k of |s|.
  *   3. b_bar = worker mean of the sparse buffers; AdamS at M_t.

@@ -146,7 +146,9 @@ struct AdamsC {
 // STEP true: the fused step pass.  Besides compressing, it keeps each masked
 // element's worker sum S = ((a^0 + a^1) + ...) + a^{K-1} in registers (the
 // single synchronised buffer of the technical summary §2: on one device all
-// K workers' entries of an element are in the same thread), applies AdamS
+// K workers' entries of an element are in the same thread), so of the
+// sparse buffers only the owner's is written (the exact recount of the
+// selection rebuilds the owner's a from it), applies AdamS
 // there with x = S * fp32(1/K) (SCAPE paper §II-C eq. (2)), and saves the
 // pre-update m of masked elements to mold[rank] for the exact fallback;
 // the owner's statistic reads m before its update.
@@ -254,7 +256,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
 #pragma unroll
               for (int q = 0; q < 4; ++q)
                 if ((nib[u] >> q) & 1u) {
-                  if ((int64_t)rr < rlim) bt[rr] = a[q];
+                  if ((!STEP || own) && (int64_t)rr < rlim) bt[rr] = a[q];
                   ++rr;
                   if (STEP) S[u][q] = (i == 0) ? a[q] : S[u][q] + a[q];
                 }

@@ -116,6 +116,40 @@ def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
 
+def _need(t, name: str, numel: int, dtype: str = "float32", pinned: bool = False) -> None:
+    """Checks a tensor argument before its address reaches the device: a
+    host tensor, a wrong dtype or a short buffer would otherwise turn into a
+    device memory fault.  None passes (the library reports null pointers)."""
+    if t is None:
+        return
+    import torch
+    if pinned:
+        if t.is_cuda or not t.is_pinned():
+            raise ValueError(f"{name} must be pinned host memory")
+    elif not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != getattr(torch, dtype):
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < numel * (t.element_size() if dtype is not None else 1):
+        raise ValueError(f"{name} is too small: {t.numel()} elements of {t.element_size()} bytes, "
+                         f"needs {numel}{'' if dtype is not None else ' bytes'}")
+
+
+def _need_state(d: Dims, params, m, v, grads=None, e=None, e_pinned=False) -> None:
+    n, K = d.n, d.num_workers
+    _need(params, "params", n)
+    _need(m, "m", n)
+    _need(v, "v", n)
+    _need(grads, "grads", K * n)
+    _need(e, "e", K * n, pinned=e_pinned)
+
+
+def _pk(d: Dims, k: int) -> int:
+    return d.num_partitions * int(k)
+
+
 def _stream(stream) -> int:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -178,26 +212,38 @@ def view_from_tensors(bits=None, idx=None, tile_off=None, meta=None) -> MaskView
 
 
 def mask_topk(d: Dims, k: int, stat, out: MaskView, workspace, stream=None) -> None:
+    _need(stat, "stat", d.n)
+    _need(workspace, "workspace", workspace_bytes(d, k), dtype=None)
     _check(lib().scape_mask_topk(ctypes.byref(d), k, _ptr(stat), out, _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def compress(d: Dims, k: int, grads, e, cur: MaskView, b, stream=None) -> None:
+    _need(grads, "grads", d.num_workers * d.n)
+    _need(e, "e", d.num_workers * d.n)
+    _need(b, "b", d.num_workers * _pk(d, k))
     _check(lib().scape_compress(ctypes.byref(d), k, _ptr(grads), _ptr(e), cur, _ptr(b), _stream(stream)))
 
 
 def reduce_sparse(d: Dims, k: int, b, b_bar, stream=None) -> None:
+    _need(b, "b", d.num_workers * _pk(d, k))
+    _need(b_bar, "b_bar", _pk(d, k))
     _check(lib().scape_reduce_sparse(ctypes.byref(d), k, _ptr(b), _ptr(b_bar), _stream(stream)))
 
 
 def adams_update(d: Dims, k: int, params, m, v, b_bar, cur: MaskView, bt: Betas, lr: float, step: int,
                  stream=None) -> None:
+    _need_state(d, params, m, v)
+    _need(b_bar, "b_bar", _pk(d, k))
     _check(lib().scape_adams_update(ctypes.byref(d), k, _ptr(params), _ptr(m), _ptr(v), _ptr(b_bar), cur,
                                     bt, lr, step, _stream(stream)))
 
 
 def step(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: float, step_no: int,
          workspace, stream=None) -> None:
+    _need_state(d, params, m, v, grads, e)
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _need(workspace, "workspace", workspace_bytes(d, k), dtype=None)
     _check(lib().scape_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
                             _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -222,6 +268,10 @@ def step_graph(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr
     """scape_step_graph: one step t >= 2 with M_t in slot cur_slot and the
     bias state (device tensor of bias_state_tensor) advanced on the device;
     safe to record into a graph."""
+    _need_state(d, params, m, v, grads, e)
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _need(bias_state, "bias_state", ctypes.sizeof(BiasState), dtype=None)
+    _need(workspace, "workspace", workspace_bytes(d, k), dtype=None)
     _check(lib().scape_step_graph(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
                                   _ptr(mask_blob), k, bt, lr, cur_slot, _ptr(bias_state), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -235,6 +285,10 @@ def step_offload(d: Dims, params, grads, m, v, e_host, mask_blob, k: int, bt: Be
                  workspace, stage, chunk_parts: int, stream=None, copy_in=None, copy_out=None) -> None:
     """scape_step with e_host ([K][n] fp32, pinned host memory) staged
     through `stage` in chunks of chunk_parts partitions on two copy streams."""
+    _need_state(d, params, m, v, grads, e_host, e_pinned=True)
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _need(workspace, "workspace", workspace_bytes(d, k), dtype=None)
+    _need(stage, "stage", offload_stage_bytes(d, k, chunk_parts), dtype=None)
     _check(lib().scape_step_offload(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e_host),
                                     _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _ptr(stage),
@@ -243,15 +297,20 @@ def step_offload(d: Dims, params, grads, m, v, e_host, mask_blob, k: int, bt: Be
 
 
 def mask_union(d: Dims, k: int, acc_bits, m: MaskView, count_out, stream=None) -> None:
+    n_p = d.n // d.num_partitions
+    _need(acc_bits, "acc_bits", d.num_partitions * ((n_p + 63) // 64) * 8, dtype=None)
+    _need(count_out, "count_out", 8, dtype=None)
     _check(lib().scape_mask_union(ctypes.byref(d), k, _ptr(acc_bits), m, _ptr(count_out), _stream(stream)))
 
 
 def dense_adams_step(d: Dims, params, grads, m, v, bt: Betas, lr: float, step_no: int, stream=None) -> None:
+    _need_state(d, params, m, v, grads)
     _check(lib().scape_dense_adams_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), bt, lr,
                                         step_no, _stream(stream)))
 
 
 def mask_overlap(d: Dims, k: int, a: MaskView, b: MaskView, count_out, stream=None) -> None:
+    _need(count_out, "count_out", 8, dtype=None)
     _check(lib().scape_mask_overlap(ctypes.byref(d), k, a, b, _ptr(count_out), _stream(stream)))
 
 

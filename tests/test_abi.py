@@ -212,3 +212,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(S, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         S.lib()
+
+
+def test_binding_checks_tensor_arguments_before_the_device_sees_them():
+    """Host tensors, wrong dtypes and short buffers are refused by the
+    binding (they would be device memory faults, not errors, in the library)."""
+    torch = pytest.importorskip("torch")
+    d = S.dims(4096, 2, 2)
+    cpu = torch.zeros(4096)
+    with pytest.raises(ValueError, match="device tensor"):
+        S.step(d, cpu, None, None, None, None, None, 10, S.betas(), 1e-3, 1, None)
+    with pytest.raises(ValueError, match="pinned host memory"):
+        S._need(torch.zeros(4), "e", 4, pinned=True)
+    meta = torch.device("meta")
+    with pytest.raises(ValueError, match="device tensor"):
+        S._need(torch.zeros(4, device=meta), "x", 4)
+    # dtype, contiguity and size are checked on device tensors; a fake stand-in
+    # for one is enough here (no GPU in this test)
+    class Fake:
+        is_cuda = True
+        def __init__(self, dtype, n, contiguous=True, esize=4):
+            self.dtype, self._n, self._c, self._e = dtype, n, contiguous, esize
+        def numel(self): return self._n
+        def element_size(self): return self._e
+        def is_contiguous(self): return self._c
+        def is_pinned(self): return False
+    with pytest.raises(ValueError, match="float32"):
+        S._need(Fake(torch.float16, 4096, esize=2), "params", 4096)
+    with pytest.raises(ValueError, match="contiguous"):
+        S._need(Fake(torch.float32, 4096, contiguous=False), "params", 4096)
+    with pytest.raises(ValueError, match="too small"):
+        S._need(Fake(torch.float32, 4095), "params", 4096)
+    with pytest.raises(ValueError, match="too small"):
+        S._need(Fake(torch.uint8, 99, esize=1), "workspace", 100, dtype=None)
+    S._need(Fake(torch.float32, 4096), "params", 4096)
+    S._need(Fake(torch.uint8, 100, esize=1), "workspace", 100, dtype=None)

@@ -383,12 +383,20 @@ def test_step_deterministic_and_resumable(S):
 
 
 def test_step_rejects_bad_arguments_on_device(S):
+    """A short workspace: the binding refuses it, and so does the library
+    itself when called directly (before anything is enqueued)."""
+    import ctypes
     d = S.dims(4096, 2, 2)
     t = torch.zeros(4096, device=DEV)
-    with pytest.raises(S.ScapeError, match="EWORKSPACE"):
-        S.step(d, t, torch.zeros(2, 4096, device=DEV), t, t, torch.zeros(2, 4096, device=DEV),
-               torch.zeros(S.mask_bytes(d, 10), dtype=torch.uint8, device=DEV), 10, S.betas(), 1e-3, 1,
-               torch.empty(16, dtype=torch.uint8, device=DEV))
+    g2 = torch.zeros(2, 4096, device=DEV)
+    mask = torch.zeros(S.mask_bytes(d, 10), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError, match="workspace"):
+        S.step(d, t, g2, t, t, g2, mask, 10, S.betas(), 1e-3, 1, ws)
+    st = S.lib().scape_step(ctypes.byref(d), t.data_ptr(), g2.data_ptr(), t.data_ptr(), t.data_ptr(), g2.data_ptr(),
+                            mask.data_ptr(), 10, S.betas(), 1e-3, 1, ws.data_ptr(), 16,
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == 3 and b"workspace" in S.lib().scape_last_error()
 
 
 def _poison_bounds(S, value_fn):

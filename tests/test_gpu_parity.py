@@ -382,6 +382,34 @@ def test_step_deterministic_and_resumable(S):
         assert np.array_equal(ra.view(np.uint8), host(getattr(d, name)).view(np.uint8)), name
 
 
+@pytest.mark.parametrize("n_p,P,K,sp", [(300_000, 2, 2, "0.99"), (10_007, 3, 4, "0.9")])
+def test_step_rebootstrap_on_existing_state(S, n_p, P, K, sp):
+    """Step 1 again after three steps: the bootstrap builds M_1 from the
+    current m and residuals (not zeros), the bias correction restarts, and
+    the next steps go on from there; bitwise equal to the oracle."""
+    cfg = W.flat_config("reboot", P * n_p, P, K, sp, steps=5, weight_decay=0.01)
+    n, k = cfg.n, cfg.k
+    w0 = W.init_params(cfg, 0)
+    hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    ora = O.OracleOptimizer(w0, P, K, k, hp)
+    opt = S.ScapeOptimizer(dev(w0), P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    for t in range(1, 6):
+        if t == 4:  # restart the step count: the next call is a step-1 call again
+            opt.t = 0
+            ora.t = 0
+        g = W.grads(cfg, t, 0)
+        print(f"[reboot] n_p={n_p} P={P} K={K} call {t} (step {opt.t + 1})", flush=True)
+        opt.step(dev(g))
+        outs = ora.step(g)
+        torch.cuda.synchronize()
+        check_mask(*opt.slot("next"), [o["nxt"] for o in outs], n_p)
+        check_mask(*opt.slot("current"), [o["cur"] for o in outs], n_p)
+        for name in ("w", "m", "v", "e"):
+            got = host(getattr(opt, "params" if name == "w" else name))
+            want = ora.gather(name)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"call {t}: {name} differs"
+
+
 def test_step_rejects_bad_arguments_on_device(S):
     """A short workspace: the binding refuses it, and so does the library
     itself when called directly (before anything is enqueued)."""

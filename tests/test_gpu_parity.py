@@ -110,6 +110,8 @@ def _sampled_tiles_large(P, n_p, seed):
     ("const", 1, 64 * 4096, 1_000),           # every key in one digit: all captured
     ("normal", 3, 64 * 4096, 1),
     ("sampled_large", 2, 80 * 4096, 65_536),  # sample misleads: captured < k, exact fallback
+    ("normal", 1, 64 * 4096, 64 * 4096),      # k = n_p: the sample holds fewer keys than its target
+    ("wide", 2, 70 * 4096 + 5, 2_000),        # subnormals .. 1e30, ragged tail, scalar path
 ])
 def test_mask_topk_first_capture(S, kind, P, n_p, k):
     """Partitions of 64 or more tiles take their first capture bound from a

@@ -74,7 +74,8 @@ def main():
 
     lines = [f"# Kernel profile — {a.workload}", ""]
     if a.command:
-        lines += ["Commands (repository root on the GPU box):", "", "```", a.command.strip(), "```", ""]
+        lines += ["Commands ($R: the repository root; $OUT: an output directory):", "", "```", a.command.strip(),
+                  "```", ""]
     lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
     for r in rows:

@@ -412,6 +412,53 @@ def test_step_rebootstrap_on_existing_state(S, n_p, P, K, sp):
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"call {t}: {name} differs"
 
 
+def test_component_chain_equals_fused_step(S):
+    """The method through the component calls (mask_topk on the owner
+    statistic, compress, reduce_sparse, adams_update) gives the fused step's
+    masks and state bit for bit, step after step."""
+    F = np.float32
+    n_p, P, K = 50_000, 4, 3
+    cfg = W.flat_config("chain", P * n_p, P, K, "0.99", steps=4, weight_decay=0.01)
+    n, k = cfg.n, cfg.k
+    w0 = W.init_params(cfg, 0)
+    bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
+    fused = S.ScapeOptimizer(dev(w0), P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    d = S.dims(n, P, K)
+    w, m, v = dev(w0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    e = torch.zeros((K, n), device=DEV)
+    b = torch.zeros((K, P * k), device=DEV)
+    bbar = torch.zeros(P * k, device=DEV)
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+    b1, c1 = F(cfg.beta1), F(1) - F(cfg.beta1)
+    for t in range(1, cfg.steps + 1):
+        g = W.grads(cfg, t, 0)
+        mh, eh = host(m), host(e)
+        stat = np.empty(n, F)
+        for p in range(P):
+            sl = slice(p * n_p, (p + 1) * n_p)
+            o = O.owner(p, P, K)
+            stat[sl] = (b1 * mh[sl]) + (c1 * (g[o, sl] + eh[o, sl]))
+        nxt, cur = S.mask_slot(d, k, blob, t & 1), S.mask_slot(d, k, blob, (t - 1) & 1)
+        S.mask_topk(d, k, dev(stat), nxt, ws)
+        if t == 1:
+            S.mask_topk(d, k, dev(stat), cur, ws)
+        S.compress(d, k, dev(g), e, cur, b)
+        S.reduce_sparse(d, k, b, bbar)
+        S.adams_update(d, k, w, m, v, bbar, cur, bt, cfg.lr, t)
+        fused.step(dev(g))
+        torch.cuda.synchronize()
+        print(f"[chain] step {t}", flush=True)
+        for name, got, want in (("w", w, fused.params), ("m", m, fused.m), ("v", v, fused.v), ("e", e, fused.e)):
+            assert np.array_equal(host(got).view(np.uint32), host(want).view(np.uint32)), f"step {t}: {name} differs"
+        for which in ("next", "current"):
+            sb = (t & 1) if which == "next" else ((t - 1) & 1)
+            mine = S.mask_slot_tensors(d, k, blob, sb)
+            theirs = fused.slot(which)
+            for a_, b_ in zip(mine, theirs):
+                assert torch.equal(a_, b_), f"step {t}: {which} mask differs"
+
+
 def test_step_rejects_bad_arguments_on_device(S):
     """A short workspace: the binding refuses it, and so does the library
     itself when called directly (before anything is enqueued)."""

@@ -10,7 +10,8 @@
 // histogram (key bits 30..19) of the captured keys.  If a partition captured
 // at least k keys, its top k lie among the captures; otherwise an exact
 // fallback recounts all its keys to find the level-1 digit and recaptures
-// from there.  The candidate select pass then reads only the captures:
+// from there.  A first capture, with no previous bound, takes its bound
+// from a histogram of a sample of tiles (kScanSample).  The candidate select pass then reads only the captures:
 // digits above the threshold digit are selected and written as whole mask
 // words, the threshold digit's captures are compacted in place and
 // histogrammed on the next digit.  The remaining levels (key bits 6..0, then
@@ -254,12 +255,12 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave per tile: reads the tile's captured candidates 64 at a time;
-// selects the digits above the level-1 threshold digit into the tile's 64
-// mask words (written whole, so every word of the partition is written);
-// compacts the threshold digit's candidates in place, in order (a write
-// position never passes the chunk being read), and histograms their
-// level-2 digit.
+// One wave per tile: reads the tile's captured candidates in rounds of
+// kCandChunks chunks of 64; selects the digits above the level-1 threshold
+// digit into the tile's 64 mask words (written whole, so every word of the
+// partition is written); compacts the threshold digit's candidates in
+// place, in order (a write position never passes the candidates already
+// read), and histograms their level-2 digit.
 __global__ void __launch_bounds__(kThreads)
 cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ cand,
                    const uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2,
@@ -371,8 +372,7 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
 }
 
 // The compacted candidate lists are walked one wave per tile (each wave
-// takes tiles wave_id, wave_id + nwaves, ...), the lanes striding over the
-// tile's candidates.
+// takes tiles wave_id, wave_id + nwaves, ...).
 // Candidates 0 .. ct-1 of a slot, read by the wave in rounds of
 // kCandChunks chunks of 64 (all loaded before any is used); f(c) runs on
 // the lanes that hold a candidate.

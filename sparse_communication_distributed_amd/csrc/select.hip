@@ -515,14 +515,45 @@ scan_tiles_kernel(Geom g, const uint32_t* __restrict__ tilecnt, uint32_t* __rest
   }
 }
 
+// Position of the r-th set bit (from 0) of a word with more than r set bits.
+__device__ __forceinline__ uint32_t select_bit(uint64_t word, uint32_t r) {
+  uint32_t pos = 0;
+  uint32_t half = (uint32_t)word;
+  const uint32_t c32 = (uint32_t)__popc(half);
+  if (r >= c32) {
+    r -= c32;
+    pos = 32;
+    half = (uint32_t)(word >> 32);
+  }
+#pragma unroll
+  for (int sh = 16; sh >= 1; sh >>= 1) {
+    const uint32_t c = (uint32_t)__popc(half & ((1u << sh) - 1u));
+    if (r >= c) {
+      r -= c;
+      pos += sh;
+      half >>= sh;
+    }
+  }
+  return pos;
+}
+
 // One wave per tile: write the tile's selected global indices in order.
+// RANKS false (sparse masks): each lane walks the set bits of its own word.
+// RANKS true (denser masks, where a lane's word holds several indices): the
+// lanes take ranks r, r + 64, ... within the tile, so consecutive lanes
+// write consecutive entries of the index list; rank r lies in the last word
+// whose exclusive popcount prefix is at most r (a binary search over the
+// tile's 64 prefixes in LDS), at that word's (r - prefix)-th set bit.
+template <bool RANKS>
 __global__ void __launch_bounds__(kThreads)
 write_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
                  uint32_t* __restrict__ idx) {
+  __shared__ unsigned long long swords[RANKS ? kThreads / 64 : 1][kWordsPerTile];
+  __shared__ uint32_t spre[RANKS ? kThreads / 64 : 1][kWordsPerTile];
   const int p = blockIdx.y;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (t >= g.tpp) return;
-  const uint32_t lane = lane_id();
+  if (t >= g.tpp) return;  // wave-uniform; the waves synchronise only among their own lanes
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   const int64_t w = t * kWordsPerTile + lane;
   uint64_t word = (w < g.wpp) ? bits[(int64_t)p * g.wpp + w] : 0ull;
   const uint32_t c = (uint32_t)__popcll(word);
@@ -532,13 +563,31 @@ write_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __re
     const uint32_t y = __shfl_up(x, d, 64);
     if ((int)lane >= d) x += y;
   }
-  int64_t pos = (int64_t)tile_off[(int64_t)p * g.tpp + t] + (x - c);
+  const int64_t base = (int64_t)tile_off[(int64_t)p * g.tpp + t];
   uint32_t* out = idx + (int64_t)p * g.k;
-  const uint32_t jbase = (uint32_t)((int64_t)p * g.n_p + w * 64);
-  while (word) {
-    if (pos < g.k) out[pos] = jbase + (uint32_t)__builtin_ctzll(word);  // bound: malformed mask
-    ++pos;
-    word &= word - 1ull;
+  if (!RANKS) {
+    int64_t pos = base + (x - c);
+    const uint32_t jbase = (uint32_t)((int64_t)p * g.n_p + w * 64);
+    while (word) {
+      if (pos < g.k) out[pos] = jbase + (uint32_t)__builtin_ctzll(word);  // bound: malformed mask
+      ++pos;
+      word &= word - 1ull;
+    }
+    return;
+  }
+  const uint32_t sw = RANKS ? wave : 0u;  // this wave's rows of the LDS arrays
+  swords[sw][lane] = word;
+  spre[sw][lane] = x - c;
+  const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
+  wave_lds_sync();
+  const uint32_t tbase = (uint32_t)((int64_t)p * g.n_p + t * kTile);
+  for (uint32_t r = lane; r < total; r += 64) {
+    uint32_t q = 0;
+#pragma unroll
+    for (uint32_t step = 32; step >= 1; step >>= 1)
+      if (spre[sw][q + step] <= r) q += step;
+    const uint32_t j = select_bit(swords[sw][q], r - spre[sw][q]);
+    if (base + r < g.k) out[base + r] = tbase + q * 64 + j;  // bound: malformed mask
   }
 }
 
@@ -617,7 +666,11 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
   if (mark) mark(ctx, 2);
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
   scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, w.tilecnt, tile_off, w.state, meta_out);
-  write_idx_kernel<<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
+  // rank-parallel emission pays from a mask density of about 5% on
+  if (g.k * 20 >= g.n_p)
+    write_idx_kernel<true><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
+  else
+    write_idx_kernel<false><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
   return hipGetLastError();
 }
 

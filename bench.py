@@ -433,7 +433,9 @@ def main():
         "bootstrap_step": {"ms": boot_ms, "stage_ms": boot_stages},
         "roofline": {"bound": "hbm", "kernel": "compress_kernel (step pass)", "achieved": comp_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": comp_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms},
+                     "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms,
+                     # counter-measured bytes over the same launch time
+                     "traffic_gbps": None if traffic is None else traffic / (comp_ms * 1e-3) / 1e9},
         "cpu_baseline": None,
     }
     b_dense = (4 * K + 20) * n

@@ -66,3 +66,26 @@ def _step_cases(count=12, seed=77):
 def test_random_step_lockstep(S, P, K, n_p, sp, law, wd, cid):
     cfg = W.flat_config("random", P * n_p, P, K, sp, steps=3, grad_law=law, config_id=cid, weight_decay=wd)
     run_lockstep(S, cfg, cfg.steps)
+
+
+def _hyper_cases(count=8, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        b1 = float(rng.choice([0.0, 0.5, 0.9, 0.99]))
+        b2 = float(rng.choice([0.0, 0.9, 0.95, 0.999, 0.9999]))
+        eps = float(10.0 ** rng.uniform(-12, -4))
+        lr = float(10.0 ** rng.uniform(-5, -1))
+        wd = float(rng.choice([0.0, 1e-4, 0.1]))
+        out.append((b1, b2, eps, lr, wd, 300 + i))
+    return out
+
+
+@pytest.mark.parametrize("b1,b2,eps,lr,wd,cid", _hyper_cases())
+def test_random_hyper_parameters_lockstep(S, b1, b2, eps, lr, wd, cid):
+    """The fused step under random AdamS hyper-parameters (beta1 = 0 makes
+    the statistic the owner's residual-compensated gradient alone; beta2
+    near 1 makes the bias correction large), bit for bit against the oracle."""
+    cfg = W.flat_config("hyper", 3 * 9_000, 3, 2, "0.95", steps=4, config_id=cid,
+                        beta1=b1, beta2=b2, eps=eps, lr=lr, weight_decay=wd)
+    run_lockstep(S, cfg, cfg.steps)

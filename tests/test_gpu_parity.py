@@ -459,6 +459,28 @@ def test_component_chain_equals_fused_step(S):
                 assert torch.equal(a_, b_), f"step {t}: {which} mask differs"
 
 
+@pytest.mark.parametrize("n_p,P,K", [(4096 * 3 + 16, 4, 3), (1001, 3, 2)])
+def test_step_at_sparsity_zero_equals_dense_adams(S, n_p, P, K):
+    """With every element selected and e starting at 0, the error feedback
+    stays 0 and a SCAPE step is dense AdamS on the worker mean: the fused
+    step and the dense kernel (two separate code paths) agree bit for bit."""
+    cfg = W.flat_config("dense0", P * n_p, P, K, "0", steps=4, weight_decay=0.01)
+    n, k = cfg.n, cfg.k
+    assert k == n_p
+    w0 = W.init_params(cfg, 0)
+    opt = S.ScapeOptimizer(dev(w0), P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    d = S.dims(n, P, K)
+    w, m, v = dev(w0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    for t in range(1, cfg.steps + 1):
+        g = dev(W.grads(cfg, t, 0))
+        opt.step(g)
+        S.dense_adams_step(d, w, g, m, v, opt.bt, cfg.lr, t)
+        torch.cuda.synchronize()
+        for name, a_, b_ in (("w", opt.params, w), ("m", opt.m, m), ("v", opt.v, v)):
+            assert np.array_equal(host(a_).view(np.uint32), host(b_).view(np.uint32)), f"step {t}: {name}"
+        assert not torch.any(opt.e != 0), f"step {t}: e is not zero"
+
+
 def test_step_rejects_bad_arguments_on_device(S):
     """A short workspace: the binding refuses it, and so does the library
     itself when called directly (before anything is enqueued)."""

@@ -451,6 +451,7 @@ def main():
     b_dense = (4 * K + 20) * n
     out["dense_adams"] = {"ms_per_step": dense_ms, "params_per_s": n / (dense_ms * 1e-3),
                           "hbm_gbps_alg": b_dense / (dense_ms * 1e-3) / 1e9,
+                          "hbm_frac_alg": b_dense / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                           "bytes_alg_per_step": b_dense,
                           "note": "local cost only: no collective runs on one GPU"}
     if calib is not None:

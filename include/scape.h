@@ -22,8 +22,8 @@
  *   - Pointers are DEVICE pointers unless stated; the caller allocates and
  *     owns every buffer, including workspaces and mask blobs.  The library
  *     never allocates or frees device memory and keeps no state between
- *     calls, except the HIP events that scape_step_offload and the stage
- *     timing create once per process.
+ *     calls, except the HIP events that scape_step_offload creates once
+ *     per device and the stage timing creates while it is on.
  *   - Arguments are validated synchronously before anything is enqueued; a
  *     failed check returns a status and touches no buffer.
  *   - Work is enqueued on `stream` and the call returns without waiting.
@@ -251,8 +251,10 @@ scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const
  * and the exact recount of the selection read e_host directly.  The three
  * streams must be distinct; `stream` waits for the last copy-out before
  * the call's selection work, so later work on `stream` sees the new e_host.
- * Uses a process-wide set of HIP events (not thread-safe across concurrent
- * offload calls).
+ * `stream`, copy_in and copy_out belong to the current device.  The
+ * pipeline's HIP events are created once per device on first use and
+ * shared by every call on that device; a call holds a process-wide lock
+ * while it enqueues, so calls from several host threads are safe.
  */
 size_t scape_offload_stage_bytes(const scape_dims* dims, int64_t k, int32_t chunk_parts);
 scape_status scape_step_offload(const scape_dims* dims, float* params, const float* grads, float* m,
@@ -291,7 +293,8 @@ const char* scape_last_error(void);
  * scape_profile_collect waits for the recorded events, writes per-stage
  * total milliseconds and launch counts (arrays of scape_profile_stages()
  * entries, host memory) and clears the record.  Stage names come from
- * scape_profile_stage_name().  Not thread-safe.
+ * scape_profile_stage_name().  Not thread-safe: enable it only while a
+ * single host thread makes calls.
  */
 int scape_profile_stages(void);
 const char* scape_profile_stage_name(int stage);

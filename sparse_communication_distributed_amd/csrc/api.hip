@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 namespace scape {
@@ -474,23 +475,32 @@ scape_status step_end(StepCtx& c, hipStream_t stream) {
   return st;
 }
 
-// Events of the offload pipeline, created once per process: per stage
-// buffer, "copied in", "pass done" and "copied out", plus the call's start.
+// Events of the offload pipeline, created once per device on first use:
+// per stage buffer, "copied in", "pass done" and "copied out", plus the
+// call's start.  A call holds g_oev_lock while it enqueues, so that every
+// wait it enqueues refers to a record of the same call (a wait takes the
+// event's latest record at the time it is enqueued).
+constexpr int kMaxDevices = 64;
 struct OffloadEvents {
   bool ready = false;
   hipEvent_t in[2], pass[2], out[2], start;
 };
-OffloadEvents g_oev;
+OffloadEvents g_oev[kMaxDevices];
+std::mutex g_oev_lock;
 
-scape_status offload_events() {
-  if (g_oev.ready) return SCAPE_OK;
-  hipEvent_t* all[7] = {&g_oev.in[0], &g_oev.in[1], &g_oev.pass[0], &g_oev.pass[1],
-                        &g_oev.out[0], &g_oev.out[1], &g_oev.start};
-  for (hipEvent_t* e : all) {
-    scape_status st = hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "offload events");
-    if (st) return st;
+scape_status offload_events(OffloadEvents** out) {
+  int dev = -1;
+  scape_status st = hip_check(hipGetDevice(&dev), "offload device");
+  if (st) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(SCAPE_EHIP, "offload: device %d out of range", dev);
+  OffloadEvents& ev = g_oev[dev];
+  if (!ev.ready) {
+    hipEvent_t* all[7] = {&ev.in[0], &ev.in[1], &ev.pass[0], &ev.pass[1], &ev.out[0], &ev.out[1], &ev.start};
+    for (hipEvent_t* e : all)
+      if ((st = hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "offload events"))) return st;
+    ev.ready = true;
   }
-  g_oev.ready = true;
+  *out = &ev;
   return SCAPE_OK;
 }
 
@@ -572,48 +582,51 @@ scape_status scape_step_offload(const scape_dims* dims, float* params, const flo
   if ((st = step_begin(c, dims, params, grads, m, v, e_host, mask_blob, k, betas, lr, step, workspace,
                        workspace_bytes, stream)))
     return st;
-  if ((st = offload_events())) return st;
+  std::lock_guard<std::mutex> hold(g_oev_lock);
+  OffloadEvents* ev = nullptr;
+  if ((st = offload_events(&ev))) return st;
+  OffloadEvents& oev = *ev;
   const int64_t n_p = g.n_p, chunk = cp * n_p;
   float* sbuf[2] = {static_cast<float*>(stage), static_cast<float*>(stage) + (size_t)g.K * chunk};
   const bool vec = c.vec && aligned16(params) && aligned16(v) && aligned16(stage) && (chunk % 4 == 0);
   const bool seg = vec && seg_ok(g, params, m, v);
   // the copies of this call follow everything already on the compute stream
-  if ((st = hip_check(hipEventRecord(g_oev.start, stream), "offload record"))) return st;
-  if ((st = hip_check(hipStreamWaitEvent(copy_in, g_oev.start, 0), "offload wait"))) return st;
+  if ((st = hip_check(hipEventRecord(oev.start, stream), "offload record"))) return st;
+  if ((st = hip_check(hipStreamWaitEvent(copy_in, oev.start, 0), "offload wait"))) return st;
   const int64_t nchunks = (g.P + cp - 1) / cp;
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     const int b = (int)(ci & 1);
     const int64_t p0 = ci * cp;
     const int64_t np = (p0 + cp <= g.P) ? cp : g.P - p0;
     // stage buffer b is free once the copy-out of chunk ci - 2 is done
-    if (ci >= 2 && (st = hip_check(hipStreamWaitEvent(copy_in, g_oev.out[b], 0), "offload wait"))) return st;
+    if (ci >= 2 && (st = hip_check(hipStreamWaitEvent(copy_in, oev.out[b], 0), "offload wait"))) return st;
     for (int i = 0; i < g.K; ++i) {
       st = hip_check(hipMemcpyAsync(sbuf[b] + (size_t)i * chunk, e_host + (size_t)i * g.n + (size_t)p0 * n_p,
                                     (size_t)np * n_p * 4, hipMemcpyHostToDevice, copy_in),
                      "offload copy in");
       if (st) return st;
     }
-    if ((st = hip_check(hipEventRecord(g_oev.in[b], copy_in), "offload record"))) return st;
-    if ((st = hip_check(hipStreamWaitEvent(stream, g_oev.in[b], 0), "offload wait"))) return st;
+    if ((st = hip_check(hipEventRecord(oev.in[b], copy_in), "offload record"))) return st;
+    if ((st = hip_check(hipStreamWaitEvent(stream, oev.in[b], 0), "offload wait"))) return st;
     StepArgs sa = c.sa;
     sa.e = sbuf[b];
     sa.p0 = (int)p0;
     sa.nparts = (int)np;
     sa.e_stride = chunk;
     if ((st = hip_check(launch_step_pass(g, sa, vec, seg, stream), "step pass"))) return st;
-    if ((st = hip_check(hipEventRecord(g_oev.pass[b], stream), "offload record"))) return st;
-    if ((st = hip_check(hipStreamWaitEvent(copy_out, g_oev.pass[b], 0), "offload wait"))) return st;
+    if ((st = hip_check(hipEventRecord(oev.pass[b], stream), "offload record"))) return st;
+    if ((st = hip_check(hipStreamWaitEvent(copy_out, oev.pass[b], 0), "offload wait"))) return st;
     for (int i = 0; i < g.K; ++i) {
       st = hip_check(hipMemcpyAsync(e_host + (size_t)i * g.n + (size_t)p0 * n_p, sbuf[b] + (size_t)i * chunk,
                                     (size_t)np * n_p * 4, hipMemcpyDeviceToHost, copy_out),
                      "offload copy out");
       if (st) return st;
     }
-    if ((st = hip_check(hipEventRecord(g_oev.out[b], copy_out), "offload record"))) return st;
+    if ((st = hip_check(hipEventRecord(oev.out[b], copy_out), "offload record"))) return st;
   }
   // the selection's fallback reads e_host: wait for every copy-out
   for (int b = 0; b < 2 && b < nchunks; ++b)
-    if ((st = hip_check(hipStreamWaitEvent(stream, g_oev.out[b], 0), "offload wait"))) return st;
+    if ((st = hip_check(hipStreamWaitEvent(stream, oev.out[b], 0), "offload wait"))) return st;
   return step_end(c, stream);
 }
 

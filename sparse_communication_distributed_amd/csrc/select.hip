@@ -497,14 +497,29 @@ scan_tiles_kernel(Geom g, const uint32_t* __restrict__ tilecnt, uint32_t* __rest
   const int64_t lo = threadIdx.x * per;
   const int64_t hi = (lo + per < g.tpp) ? lo + per : g.tpp;
   const uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
+  // a thread's counts are read in batches, all loads of a batch issued
+  // before any is used
+  constexpr int kBatch = 16;
   uint32_t s = 0;
-  for (int64_t t = lo; t < hi; ++t) s += tc[t];
+  for (int64_t t0 = lo; t0 < hi; t0 += kBatch) {
+    uint32_t x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) x[u] = (t0 + u < hi) ? tc[t0 + u] : 0u;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) s += x[u];
+  }
   uint32_t tot;
   uint32_t run = block_excl_scan(s, wtot, &tot);
   uint32_t* to = tile_off + (int64_t)p * g.tpp;
-  for (int64_t t = lo; t < hi; ++t) {
-    to[t] = run;
-    run += tc[t];
+  for (int64_t t0 = lo; t0 < hi; t0 += kBatch) {
+    uint32_t x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) x[u] = (t0 + u < hi) ? tc[t0 + u] : 0u;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (t0 + u < hi) to[t0 + u] = run;
+      run += x[u];
+    }
   }
   if (threadIdx.x == 0) {
     if (tot != (uint32_t)g.k) state[p].fault |= 2u;

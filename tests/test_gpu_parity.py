@@ -584,3 +584,58 @@ def test_step_offload_matches_oracle(S, chunk_parts, poison):
         for name, got, want in (("w", params, ora.gather("w")), ("m", m, ora.gather("m")),
                                 ("v", v, ora.gather("v")), ("e", e_host, ora.gather("e"))):
             assert np.array_equal(host(got).view(np.uint32), want.view(np.uint32)), f"step {t} {name}"
+
+
+def test_step_offload_two_host_threads(S):
+    """Two host threads run offloaded steps at once, each on its own
+    buffers and three streams of its own: both match the oracle bit for bit
+    (the pipeline's events are shared per device; each call enqueues its
+    records and waits without another call's in between)."""
+    import threading
+    cfg = W.flat_config("offload2", 4 * 10_000, 4, 2, "0.99", steps=4)
+    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
+    hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    d = S.dims(n, P, K)
+    grads = {t: W.grads(cfg, t) for t in range(1, cfg.steps + 1)}
+    ora = O.OracleOptimizer(W.init_params(cfg), P, K, k, hp)
+    want = []
+    for t in range(1, cfg.steps + 1):
+        ora.step(grads[t])
+        want.append({name: ora.gather(name).copy() for name in ("w", "m", "v", "e")})
+    results, errors = {}, []
+
+    def worker(tid, chunk_parts):
+        try:
+            torch.cuda.set_device(DEV)
+            params = dev(W.init_params(cfg))
+            m = torch.zeros(n, device=DEV)
+            v = torch.zeros(n, device=DEV)
+            e_host = torch.zeros((K, n), dtype=torch.float32, pin_memory=True)
+            mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+            ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+            stage = torch.empty(S.offload_stage_bytes(d, k, chunk_parts), dtype=torch.uint8, device=DEV)
+            s, cin, cout = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+            got = []
+            with torch.cuda.stream(s):
+                for t in range(1, cfg.steps + 1):
+                    g = dev(grads[t])
+                    S.step_offload(d, params, g, m, v, e_host, mask, k, S.betas(), cfg.lr, t, ws, stage,
+                                   chunk_parts, stream=s, copy_in=cin, copy_out=cout)
+                    s.synchronize()
+                    got.append({"w": host(params), "m": host(m), "v": host(v), "e": host(e_host).copy()})
+            results[tid] = got
+        except Exception as exc:  # reported by the main thread
+            errors.append(f"thread {tid}: {exc!r}")
+
+    threads = [threading.Thread(target=worker, args=(i, cp)) for i, cp in enumerate((1, 3))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=300)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for tid, got in results.items():
+        for t, (g_, w_) in enumerate(zip(got, want), start=1):
+            for name in ("w", "m", "v", "e"):
+                assert np.array_equal(g_[name].view(np.uint32), w_[name].view(np.uint32)), f"thread {tid} step {t} {name}"
+

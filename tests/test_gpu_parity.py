@@ -276,10 +276,12 @@ def _offset_view(x, offset):
 
 
 def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=None, before_step=None,
-                 offset=0):
+                 offset=0, nan_equal=False):
     """Runs the fused GPU step and the oracle side by side from the same
     inputs; compares the next mask and all state after every step.  With
-    `offset`, w, m and v live that many floats into their buffers."""
+    `offset`, w, m and v live that many floats into their buffers.  With
+    `nan_equal`, a NaN on both sides counts as equal whatever its sign and
+    payload."""
     n, P, K, k, n_p = cfg.n, cfg.P, cfg.K, cfg.k, cfg.n_p
     w0 = W.init_params(cfg, seed)
     hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
@@ -302,6 +304,8 @@ def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=N
             got = host(getattr(opt, "params" if name == "w" else name))
             want = ora.gather(name)
             eq = assert_close(got, want, rt, f"step {t} {name}")
+            if nan_equal:
+                eq += int(np.sum(np.isnan(got) & np.isnan(want) & (got.view(np.uint32) != want.view(np.uint32))))
             assert eq == want.size, f"step {t} {name}: {want.size - eq} entries not bitwise equal"
     return opt, ora
 
@@ -336,6 +340,35 @@ def test_step_small_shapes(S, n_p, P, K, sp, law):
     steps = 2 if P >= 20_000 else 4  # the host generator draws per partition
     cfg = W.flat_config("small", P * n_p, P, K, sp, steps=steps, grad_law=law, weight_decay=0.01)
     run_lockstep(S, cfg, cfg.steps)
+
+
+def _extreme_grads(cfg, t):
+    """The workload's gradients with planted extremes: partition 1 wholly
+    subnormal or nearly so (its selected entries run AdamS on subnormals),
+    values whose squares (and sums) overflow, signed zeros, and at step 3
+    also +-inf and NaN."""
+    g = W.grads(cfg, t).copy()
+    g[:, cfg.n_p:2 * cfg.n_p] *= np.float32(1e-38)
+    flat = g.reshape(-1)
+    pos = np.random.default_rng(1000 + t).choice(flat.size, 400, replace=False)
+    flat[pos[:100]] *= np.float32(1e-38)
+    flat[pos[100:150]] = np.float32(1e30)
+    flat[pos[150:170]] = np.float32(3e38)
+    flat[pos[170:200]] = np.float32(-0.0)
+    if t == 3:
+        flat[pos[200:205]] = np.inf
+        flat[pos[205:210]] = -np.inf
+        flat[pos[210:213]] = np.nan
+    return g
+
+
+def test_step_extreme_gradients(S):
+    """Subnormal, overflowing, infinite and NaN gradients: masks bit for bit
+    (a NaN statistic's key lies above +inf on both sides), state bit for bit
+    except that NaNs may differ in sign and payload (IEEE 754 leaves the
+    encoding of a NaN produced by an invalid operation open)."""
+    cfg = W.flat_config("extreme", 3 * 5000, 3, 2, "0.9", steps=5)
+    run_lockstep(S, cfg, cfg.steps, grad_fn=lambda t: _extreme_grads(cfg, t), nan_equal=True)
 
 
 @pytest.mark.parametrize("n_p,offset,sp", [

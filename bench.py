@@ -10,7 +10,10 @@ before the timed region; the timed region is bracketed by synchronisations
 and holds exactly --steps calls.  Prints one JSON line.
 
 Algorithmic bytes per step (what the method must move, independent of this
-implementation):  B = (12K + 4 + (K+1)/8) * n + (8K + 28) * P * k.
+implementation):  B = (12K + 4 + (K+1)/8) * n + (8K + 24) * P * k, and
+4 * P * k more where v_t is also stored (--store-v).  AdamS keeps no second
+moment (it is rebuilt from m_{t-1} every step), so by default the step
+stores none; the bench line also times the step that stores it.
 """
 
 import argparse
@@ -32,19 +35,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def alg_bytes_step(n, P, K, k):
-    return (12 * K + 4 + (K + 1) / 8) * n + (8 * K + 28) * P * k
+def alg_bytes_step(n, P, K, k, v_out=False):
+    return (12 * K + 4 + (K + 1) / 8) * n + (8 * K + 24 + (4 if v_out else 0)) * P * k
 
 
-def alg_bytes_step_pass(n, P, K, k):
+def alg_bytes_step_pass(n, P, K, k, v_out=False):
     """The fused step pass: K workers read g and e and write e, the owner
     statistic reads m, the mask words are read once, the owner's sparse
     buffer is written (the workers' values are summed in registers, so the
     other K-1 buffers are not needed on one device), and AdamS reads w and
-    writes w, m, v at the P*k masked elements (its m read is the
-    statistic's).  Candidate captures and the saved pre-update m are
-    implementation traffic, not counted."""
-    return (12 * K + 4) * n + n / 8 + 4 * P * k + 16 * P * k
+    writes w and m (and v, if stored) at the P*k masked elements (its m
+    read is the statistic's).  Candidate captures and the saved pre-update
+    m are implementation traffic, not counted."""
+    return (12 * K + 4) * n + n / 8 + 4 * P * k + (16 if v_out else 12) * P * k
 
 
 def _oracle_partition(name, p, seed, barrier, results):
@@ -188,7 +191,7 @@ def offload_bench(S, W, cfg, args, log_fn):
     params = torch.empty(n, dtype=torch.float32, device=dev)
     W.device_init_params(cfg, args.seed, params)
     m = torch.zeros(n, dtype=torch.float32, device=dev)
-    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev) if args.store_v else None
     log_fn(f"pinning {K * n * 4 / 1e9:.1f} GB of host memory for e")
     e_host = torch.zeros((K, n), dtype=torch.float32, pin_memory=True)
     mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
@@ -279,6 +282,8 @@ def main():
                     help="also time two steps captured in a HIP graph (scape_step_graph) and replayed")
     ap.add_argument("--study", choices=["fillin"], default=None,
                     help="run a study instead of the step benchmark")
+    ap.add_argument("--store-v", action="store_true",
+                    help="the timed steps also store v_t at the masked entries (AdamS never reads it back)")
     ap.add_argument("--calib", action="store_true",
                     help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
     args = ap.parse_args()
@@ -317,7 +322,7 @@ def main():
     params = torch.empty(n, dtype=torch.float32, device=dev)
     W.device_init_params(cfg, args.seed, params)
     m = torch.zeros(n, dtype=torch.float32, device=dev)
-    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev) if args.store_v else None
     e = torch.zeros((K, n), dtype=torch.float32, device=dev)
     mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
     ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
@@ -335,10 +340,10 @@ def main():
 
     t = 0
 
-    def one_step():
+    def one_step(v_out=v):
         nonlocal t
         t += 1
-        S.step(d, params, pool[(t - 1) % len(pool)], m, v, e, mask, k, bt, cfg.lr, t, ws, stream)
+        S.step(d, params, pool[(t - 1) % len(pool)], m, v_out, e, mask, k, bt, cfg.lr, t, ws, stream)
 
     for _ in range(args.warmup):
         one_step()
@@ -388,6 +393,23 @@ def main():
     dense_ms = ev2.elapsed_time(ev3) / args.steps
     log(f"dense AdamS: {dense_ms:.3f} ms/step")
 
+    # the same steps storing v_t as well (an output AdamS never reads back)
+    vstore = None
+    if v is None:
+        v_keep = torch.zeros(n, dtype=torch.float32, device=dev)
+        one_step(v_keep)
+        torch.cuda.synchronize()
+        ev2.record(stream)
+        for _ in range(args.steps):
+            one_step(v_keep)
+        ev3.record(stream)
+        torch.cuda.synchronize()
+        vs_ms = ev2.elapsed_time(ev3) / args.steps
+        del v_keep
+        log(f"steps storing v: {vs_ms:.3f} ms/step")
+        vstore = {"ms_per_step": vs_ms, "params_per_s": n / (vs_ms * 1e-3),
+                  "hbm_gbps_alg": alg_bytes_step(n, P, K, k, True) / (vs_ms * 1e-3) / 1e9}
+
     graph_rec = None
     if args.graph:  # continues the SCAPE steps: t steps done, M_{t+1} in slot t & 1
         graph_rec = graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, cfg.lr, t, ws, args.steps, log)
@@ -405,14 +427,14 @@ def main():
     S.profile_enable(False)
     log(f"bootstrap step (t = 1): {boot_ms:.3f} ms")
 
-    b_step = alg_bytes_step(n, P, K, k)
-    b_comp = alg_bytes_step_pass(n, P, K, k)
+    b_step = alg_bytes_step(n, P, K, k, args.store_v)
+    b_comp = alg_bytes_step_pass(n, P, K, k, args.store_v)
     gbps = b_step / (ms * 1e-3) / 1e9
     comp_ms = stage_ms.get("step_pass", float("nan"))
     comp_gbps = b_comp / (comp_ms * 1e-3) / 1e9
     traffic = None
     prof_path = os.path.join(ROOT, "profiles", f"step_pass_{cfg.name}_counters.json")
-    if os.path.exists(prof_path):
+    if os.path.exists(prof_path) and not args.store_v:  # the counters come from the default (v-less) bench
         from sparse_communication_distributed_amd.prof_summary import step_pass_source_hash
         with open(prof_path) as f:
             doc = json.load(f)
@@ -434,7 +456,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "n_params": n, "tensors": len(cfg.tensors), "partitions": P,
                    "workers": K, "k_per_partition": k, "sparsity": cfg.sparsity,
-                   "gradient_law": cfg.grad_law, "gradient_sets": args.pool},
+                   "gradient_law": cfg.grad_law, "gradient_sets": args.pool, "v_stored": bool(args.store_v)},
         "hbm_gbps_alg": gbps,
         "hbm_frac_alg": gbps / HBM_PEAK_GBPS,
         "bytes_alg_per_step": b_step,
@@ -448,12 +470,14 @@ def main():
                      "traffic_gbps": None if traffic is None else traffic / (comp_ms * 1e-3) / 1e9},
         "cpu_baseline": None,
     }
-    b_dense = (4 * K + 20) * n
+    b_dense = (4 * K + (20 if args.store_v else 16)) * n
     out["dense_adams"] = {"ms_per_step": dense_ms, "params_per_s": n / (dense_ms * 1e-3),
                           "hbm_gbps_alg": b_dense / (dense_ms * 1e-3) / 1e9,
                           "hbm_frac_alg": b_dense / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                           "bytes_alg_per_step": b_dense,
                           "note": "local cost only: no collective runs on one GPU"}
+    if vstore is not None:
+        out["step_storing_v"] = vstore
     if calib is not None:
         out["stream_calibration"] = calib
     if overlaps:

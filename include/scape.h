@@ -159,8 +159,10 @@ scape_status scape_reduce_sparse(const scape_dims* dims, int64_t k, const float*
  *   mh = mn / (1 - b1^step); vh = vn / (1 - b2^step)   (host-computed fp32
  *                                                        reciprocals)
  *   params[j] = wo - lr*(mh/(sqrt(vh) + eps) + weight_decay*wo)
- *   m[j] = mn; v[j] = vn.
- * Entries off the mask are untouched; v is written, never read.
+ *   m[j] = mn; v[j] = vn (if v is not NULL).
+ * Entries off the mask are untouched.  AdamS keeps no second moment: v_t is
+ * rebuilt from m_{t-1} and the step's gradient every step ([P] §II-C), so
+ * v is an optional output (NULL: not stored), written and never read.
  */
 scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params, float* m,
                                 float* v, const float* b_bar, scape_mask_view cur,
@@ -183,8 +185,10 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
  *   2. statistic per partition p with owner o: s = b1*m + (1-b1)*a^o, using
  *      m before this step's update; M_{t+1} = per-partition top-k of |s|.
  *   3. b_bar = worker mean of the sparse buffers; AdamS at M_t.
- * params, m, v [n], e [K][n] and mask_blob are in/out; grads [K][n] is
- * read-only; workspace as scape_workspace_bytes().
+ * params, m [n], e [K][n] and mask_blob are in/out; grads [K][n] is
+ * read-only; workspace as scape_workspace_bytes().  v [n] is an optional
+ * output (NULL: not stored): the uncorrected v_t at the masked entries, as
+ * in scape_adams_update.
  */
 scape_status scape_step(const scape_dims* dims, float* params, const float* grads, float* m,
                         float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
@@ -232,8 +236,9 @@ scape_status scape_step_graph(const scape_dims* dims, float* params, const float
  * per-step time with ([P] abstract; [S] §4).  For every element j:
  *   x = (((grads[0][j] + grads[1][j]) + ...) + grads[K-1][j]) * fp32(1/K)
  *   then the AdamS update of scape_adams_update at j ([P] §II-C eq. (2)).
- * params, m, v [n] in/out; grads [K][n] read-only.  No error feedback, no
- * mask, no workspace.  dims->num_partitions only has to divide n.
+ * params, m [n] in/out; v [n] an optional output (NULL: not stored);
+ * grads [K][n] read-only.  No error feedback, no mask, no workspace.
+ * dims->num_partitions only has to divide n.
  */
 scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const float* grads, float* m,
                                    float* v, scape_betas betas, float lr, int64_t step, hipStream_t stream);

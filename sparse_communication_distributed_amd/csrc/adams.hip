@@ -33,7 +33,7 @@ __device__ __forceinline__ void adams_one(int64_t j, float x, float* __restrict_
   const float u = mh / d;
   const float wn = wo - (c.lr * (u + (c.wd * wo)));
   m[j] = mn;
-  v[j] = vn;
+  if (v) v[j] = vn;  // optional: AdamS never reads v back
   w[j] = wn;
 }
 
@@ -105,7 +105,7 @@ dense_adams_kernel(const float* __restrict__ g, int K, int64_t n, float invK, fl
     }
     if (VEC) {
       __builtin_nontemporal_store((v4f){mn[0], mn[1], mn[2], mn[3]}, reinterpret_cast<v4f*>(m + j0));
-      __builtin_nontemporal_store((v4f){vn[0], vn[1], vn[2], vn[3]}, reinterpret_cast<v4f*>(v + j0));
+      if (v) __builtin_nontemporal_store((v4f){vn[0], vn[1], vn[2], vn[3]}, reinterpret_cast<v4f*>(v + j0));
       __builtin_nontemporal_store((v4f){wn[0], wn[1], wn[2], wn[3]}, reinterpret_cast<v4f*>(w + j0));
     } else {
 #pragma unroll
@@ -113,7 +113,7 @@ dense_adams_kernel(const float* __restrict__ g, int K, int64_t n, float invK, fl
         const int64_t j = j0 + q;
         if (j >= n) break;
         m[j] = mn[q];
-        v[j] = vn[q];
+        if (v) v[j] = vn[q];
         w[j] = wn[q];
       }
     }

@@ -113,11 +113,14 @@ scape_status check_betas(const scape_betas& b, float lr) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-// Whole 64-byte segments of w, m and v per 16 elements: needs aligned
-// segments, and pays only where masked elements are not too rare (at a
-// density of 0.1% the segment reads cost more than the writes save).
+// Whole 64-byte segments of w, m (and v) per 16 elements: needs aligned
+// segments.  A segment costs the read of w's line, which the update reads
+// anyway, so without v it pays at any density; with v it also reads v's
+// line, which pays only where masked elements are not too rare (at a
+// density of 0.1% that read costs more than the whole writes save).
 bool seg_ok(const Geom& g, const void* w, const void* m, const void* v) {
-  return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0 && g.k * 200 >= g.n_p;
+  return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0 &&
+         (v == nullptr || g.k * 200 >= g.n_p);
 }
 
 // fp32(1 / (1 - beta^t)), beta^t formed by t binary64 multiplications by
@@ -356,7 +359,7 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
   Geom g;
   scape_status st = check_dims(dims, k, &g);
   if (st) return st;
-  if (!params || !m || !v || !b_bar || !cur.idx) return fail(SCAPE_EINVAL, "null pointer argument");
+  if (!params || !m || !b_bar || !cur.idx) return fail(SCAPE_EINVAL, "null pointer argument");
   if ((st = check_betas(betas, lr))) return st;
   if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
   const float b1 = betas.beta1, b2 = betas.beta2;
@@ -396,7 +399,7 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   scape_status st = check_dims(dims, k, &c.g);
   if (st) return st;
   const Geom& g = c.g;
-  if (!params || !grads || !m || !v || !e || !mask_blob || !workspace)
+  if (!params || !grads || !m || !e || !mask_blob || !workspace)  // v is optional
     return fail(SCAPE_EINVAL, "null pointer argument");
   if ((st = check_betas(betas, lr))) return st;
   if (!bias && step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
@@ -635,7 +638,7 @@ scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const
   Geom g;
   scape_status st = check_dims(dims, 1, &g);
   if (st) return st;
-  if (!params || !grads || !m || !v) return fail(SCAPE_EINVAL, "null pointer argument");
+  if (!params || !grads || !m) return fail(SCAPE_EINVAL, "null pointer argument");  // v is optional
   if ((st = check_betas(betas, lr))) return st;
   if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
   const float b1 = betas.beta1, b2 = betas.beta2;

@@ -161,7 +161,9 @@ constexpr int kChunkGroup = 2;
 // 128, which the chunk group of 2 fits without spilling).
 constexpr int kStepMinWaves = 4;
 
-template <bool STEP, bool VEC, bool SEG>
+// VOUT: v_t is stored at the masked elements (v non-null).  AdamS never
+// reads v back, so a caller may leave it out.
+template <bool STEP, bool VEC, bool SEG, bool VOUT>
 __global__ void __launch_bounds__(kThreads, kStepMinWaves)
 compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
@@ -285,8 +287,8 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         for (int u = 0; u < kChunkGroup; ++u) {
           float wo[4], vo[4], mn4[4], wn4[4];
           if (SEG) {
-            // w, m and v are written as whole 64-byte segments (4 lanes x 4
-            // elements) wherever a segment holds a masked element, the
+            // w, m (and v) are written as whole 64-byte segments (4 lanes x
+            // 4 elements) wherever a segment holds a masked element, the
             // unmasked elements with the values just read.  A 4-byte write
             // still occupies a whole memory burst; aligned whole segments
             // measured faster than scattered element writes.
@@ -294,7 +296,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             const uint64_t act = __ballot(nib[u] != 0u);
             if (!((act >> (lane & ~3u)) & 0xfull) || o[u] >= tn) continue;
             load4t(wt, o[u], wo);
-            load4t(vt, o[u], vo);
+            if (VOUT) load4t(vt, o[u], vo);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               mn4[q] = ma[u][q];
@@ -325,7 +327,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
               wn4[q] = wn;
             } else {
               mw[o[u] + q] = mn;
-              vt[o[u] + q] = vn;
+              if (VOUT) vt[o[u] + q] = vn;
               wt[o[u] + q] = wn;
             }
             if ((int64_t)rr < rlim) ot[rr] = mo;
@@ -333,7 +335,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
           }
           if (SEG) {
             store4t(mw, o[u], mn4);
-            store4t(vt, o[u], vo);
+            if (VOUT) store4t(vt, o[u], vo);
             store4t(wt, o[u], wn4);
           }
         }
@@ -483,31 +485,36 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
   const dim3 grid = stream_grid(g.P, g.G);
   AdamsC ac{};
   if (vec)
-    compress_kernel<false, true, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
-                                                                  nullptr, nullptr, ac, nullptr, nullptr, nullptr,
-                                                                  nullptr, 0, g.n, nullptr);
+    compress_kernel<false, true, false, false><<<grid, kThreads, 0, s>>>(
+        g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
+        0, g.n, nullptr);
   else
-    compress_kernel<false, false, false><<<grid, kThreads, 0, s>>>(g, grads, e, bits, tile_off, b, nullptr, nullptr,
-                                                                   nullptr, nullptr, ac, nullptr, nullptr, nullptr,
-                                                                   nullptr, 0, g.n, nullptr);
+    compress_kernel<false, false, false, false><<<grid, kThreads, 0, s>>>(
+        g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
+        0, g.n, nullptr);
   return hipGetLastError();
 }
 
+template <bool VEC, bool SEG, bool VOUT>
+void launch_step_t(const Geom& g, const StepArgs& a, const AdamsC& ac, hipStream_t s) {
+  compress_kernel<true, VEC, SEG, VOUT><<<stream_grid(a.nparts, g.G), kThreads, 0, s>>>(
+      g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
+      a.e_stride, a.ibc_dev);
+}
+
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
-  const dim3 grid = stream_grid(a.nparts, g.G);
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
-  if (vec && seg)
-    compress_kernel<true, true, true><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
-                                                                a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-                                                                a.e_stride, a.ibc_dev);
-  else if (vec)
-    compress_kernel<true, true, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v,
-                                                                 a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-                                                                 a.e_stride, a.ibc_dev);
-  else
-    compress_kernel<true, false, false><<<grid, kThreads, 0, s>>>(g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m,
-                                                                  a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist,
-                                                                  a.p0, a.e_stride, a.ibc_dev);
+  const bool vout = a.v != nullptr;
+  if (vec && seg) {
+    if (vout) launch_step_t<true, true, true>(g, a, ac, s);
+    else launch_step_t<true, true, false>(g, a, ac, s);
+  } else if (vec) {
+    if (vout) launch_step_t<true, false, true>(g, a, ac, s);
+    else launch_step_t<true, false, false>(g, a, ac, s);
+  } else {
+    if (vout) launch_step_t<false, false, true>(g, a, ac, s);
+    else launch_step_t<false, false, false>(g, a, ac, s);
+  }
   return hipGetLastError();
 }
 

@@ -10,8 +10,9 @@ several times, one file per process: the first gives the kernel table, and
 every file's step-pass average is listed, since large allocations land
 differently in each process and the step pass's duration follows them.
 The HBM counters are scaled by what they read for the 1 GiB calibration
-copy that bench.py --calib runs (reads 1 GiB, writes 1 GiB).  The JSON records a hash of the step
-pass's sources; bench.py ignores it once the sources change.
+copy that bench.py --calib runs (reads 1 GiB, writes 1 GiB).  The JSON
+records a hash of the step pass's sources and of the host code that picks
+its variant; bench.py ignores it once they change.
 """
 
 import argparse
@@ -37,9 +38,10 @@ def _code_only(text: str) -> str:
 
 
 def step_pass_source_hash() -> str:
-    """Hash of the step pass's code (comments and layout ignored)."""
+    """Hash of the step pass's code and of the host code that picks its
+    variant (comments and layout ignored)."""
     h = hashlib.sha256()
-    for name in ("compress.hip", "scape_internal.h"):
+    for name in ("compress.hip", "scape_internal.h", "api.hip"):
         with open(os.path.join(PKG, "csrc", name), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]

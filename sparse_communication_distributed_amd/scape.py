@@ -342,12 +342,15 @@ def profile_collect():
 class ScapeOptimizer:
     """Device state of one SCAPE optimizer over a flat fp32 buffer.
 
-    Holds params, m, v [n], the K error-feedback rows e [K][n], the two-slot
+    Holds params, m [n], the K error-feedback rows e [K][n], the two-slot
     mask blob and the workspace; ``step(grads)`` runs one fused step with
-    grads [K][n] (fp32, device)."""
+    grads [K][n] (fp32, device).  AdamS keeps no second moment (v_t is
+    rebuilt every step); with ``store_v`` the step also writes the
+    uncorrected v_t at the masked entries into ``v`` [n], else ``v`` is
+    None."""
 
     def __init__(self, params, P: int, K: int, k: int, beta1=0.9, beta2=0.95, eps=1e-8,
-                 weight_decay=0.0, lr=1e-3, device=None):
+                 weight_decay=0.0, lr=1e-3, device=None, store_v: bool = True):
         import torch
         self.n = params.numel()
         self.d = dims(self.n, P, K)
@@ -357,7 +360,7 @@ class ScapeOptimizer:
         dev = params.device if device is None else device
         self.params = params.to(dev, torch.float32).contiguous()
         self.m = torch.zeros(self.n, dtype=torch.float32, device=dev)
-        self.v = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(self.n, dtype=torch.float32, device=dev) if store_v else None
         self.e = torch.zeros((K, self.n), dtype=torch.float32, device=dev)
         mb = mask_bytes(self.d, self.k)
         wb = workspace_bytes(self.d, self.k)

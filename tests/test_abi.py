@@ -81,7 +81,9 @@ def _step(d, k, ptrs=None, bt=None, lr=1e-3, step=1, wsb=None):
                         S.workspace_bytes(d, k) if wsb is None else wsb, None)
 
 
-@pytest.mark.parametrize("which", ["params", "grads", "m", "v", "e", "mask", "ws"])
+# v is optional (NULL: the second moment is not stored), so it is not here:
+# with fake addresses a call that passes validation would launch kernels.
+@pytest.mark.parametrize("which", ["params", "grads", "m", "e", "mask", "ws"])
 def test_step_rejects_null_pointers(which):
     d = S.dims(4096, 2, 2)
     assert _step(d, 10, {which: None}) == 1

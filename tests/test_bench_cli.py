@@ -21,11 +21,15 @@ def test_bench_refuses_more_than_one_gpu():
 def test_algorithmic_bytes_formula():
     sys.path.insert(0, ROOT)
     import bench
-    # Llama-1.8B layout, 99% sparsity: 94.49 GB per step
+    # Llama-1.8B layout, 99% sparsity: 94.42 GB per step, 94.49 GB storing v
     n, P, K, k = 1_775_372_288, 32, 4, 554_803
-    assert abs(bench.alg_bytes_step(n, P, K, k) / 1e9 - 94.494) < 0.01
+    assert abs(bench.alg_bytes_step(n, P, K, k) / 1e9 - 94.423) < 0.01
+    assert abs(bench.alg_bytes_step(n, P, K, k, True) / 1e9 - 94.494) < 0.01
+    assert bench.alg_bytes_step(n, P, K, k, True) - bench.alg_bytes_step(n, P, K, k) == 4 * P * k
     # the step pass moves everything except the emitted index list and the read-back of b
-    assert bench.alg_bytes_step_pass(n, P, K, k) < bench.alg_bytes_step(n, P, K, k)
+    for v_out in (False, True):
+        assert bench.alg_bytes_step_pass(n, P, K, k, v_out) < bench.alg_bytes_step(n, P, K, k, v_out)
+    assert bench.alg_bytes_step_pass(n, P, K, k, True) - bench.alg_bytes_step_pass(n, P, K, k) == 4 * P * k
 
 
 def _write_csv(path, header, rows):

@@ -41,3 +41,4 @@ def test_bench_json_line_tiny():
     assert cb["tiny_single_core"]["ms_per_step"] > 0
     assert d["graph"]["ms_per_step"] > 0
     assert d["bootstrap_step"]["ms"] > 0
+    assert d["config"]["v_stored"] is False and d["step_storing_v"]["ms_per_step"] > 0

@@ -196,11 +196,14 @@ def test_adams_update(S, t, wd):
     hp = O.Hyper.make(0.9, 0.95, 1e-8, wd, 1e-3)
     w_t, m_t, v_t = dev(w), dev(m), dev(v)
     x_t, idx_t = dev(x), dev(idx.view(np.int32))  # kept alive until the kernel has run
+    w2, m2 = dev(w), dev(m)
     S.adams_update(S.dims(n, P, 2), k, w_t, m_t, v_t, x_t, S.view_from_tensors(None, idx_t, None),
                    S.betas(0.9, 0.95, 1e-8, wd), 1e-3, t)
+    S.adams_update(S.dims(n, P, 2), k, w2, m2, None, x_t, S.view_from_tensors(None, idx_t, None),
+                   S.betas(0.9, 0.95, 1e-8, wd), 1e-3, t)  # v not stored
     torch.cuda.synchronize()
     O.adams_update(w, m, v, idx.astype(np.int64), x, hp, t)
-    for name, got, want in (("w", w_t, w), ("m", m_t, m), ("v", v_t, v)):
+    for name, got, want in (("w", w_t, w), ("m", m_t, m), ("v", v_t, v), ("w (no v)", w2, w), ("m (no v)", m2, m)):
         eq = assert_close(host(got), want, 1e-6, name)
         assert eq == n, f"{name}: {n - eq} entries not bitwise equal"
 
@@ -214,13 +217,16 @@ def test_dense_adams_step(S, n, P, K):
     w = (rng.standard_normal(n) * 0.02).astype(F32)
     m, v = np.zeros(n, F32), np.zeros(n, F32)
     w_t, m_t, v_t = dev(w), dev(m), dev(v)
+    w2, m2 = dev(w), dev(m)  # the same steps without storing v
     for t in range(1, 5):
         g = (rng.standard_normal((K, n)) * 10.0 ** rng.integers(-5, -1, (K, n))).astype(F32)
         g_t = dev(g)
         S.dense_adams_step(S.dims(n, P, K), w_t, g_t, m_t, v_t, S.betas(0.9, 0.95, 1e-8, 0.01), 1e-3, t)
+        S.dense_adams_step(S.dims(n, P, K), w2, g_t, m2, None, S.betas(0.9, 0.95, 1e-8, 0.01), 1e-3, t)
         O.dense_adams_step(w, m, v, g, hp, t)
         torch.cuda.synchronize()
-        for name, got, want in (("w", w_t, w), ("m", m_t, m), ("v", v_t, v)):
+        for name, got, want in (("w", w_t, w), ("m", m_t, m), ("v", v_t, v), ("w (no v)", w2, w),
+                                ("m (no v)", m2, m)):
             assert np.array_equal(host(got).view(np.uint32), want.view(np.uint32)), f"step {t} {name}"
 
 
@@ -276,19 +282,22 @@ def _offset_view(x, offset):
 
 
 def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=None, before_step=None,
-                 offset=0, nan_equal=False):
+                 offset=0, nan_equal=False, store_v=True):
     """Runs the fused GPU step and the oracle side by side from the same
     inputs; compares the next mask and all state after every step.  With
     `offset`, w, m and v live that many floats into their buffers.  With
     `nan_equal`, a NaN on both sides counts as equal whatever its sign and
-    payload."""
+    payload.  Without `store_v` the step keeps no v and v is not compared."""
     n, P, K, k, n_p = cfg.n, cfg.P, cfg.K, cfg.k, cfg.n_p
     w0 = W.init_params(cfg, seed)
     hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
     ora = O.OracleOptimizer(w0, P, K, k, hp)
-    opt = S.ScapeOptimizer(dev(w0), P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
+    opt = S.ScapeOptimizer(dev(w0), P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr,
+                           store_v=store_v)
     if offset:
-        opt.params, opt.m, opt.v = (_offset_view(x, offset) for x in (opt.params, opt.m, opt.v))
+        opt.params, opt.m = (_offset_view(x, offset) for x in (opt.params, opt.m))
+        if store_v:
+            opt.v = _offset_view(opt.v, offset)
     for t in range(1, steps + 1):
         g = W.grads(cfg, t, seed) if grad_fn is None else grad_fn(t)
         print(f"[lockstep] {cfg.name} n={n} P={P} K={K} k={k} step {t}", flush=True)
@@ -300,7 +309,7 @@ def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=N
         check_mask(*opt.slot("next"), [o["nxt"] for o in outs], n_p)
         check_mask(*opt.slot("current"), [o["cur"] for o in outs], n_p)
         rt = rtol_end if t == steps else rtol_step
-        for name in ("w", "m", "v", "e"):
+        for name in ("w", "m", "v", "e") if store_v else ("w", "m", "e"):
             got = host(getattr(opt, "params" if name == "w" else name))
             want = ora.gather(name)
             eq = assert_close(got, want, rt, f"step {t} {name}")
@@ -387,6 +396,37 @@ def test_step_adams_store_paths(S, n_p, offset, sp):
     run_lockstep(S, cfg, cfg.steps, offset=offset)
 
 
+@pytest.mark.parametrize("n_p,offset,sp", [
+    (4096 + 160, 0, "0.9"),    # whole-segment w/m writes
+    (4096 + 160, 4, "0.9"),    # per-element writes, vector streams
+    (4096 + 160, 1, "0.9"),    # scalar path
+    (4096 + 160, 0, "0.999"),  # whole segments still (no v line to read)
+    (4096 + 164, 0, "0.9"),    # n_p % 16 == 4: per-element writes
+])
+def test_step_without_v(S, n_p, offset, sp):
+    """v not stored (AdamS keeps no second moment): w, m, e and the masks
+    equal the oracle's bit for bit on every store path."""
+    cfg = W.flat_config("nov", 3 * n_p, 3, 2, sp, steps=4, weight_decay=0.01)
+    run_lockstep(S, cfg, cfg.steps, offset=offset, store_v=False)
+
+
+def test_step_without_v_matches_with_v(S):
+    """Two optimizers from the same inputs, one storing v and one not: w, m,
+    e and both mask slots agree bit for bit after every step."""
+    cfg = W.flat_config("nov2", 4 * 30_000, 4, 2, "0.99", steps=5)
+    w0 = dev(W.init_params(cfg))
+    a = S.ScapeOptimizer(w0.clone(), cfg.P, cfg.K, cfg.k, lr=cfg.lr)
+    b = S.ScapeOptimizer(w0.clone(), cfg.P, cfg.K, cfg.k, lr=cfg.lr, store_v=False)
+    assert b.v is None
+    for t in range(1, cfg.steps + 1):
+        g = dev(W.grads(cfg, t))
+        a.step(g)
+        b.step(g)
+        torch.cuda.synchronize()
+        for name in ("params", "m", "e", "mask"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), f"step {t} {name}"
+
+
 def test_step_deterministic_and_resumable(S):
     cfg = W.flat_config("resume", 4 * 50_000, 4, 2, "0.95", steps=8)
     w0 = W.init_params(cfg)
@@ -439,7 +479,7 @@ def test_step_rebootstrap_on_existing_state(S, n_p, P, K, sp):
         torch.cuda.synchronize()
         check_mask(*opt.slot("next"), [o["nxt"] for o in outs], n_p)
         check_mask(*opt.slot("current"), [o["cur"] for o in outs], n_p)
-        for name in ("w", "m", "v", "e"):
+        for name in ("w", "m", "v", "e") if store_v else ("w", "m", "e"):
             got = host(getattr(opt, "params" if name == "w" else name))
             want = ora.gather(name)
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"call {t}: {name} differs"

@@ -479,7 +479,7 @@ def test_step_rebootstrap_on_existing_state(S, n_p, P, K, sp):
         torch.cuda.synchronize()
         check_mask(*opt.slot("next"), [o["nxt"] for o in outs], n_p)
         check_mask(*opt.slot("current"), [o["cur"] for o in outs], n_p)
-        for name in ("w", "m", "v", "e") if store_v else ("w", "m", "e"):
+        for name in ("w", "m", "v", "e"):
             got = host(getattr(opt, "params" if name == "w" else name))
             want = ora.gather(name)
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"call {t}: {name} differs"

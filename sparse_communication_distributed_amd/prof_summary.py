@@ -47,19 +47,59 @@ def step_pass_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def short_name(full: str) -> str:
+    """A kernel's name with its template arguments but without return type,
+    namespaces and parameter list: 'void scape::(anonymous
+    namespace)::compress_kernel<true, true, true, false>(scape::Geom, ...)'
+    becomes 'compress_kernel<true, true, true, false>'; template argument
+    lists longer than 48 characters become '<…>'.  Names that are already
+    short pass through."""
+    s = full.strip()
+    if s.startswith("void "):
+        s = s[5:]
+    depth, cut = 0, len(s)
+    for i, ch in enumerate(s):  # the parameter list opens at the first '(' outside <...>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not s.startswith("(anonymous", i):
+            cut = i
+            break
+    s = s[:cut]
+    head = s.split("<", 1)
+    base = head[0].split("::")[-1]
+    if len(head) == 1:
+        return base
+    targs = "<" + head[1]
+    # long template arguments (library kernels' functors) are elided
+    return base + (targs if len(targs) <= 48 else "<…>")
+
+
+def is_step_pass(name: str) -> bool:
+    """The fused step pass that stores no v: compress_kernel<STEP = true,
+    VEC, SEG, VOUT = false> (the component compression has STEP = false,
+    the v-storing step VOUT = true)."""
+    n = short_name(name)
+    if not n.startswith(STEP_KERNEL + "<"):
+        return False
+    args = [x.strip() for x in n[len(STEP_KERNEL) + 1:-1].split(",")]
+    return len(args) == 4 and args[0] == "true" and args[3] == "false"
+
+
 def read_counter(path, counter):
     per = defaultdict(list)
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] == counter:
-            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return per
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stats", required=True, action="append")
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", default=None, help="FETCH_SIZE run (omit with --write: kernel trace only)")
+    ap.add_argument("--write", default=None)
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", default="")
@@ -69,11 +109,6 @@ def main():
 
     runs = [list(csv.DictReader(open(path))) for path in a.stats]
     rows = runs[0]
-    fetch = read_counter(a.fetch, "FETCH_SIZE")
-    write = read_counter(a.write, "WRITE_SIZE")
-    f_scale = GIB_KIB / (sum(fetch[CALIB_KERNEL]) / len(fetch[CALIB_KERNEL]))
-    w_scale = GIB_KIB / (sum(write[CALIB_KERNEL]) / len(write[CALIB_KERNEL]))
-
     lines = [f"# Kernel profile — {a.workload}", ""]
     if a.command:
         lines += ["Commands ($R: the repository root; $OUT: an output directory):", "", "```", a.command.strip(),
@@ -81,24 +116,34 @@ def main():
     lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
     step_ms = []
     for run in runs:
         for r in run:
-            if r["Name"] == STEP_KERNEL:
+            if is_step_pass(r["Name"]):
                 step_ms.append((float(r["AverageNs"]) / 1e6, float(r["MinNs"]) / 1e6, float(r["MaxNs"]) / 1e6))
     if len(runs) > 1:
-        lines += ["", f"## {STEP_KERNEL} in each profiled process", "",
+        lines += ["", f"## {STEP_KERNEL} (step pass, no v stored) in each profiled process", "",
                   "| process | avg ms | min ms | max ms |", "|---|---|---|---|"]
         lines += [f"| {i + 1} | {av:.3f} | {mn:.3f} | {mx:.3f} |" for i, (av, mn, mx) in enumerate(step_ms)]
+    if not (a.fetch and a.write):  # kernel trace only: no counters file
+        with open(a.out + ".md", "w") as f:
+            f.write("\n".join(lines) + "\n")
+        return
+    fetch = read_counter(a.fetch, "FETCH_SIZE")
+    write = read_counter(a.write, "WRITE_SIZE")
+    f_scale = GIB_KIB / (sum(fetch[CALIB_KERNEL]) / len(fetch[CALIB_KERNEL]))
+    w_scale = GIB_KIB / (sum(write[CALIB_KERNEL]) / len(write[CALIB_KERNEL]))
     lines += ["", "## HBM bytes (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"Calibration copy of 1 GiB: FETCH_SIZE scale {f_scale:.3f}, WRITE_SIZE scale {w_scale:.3f}.", "",
               "| kernel | launches | read GB / launch (scaled) | write GB / launch (scaled) |", "|---|---|---|---|"]
     out = {}
+    step_name = None
     for k in sorted(set(fetch) | set(write)):
         fv, wv = fetch.get(k, []), write.get(k, [])
-        if k == STEP_KERNEL:
+        if is_step_pass(k):
+            step_name = k
             fv, wv = fv[a.step_launches_skip:], wv[a.step_launches_skip:]
         if not fv or not wv:
             continue
@@ -109,8 +154,8 @@ def main():
             lines.append(f"| {k} | {len(fv)} | {rd:.3f} | {wr:.3f} |")
     with open(a.out + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
-    rd, wr = out[STEP_KERNEL]
-    doc = {"workload": a.workload, "kernel": STEP_KERNEL, "source_hash": step_pass_source_hash(),
+    rd, wr = out[step_name]
+    doc = {"workload": a.workload, "kernel": step_name, "source_hash": step_pass_source_hash(),
            "hbm_read_bytes_per_launch": rd * 1e9, "hbm_write_bytes_per_launch": wr * 1e9,
            "hbm_bytes_per_launch": (rd + wr) * 1e9, "fetch_scale": f_scale, "write_scale": w_scale,
            "step_pass_avg_ms_per_process": [av for av, _, _ in step_ms]}

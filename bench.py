@@ -427,6 +427,23 @@ def main():
     S.profile_enable(False)
     log(f"bootstrap step (t = 1): {boot_ms:.3f} ms")
 
+    # a reference rate for the same allocations: torch's own elementwise
+    # kernel adding every worker's gradient row into its error-feedback row
+    # (read g, read e, write e: the step pass's 12K bytes per element);
+    # last, since it changes e
+    for i in range(K):
+        e[i].add_(pool[0][i])
+    ev2.record(stream)
+    for _ in range(2):
+        for i in range(K):
+            e[i].add_(pool[0][i])
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    ref_ms = ev2.elapsed_time(ev3) / 2
+    ref = {"kernel": "torch add_: e[i] += g[i] for every worker", "bytes": 12 * K * n, "ms": ref_ms,
+           "GBps": 12 * K * n / (ref_ms * 1e-3) / 1e9}
+    log(f"reference stream (torch add_ over the e and g rows): {ref_ms:.3f} ms, {ref['GBps']:.0f} GB/s")
+
     b_step = alg_bytes_step(n, P, K, k, args.store_v)
     b_comp = alg_bytes_step_pass(n, P, K, k, args.store_v)
     gbps = b_step / (ms * 1e-3) / 1e9
@@ -478,6 +495,7 @@ def main():
                           "note": "local cost only: no collective runs on one GPU"}
     if vstore is not None:
         out["step_storing_v"] = vstore
+    out["stream_reference"] = ref
     if calib is not None:
         out["stream_calibration"] = calib
     if overlaps:

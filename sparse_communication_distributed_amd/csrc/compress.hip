@@ -281,7 +281,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         // AdamS at the group's masked elements.
         float* wt = w + pbase + tb;
         float* mw = m + pbase + tb;
-        float* vt = v + pbase + tb;
+        float* vt = VOUT ? v + pbase + tb : nullptr;  // v may be null without VOUT
         float* ot = mold + rbase;
 #pragma unroll
         for (int u = 0; u < kChunkGroup; ++u) {

@@ -371,9 +371,10 @@ class ScapeOptimizer:
         self.t = 0
 
     def step(self, grads, stream=None) -> None:
-        self.t += 1
+        t = self.t + 1
         step(self.d, self.params, grads, self.m, self.v, self.e, self.mask, self.k, self.bt, self.lr,
-             self.t, self.ws, stream)
+             t, self.ws, stream)
+        self.t = t  # a rejected call leaves the step count unchanged
 
     def slot(self, which: str = "next"):
         """Mask views (bits, idx, tile_off): "next" = M_{t+1}, "current" = M_t."""

@@ -249,3 +249,14 @@ def test_binding_checks_tensor_arguments_before_the_device_sees_them():
         S._need(Fake(torch.uint8, 99, esize=1), "workspace", 100, dtype=None)
     S._need(Fake(torch.float32, 4096), "params", 4096)
     S._need(Fake(torch.uint8, 100, esize=1), "workspace", 100, dtype=None)
+
+
+def test_optimizer_step_count_unchanged_by_a_rejected_call():
+    """A step the binding refuses (host tensors here: no GPU in this test)
+    leaves ScapeOptimizer's step count, and so its mask slot choice, as it
+    was."""
+    torch = pytest.importorskip("torch")
+    opt = S.ScapeOptimizer(torch.zeros(4096), P=2, K=2, k=10, device="cpu")
+    with pytest.raises(ValueError, match="device tensor"):
+        opt.step(torch.zeros((2, 4096)))
+    assert opt.t == 0

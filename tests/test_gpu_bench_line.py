@@ -42,3 +42,6 @@ def test_bench_json_line_tiny():
     assert d["graph"]["ms_per_step"] > 0
     assert d["bootstrap_step"]["ms"] > 0
     assert d["config"]["v_stored"] is False and d["step_storing_v"]["ms_per_step"] > 0
+    sr = d["stream_reference"]
+    assert sr["bytes"] == 12 * d["config"]["workers"] * n and sr["ms"] > 0
+    assert sr["GBps"] == pytest.approx(sr["bytes"] / (sr["ms"] * 1e-3) / 1e9, rel=1e-9)

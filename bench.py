@@ -39,15 +39,22 @@ def alg_bytes_step(n, P, K, k, v_out=False):
     return (12 * K + 4 + (K + 1) / 8) * n + (8 * K + 24 + (4 if v_out else 0)) * P * k
 
 
-def alg_bytes_step_pass(n, P, K, k, v_out=False):
-    """The fused step pass: K workers read g and e and write e, the owner
-    statistic reads m, the mask words are read once, the owner's sparse
-    buffer is written (the workers' values are summed in registers, so the
-    other K-1 buffers are not needed on one device), and AdamS reads w and
-    writes w and m (and v, if stored) at the P*k masked elements (its m
-    read is the statistic's).  Candidate captures and the saved pre-update
-    m are implementation traffic, not counted."""
-    return (12 * K + 4) * n + n / 8 + 4 * P * k + (16 if v_out else 12) * P * k
+def alg_bytes_step_pass(n, P, K, k, v_out=False, passes=1):
+    """The step pass: every worker reads g and e and writes e, the owner
+    statistic reads m, the owner's sparse buffer is written (the exact
+    recount of the selection needs it), and AdamS reads w and writes w and m
+    (and v, if stored) at the P*k masked elements (its m read is the
+    statistic's).  As one pass (passes = 1) the mask words are read once and
+    the workers' values are summed in registers, so the other K - 1 sparse
+    buffers are not needed.  As K passes (one per non-owner worker, then the
+    owner's) every pass reads the mask words, and each non-owner worker
+    writes its sparse buffer, which the owner pass reads back.  Candidate
+    captures and the saved pre-update m are implementation traffic, not
+    counted."""
+    per_masked = (16 if v_out else 12) + 4
+    if passes > 1:
+        return (12 * K + 4) * n + K * n / 8 + (8 * (K - 1) + per_masked) * P * k
+    return (12 * K + 4) * n + n / 8 + per_masked * P * k
 
 
 def _oracle_partition(name, p, seed, barrier, results):
@@ -445,7 +452,8 @@ def main():
     log(f"reference stream (torch add_ over the e and g rows): {ref_ms:.3f} ms, {ref['GBps']:.0f} GB/s")
 
     b_step = alg_bytes_step(n, P, K, k, args.store_v)
-    b_comp = alg_bytes_step_pass(n, P, K, k, args.store_v)
+    passes = S.step_pass_count(d, k)
+    b_comp = alg_bytes_step_pass(n, P, K, k, args.store_v, passes)
     gbps = b_step / (ms * 1e-3) / 1e9
     comp_ms = stage_ms.get("step_pass", float("nan"))
     comp_gbps = b_comp / (comp_ms * 1e-3) / 1e9
@@ -456,7 +464,7 @@ def main():
         with open(prof_path) as f:
             doc = json.load(f)
         if doc.get("source_hash") == step_pass_source_hash():  # counters of this very kernel
-            traffic = doc.get("hbm_bytes_per_launch")
+            traffic = doc.get("hbm_bytes_per_step_pass")
 
     out = {
         "metric": METRIC,
@@ -480,9 +488,10 @@ def main():
         "stage_ms": stage_ms,
         "profiled_step_ms": step_ms,
         "bootstrap_step": {"ms": boot_ms, "stage_ms": boot_stages},
-        "roofline": {"bound": "hbm", "kernel": "compress_kernel (step pass)", "achieved": comp_gbps,
+        "roofline": {"bound": "hbm", "kernel": "compress_kernel (step pass" + (": K - 1 worker passes, then the owner pass)" if passes > 1 else ")"), "achieved": comp_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": comp_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "bytes_alg_per_launch": b_comp, "ms_per_launch": comp_ms,
+                     "traffic": traffic, "bytes_alg_per_step_pass": b_comp, "ms_per_step_pass": comp_ms,
+                     "launches_per_step_pass": passes,
                      # counter-measured bytes over the same launch time
                      "traffic_gbps": None if traffic is None else traffic / (comp_ms * 1e-3) / 1e9},
         "cpu_baseline": None,

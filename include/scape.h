@@ -101,6 +101,13 @@ typedef struct {
 /* Elements per compaction tile (the granularity of tile_off). */
 int64_t scape_tile_elems(void);
 
+/* Passes over the flat buffer that scape_step and scape_step_graph make
+ * for these dims and k: 1 (every worker's rows in one pass) or K (one pass
+ * per non-owner worker of each partition, then the owner's pass), chosen
+ * by measured speed; the results are the same bit for bit.  -1 if dims/k
+ * are invalid. */
+int32_t scape_step_pass_count(const scape_dims* dims, int64_t k);
+
 /* Bytes of a mask blob holding TWO mask slots (the current mask M_t and the
  * next one, for the one-step lag of [S] §2).  0 if dims/k are invalid. */
 size_t scape_mask_bytes(const scape_dims* dims, int64_t k);
@@ -180,8 +187,10 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
  *   (see scape_mask_view) to bound its candidate capture, and writes the
  *   record of slot t&1.
  *   1. a^i = grads[i] + e[i]; error-feedback compression at M_t; e updated
- *      in place.  The K workers' sparse buffers are summed in registers;
- *      only the owner's is kept (in the workspace), for the exact recount.
+ *      in place; every worker's sparse buffer is written to the workspace.
+ *      The step runs as K passes over the flat buffer: for every partition,
+ *      one pass per non-owner worker, then the owner's pass (steps 2 and 3),
+ *      which reads the other workers' sparse buffers back.
  *   2. statistic per partition p with owner o: s = b1*m + (1-b1)*a^o, using
  *      m before this step's update; M_{t+1} = per-partition top-k of |s|.
  *   3. b_bar = worker mean of the sparse buffers; AdamS at M_t.

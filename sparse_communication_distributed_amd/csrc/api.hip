@@ -294,6 +294,12 @@ extern "C" {
 
 int64_t scape_tile_elems(void) { return kTile; }
 
+int32_t scape_step_pass_count(const scape_dims* dims, int64_t k) {
+  Geom g;
+  if (!dims || !make_geom(dims->n, dims->num_partitions, dims->num_workers, k, &g)) return -1;
+  return multi_pass_pays(g) ? g.K : 1;
+}
+
 size_t scape_mask_bytes(const scape_dims* dims, int64_t k) {
   Geom g;
   if (!dims || !make_geom(dims->n, dims->num_partitions, dims->num_workers, k, &g)) return 0;
@@ -524,7 +530,7 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   if (st) return st;
   const bool vec = c.vec && aligned16(params) && aligned16(v);
   const bool seg = vec && seg_ok(c.g, params, m, v);
-  if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
+  if ((st = hip_check(launch_step_passes(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
   return step_end(c, stream);
 }
 
@@ -555,7 +561,7 @@ scape_status scape_step_graph(const scape_dims* dims, float* params, const float
   if (st) return st;
   const bool vec = c.vec && aligned16(params) && aligned16(v);
   const bool seg = vec && seg_ok(c.g, params, m, v);
-  if ((st = hip_check(launch_step_pass(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
+  if ((st = hip_check(launch_step_passes(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
   return step_end(c, stream);
 }
 

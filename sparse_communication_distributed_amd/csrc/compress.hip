@@ -161,17 +161,45 @@ constexpr int kChunkGroup = 2;
 // 128, which the chunk group of 2 fits without spilling).
 constexpr int kStepMinWaves = 4;
 
+// Which workers a block walks (MODE):
+//  kModeAll     every worker: the component compression (STEP false) and
+//               the single-pass fused step (STEP true).
+//  kModeWorker  STEP false, one worker per partition, (owner + 1 + rot) % K:
+//               one of the K - 1 non-owner passes of the multi-pass step.
+//               It compresses that worker's row and writes its sparse buffer.
+//  kModeOwner   STEP true, the owner alone: the last pass of the multi-pass
+//               step.  The worker sum at a masked element is formed here, in
+//               worker order, from the other workers' sparse buffers and the
+//               owner's own value.
+// A pass over one worker streams three rows (g, e read; e written) where
+// the single pass streams 3K + 1 at once; HBM serves the narrower mix
+// faster.
+// Minimum waves per SIMD the owner and worker passes are compiled for, and
+// their chunk groups.
+constexpr int kOwnerMinWaves = 8;
+constexpr int kOwnerChunkGroup = 1;
+constexpr int kWorkerMinWaves = 4;
+constexpr int kWorkerChunkGroup = 2;
+constexpr int kModeAll = 0;
+constexpr int kModeWorker = 1;
+constexpr int kModeOwner = 2;
+
 // VOUT: v_t is stored at the masked elements (v non-null).  AdamS never
 // reads v back, so a caller may leave it out.
-template <bool STEP, bool VEC, bool SEG, bool VOUT>
-__global__ void __launch_bounds__(kThreads, kStepMinWaves)
+template <bool STEP, bool VEC, bool SEG, bool VOUT, int MODE>
+__global__ void __launch_bounds__(kThreads, MODE == kModeOwner    ? kOwnerMinWaves
+                                           : MODE == kModeWorker ? kWorkerMinWaves
+                                                                 : kStepMinWaves)
 compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
                 float* __restrict__ b, float* __restrict__ m, float* __restrict__ v,
                 float* __restrict__ w, float* __restrict__ mold, AdamsC ac,
                 const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
                 uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int p0, int64_t e_stride,
-                const float* __restrict__ ibc_dev) {
+                const float* __restrict__ ibc_dev, int rot) {
+  static_assert(MODE == kModeAll || (MODE == kModeWorker && !STEP) || (MODE == kModeOwner && STEP),
+                "worker passes compress only; the owner pass is a step pass");
+  constexpr int CG = (MODE == kModeOwner) ? kOwnerChunkGroup : (MODE == kModeWorker) ? kWorkerChunkGroup : kChunkGroup;
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[STEP ? kBins : 1];
@@ -189,6 +217,9 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
   const int64_t wbase = (int64_t)p * g.wpp;
   const int64_t pk = (int64_t)g.P * g.k;
   const int owner = (int)(((int64_t)p * g.K) / g.P);
+  // the one worker of a worker or owner pass
+  const int wsel = (MODE == kModeWorker) ? (owner + 1 + rot) % g.K : owner;
+  const int nwork = (MODE == kModeAll) ? g.K : 1;
   const uint32_t lo = STEP ? lo_in[p] : 0u;
   const int lane16 = threadIdx.x & 15;
   const int sh4 = 4 * lane16;
@@ -211,10 +242,10 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
     uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
     const float* mt = m + pbase + tb;
 
-    for (int cg = 0; cg < 4; cg += kChunkGroup) {
-      uint32_t nib[kChunkGroup], rr0[kChunkGroup], o[kChunkGroup];
+    for (int cg = 0; cg < 4; cg += CG) {
+      uint32_t nib[CG], rr0[CG], o[CG];
 #pragma unroll
-      for (int u = 0; u < kChunkGroup; ++u) {
+      for (int u = 0; u < CG; ++u) {
         const int c = cg + u;
         const int q = c * 16 + (threadIdx.x >> 4);
         const uint64_t word = sw[q];
@@ -222,20 +253,41 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         rr0[u] = spre[q] + (uint32_t)__popcll(word & below);
         o[u] = c * 1024 + 4 * threadIdx.x;
       }
-      float ma[kChunkGroup][4], S[kChunkGroup][4];
+      float ma[CG][4], S[CG][4];
       (void)S;
       if (STEP) {
 #pragma unroll
-        for (int u = 0; u < kChunkGroup; ++u)
+        for (int u = 0; u < CG; ++u)
           if (o[u] < tn) load4(mt, o[u], tn, VEC, ma[u]);
       }
-      for (int i = 0; i < g.K; ++i) {
+      // The owner pass streams too few rows to hide the latency of the w
+      // gather behind them, so it loads w at the group's masked elements
+      // (their segments, with SEG) here, together with m.
+      float wpre[CG][4];
+      (void)wpre;
+      if (MODE == kModeOwner) {
+        const float* wt0 = w + pbase + tb;
+#pragma unroll
+        for (int u = 0; u < CG; ++u) {
+          if (SEG) {
+            const uint32_t lane = threadIdx.x & 63u;
+            const uint64_t act = __ballot(nib[u] != 0u);
+            if (((act >> (lane & ~3u)) & 0xfull) && o[u] < tn) load4t(wt0, o[u], wpre[u]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (((nib[u] >> q) & 1u) && o[u] + q < tn) wpre[u][q] = wt0[o[u] + q];
+          }
+        }
+      }
+      for (int ii = 0; ii < nwork; ++ii) {
+        const int i = (MODE == kModeAll) ? ii : wsel;
         const float* gt = grads + (int64_t)i * g.n + pbase + tb;
         float* et = e + (int64_t)i * e_stride + ebase + tb;
         float* bt = b + (int64_t)i * pk + rbase;
-        float ga[kChunkGroup][4], ea[kChunkGroup][4];
+        float ga[CG][4], ea[CG][4];
 #pragma unroll
-        for (int u = 0; u < kChunkGroup; ++u) {
+        for (int u = 0; u < CG; ++u) {
           if (o[u] < tn) {
             load4(gt, o[u], tn, VEC, ga[u]);
             load4(et, o[u], tn, VEC, ea[u]);
@@ -243,7 +295,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         }
         const bool own = STEP && (i == owner);  // block-uniform
 #pragma unroll
-        for (int u = 0; u < kChunkGroup; ++u) {
+        for (int u = 0; u < CG; ++u) {
           float a[4];
           if (o[u] < tn) {
             float eo[4];
@@ -260,7 +312,8 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 if ((nib[u] >> q) & 1u) {
                   if ((!STEP || own) && (int64_t)rr < rlim) bt[rr] = a[q];
                   ++rr;
-                  if (STEP) S[u][q] = (i == 0) ? a[q] : S[u][q] + a[q];
+                  // the worker sum so far (the owner pass: the owner's value)
+                  if (STEP) S[u][q] = (MODE == kModeOwner || i == 0) ? a[q] : S[u][q] + a[q];
                 }
             }
           }
@@ -284,7 +337,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
         float* vt = VOUT ? v + pbase + tb : nullptr;  // v may be null without VOUT
         float* ot = mold + rbase;
 #pragma unroll
-        for (int u = 0; u < kChunkGroup; ++u) {
+        for (int u = 0; u < CG; ++u) {
           float wo[4], vo[4], mn4[4], wn4[4];
           if (SEG) {
             // w, m (and v) are written as whole 64-byte segments (4 lanes x
@@ -295,7 +348,12 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             const uint32_t lane = threadIdx.x & 63u;
             const uint64_t act = __ballot(nib[u] != 0u);
             if (!((act >> (lane & ~3u)) & 0xfull) || o[u] >= tn) continue;
-            load4t(wt, o[u], wo);
+            if (MODE == kModeOwner) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) wo[q] = wpre[u][q];
+            } else {
+              load4t(wt, o[u], wo);
+            }
             if (VOUT) load4t(vt, o[u], vo);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -306,13 +364,21 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             if (!nib[u]) continue;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              if (((nib[u] >> q) & 1u) && o[u] + q < tn) wo[q] = wt[o[u] + q];
+              if (((nib[u] >> q) & 1u) && o[u] + q < tn) wo[q] = (MODE == kModeOwner) ? wpre[u][q] : wt[o[u] + q];
           }
           uint32_t rr = rr0[u];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             if (!((nib[u] >> q) & 1u) || o[u] + q >= tn) continue;
-            const float x = S[u][q] * ac.invK;
+            float sum = S[u][q];
+            if (MODE == kModeOwner) {  // ((x^0 + x^1) + ...) + x^{K-1}, x^owner in registers
+              const float* bp = b + rbase + rr;
+              for (int i2 = 0; i2 < g.K; ++i2) {
+                const float xi = (i2 == owner) ? S[u][q] : (((int64_t)rr < rlim) ? bp[(int64_t)i2 * pk] : 0.0f);
+                sum = (i2 == 0) ? xi : sum + xi;
+              }
+            }
+            const float x = sum * ac.invK;
             const float mo = ma[u][q];
             const float mn = (ac.b1 * mo) + (ac.c1 * x);
             const float vn = (ac.b2 * (mo * mo)) + (ac.c2 * (x * x));
@@ -480,41 +546,76 @@ hipError_t launch_stat(const Geom& g, int src, int phase, const StatArgs& a, boo
   return hipGetLastError();
 }
 
-hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
-                           const uint32_t* tile_off, float* b, hipStream_t s, bool vec) {
+template <int MODE>
+void launch_compress_t(const Geom& g, const float* grads, float* e, const uint64_t* bits, const uint32_t* tile_off,
+                       float* b, bool vec, int rot, hipStream_t s) {
   const dim3 grid = stream_grid(g.P, g.G);
   AdamsC ac{};
   if (vec)
-    compress_kernel<false, true, false, false><<<grid, kThreads, 0, s>>>(
+    compress_kernel<false, true, false, false, MODE><<<grid, kThreads, 0, s>>>(
         g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
-        0, g.n, nullptr);
+        0, g.n, nullptr, rot);
   else
-    compress_kernel<false, false, false, false><<<grid, kThreads, 0, s>>>(
+    compress_kernel<false, false, false, false, MODE><<<grid, kThreads, 0, s>>>(
         g, grads, e, bits, tile_off, b, nullptr, nullptr, nullptr, nullptr, ac, nullptr, nullptr, nullptr, nullptr,
-        0, g.n, nullptr);
+        0, g.n, nullptr, rot);
+}
+
+hipError_t launch_compress(const Geom& g, const float* grads, float* e, const uint64_t* bits,
+                           const uint32_t* tile_off, float* b, hipStream_t s, bool vec) {
+  launch_compress_t<kModeAll>(g, grads, e, bits, tile_off, b, vec, 0, s);
   return hipGetLastError();
 }
 
-template <bool VEC, bool SEG, bool VOUT>
+template <bool VEC, bool SEG, bool VOUT, int MODE>
 void launch_step_t(const Geom& g, const StepArgs& a, const AdamsC& ac, hipStream_t s) {
-  compress_kernel<true, VEC, SEG, VOUT><<<stream_grid(a.nparts, g.G), kThreads, 0, s>>>(
+  compress_kernel<true, VEC, SEG, VOUT, MODE><<<stream_grid(a.nparts, g.G), kThreads, 0, s>>>(
       g, a.grads, a.e, a.bits, a.tile_off, a.b, a.m, a.v, a.w, a.mold, ac, a.lo, a.cand, a.cnt1, a.hist, a.p0,
-      a.e_stride, a.ibc_dev);
+      a.e_stride, a.ibc_dev, 0);
 }
 
-hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
+template <int MODE>
+void launch_step_mode(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
   AdamsC ac{a.b1, a.b2, a.c1, a.c2, a.ibc1, a.ibc2, a.eps, a.wd, a.lr, (float)(1.0 / (double)g.K)};
   const bool vout = a.v != nullptr;
   if (vec && seg) {
-    if (vout) launch_step_t<true, true, true>(g, a, ac, s);
-    else launch_step_t<true, true, false>(g, a, ac, s);
+    if (vout) launch_step_t<true, true, true, MODE>(g, a, ac, s);
+    else launch_step_t<true, true, false, MODE>(g, a, ac, s);
   } else if (vec) {
-    if (vout) launch_step_t<true, false, true>(g, a, ac, s);
-    else launch_step_t<true, false, false>(g, a, ac, s);
+    if (vout) launch_step_t<true, false, true, MODE>(g, a, ac, s);
+    else launch_step_t<true, false, false, MODE>(g, a, ac, s);
   } else {
-    if (vout) launch_step_t<false, false, true>(g, a, ac, s);
-    else launch_step_t<false, false, false>(g, a, ac, s);
+    if (vout) launch_step_t<false, false, true, MODE>(g, a, ac, s);
+    else launch_step_t<false, false, false, MODE>(g, a, ac, s);
   }
+}
+
+hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
+  launch_step_mode<kModeAll>(g, a, vec, seg, s);
+  return hipGetLastError();
+}
+
+bool multi_pass_pays(const Geom& g) {
+  // Measured on Llama-shaped workloads: at K = 8 and 1% density the K
+  // passes ran 5-7% faster than the single pass, at K = 4 they tied, and
+  // at K = 8 and 10% density (the sparse buffers' round trip, 8(K-1)Pk
+  // bytes, at 5.6% of the streams) they ran 10% slower.
+  const double trip = 8.0 * (g.K - 1) * (double)g.P * (double)g.k;
+  const double streams = (12.0 * g.K + 4.0) * (double)g.n;
+  return g.K >= 8 && trip <= 0.02 * streams;
+}
+
+hipError_t launch_step_passes(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
+  if (!multi_pass_pays(g)) return launch_step_pass(g, a, vec, seg, s);
+  // K - 1 non-owner passes (pass j: worker (owner + 1 + j) % K of every
+  // partition), then the owner pass; stream order makes every sparse buffer
+  // complete before the owner pass reads it
+  for (int j = 0; j + 1 < g.K; ++j) {
+    launch_compress_t<kModeWorker>(g, a.grads, a.e, a.bits, a.tile_off, a.b, vec, j, s);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  launch_step_mode<kModeOwner>(g, a, vec, seg, s);
   return hipGetLastError();
 }
 

@@ -155,6 +155,14 @@ hipError_t launch_compress(const Geom& g, const float* grads, float* e, const ui
 // worker-sum reduction and AdamS at M_t.
 // seg: w, m, v rows 64-byte aligned and n_p % 16 == 0 (whole-segment AdamS writes)
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
+// The step over the resident buffers (all partitions, p0 = 0), as the
+// single pass above or, where multi_pass_pays(g), as K passes: K - 1 passes
+// each compress one non-owner worker per partition into its sparse buffer,
+// then the owner pass (statistic, capture, worker sum from the sparse
+// buffers in worker order, AdamS).  Both forms give the same results, bit
+// for bit.
+bool multi_pass_pays(const Geom& g);
+hipError_t launch_step_passes(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
 
 hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
 // target 0: the capture target of a step (kCaptureMargin * k)

@@ -76,15 +76,42 @@ def short_name(full: str) -> str:
     return base + (targs if len(targs) <= 48 else "<…>")
 
 
-def is_step_pass(name: str) -> bool:
-    """The fused step pass that stores no v: compress_kernel<STEP = true,
-    VEC, SEG, VOUT = false> (the component compression has STEP = false,
-    the v-storing step VOUT = true)."""
+def step_pass_role(name: str):
+    """Role of a launch in the step pass, from its template arguments
+    compress_kernel<STEP, VEC, SEG, VOUT, MODE>: "worker" for a non-owner
+    worker pass (STEP false, MODE 1), "owner" for the owner pass (MODE 2) or
+    the single step pass (MODE 0) that stores no v (STEP true, VOUT false),
+    "owner_v" for those that store v; None for anything else (the component
+    compression has STEP false, MODE 0)."""
     n = short_name(name)
     if not n.startswith(STEP_KERNEL + "<"):
-        return False
+        return None
     args = [x.strip() for x in n[len(STEP_KERNEL) + 1:-1].split(",")]
-    return len(args) == 4 and args[0] == "true" and args[3] == "false"
+    if len(args) != 5:
+        return None
+    if args[0] == "false" and args[4] == "1":
+        return "worker"
+    if args[0] == "true" and args[4] in ("0", "2"):  # the single pass, or the owner pass
+        return "owner" if args[3] == "false" else "owner_v"
+    return None
+
+
+def step_pass_ms(run):
+    """One process's step pass time from its kernel statistics: the owner
+    pass's average plus (K - 1) worker-pass averages, K - 1 being the
+    worker launches per owner launch (v-storing owner launches count too:
+    their steps run the same worker passes)."""
+    by = {}
+    for r in run:
+        role = step_pass_role(r["Name"])
+        if role:
+            by[role] = (float(r["AverageNs"]) / 1e6, int(r["Calls"]))
+    if "owner" not in by:
+        return None
+    owners = by["owner"][1] + by.get("owner_v", (0.0, 0))[1]
+    wav, wcalls = by.get("worker", (0.0, 0))
+    per = wcalls / owners
+    return by["owner"][0], wav, per, by["owner"][0] + per * wav
 
 
 def read_counter(path, counter):
@@ -118,15 +145,14 @@ def main():
     for r in rows:
         lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
-    step_ms = []
-    for run in runs:
-        for r in run:
-            if is_step_pass(r["Name"]):
-                step_ms.append((float(r["AverageNs"]) / 1e6, float(r["MinNs"]) / 1e6, float(r["MaxNs"]) / 1e6))
-    if len(runs) > 1:
-        lines += ["", f"## {STEP_KERNEL} (step pass, no v stored) in each profiled process", "",
-                  "| process | avg ms | min ms | max ms |", "|---|---|---|---|"]
-        lines += [f"| {i + 1} | {av:.3f} | {mn:.3f} | {mx:.3f} |" for i, (av, mn, mx) in enumerate(step_ms)]
+    step_ms = [step_pass_ms(run) for run in runs]
+    multi = any(per > 0 for _, _, per, _ in step_ms)
+    form = "worker passes, then the owner pass" if multi else "one pass"
+    lines += ["", f"## Step pass ({STEP_KERNEL}, {form}; no v stored) in each profiled process", "",
+              "| process | owner pass avg ms | worker pass avg ms | worker passes per step | step pass ms |",
+              "|---|---|---|---|---|"]
+    lines += [f"| {i + 1} | {ow:.3f} | {wk:.3f} | {per:.2f} | {tot:.3f} |"
+              for i, (ow, wk, per, tot) in enumerate(step_ms)]
     if not (a.fetch and a.write):  # kernel trace only: no counters file
         with open(a.out + ".md", "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -138,13 +164,18 @@ def main():
     lines += ["", "## HBM bytes (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"Calibration copy of 1 GiB: FETCH_SIZE scale {f_scale:.3f}, WRITE_SIZE scale {w_scale:.3f}.", "",
               "| kernel | launches | read GB / launch (scaled) | write GB / launch (scaled) |", "|---|---|---|---|"]
-    out = {}
-    step_name = None
+    out, names = {}, {}
+    roles = {k: step_pass_role(k) for k in set(fetch) | set(write)}
+    owners = sum(len(fetch.get(k, [])) for k, r in roles.items() if r in ("owner", "owner_v"))
+    workers = sum(len(fetch.get(k, [])) for k, r in roles.items() if r == "worker")
+    per = workers / owners if owners else 0.0  # worker passes per step
     for k in sorted(set(fetch) | set(write)):
         fv, wv = fetch.get(k, []), write.get(k, [])
-        if is_step_pass(k):
-            step_name = k
-            fv, wv = fv[a.step_launches_skip:], wv[a.step_launches_skip:]
+        role = roles[k]
+        if role in ("owner", "worker"):  # the first step's launches dropped
+            skip = a.step_launches_skip * (1 if role == "owner" else round(per))
+            fv, wv = fv[skip:], wv[skip:]
+            names[role] = k
         if not fv or not wv:
             continue
         rd = sum(fv) / len(fv) * 1024 * f_scale / 1e9
@@ -152,13 +183,19 @@ def main():
         out[k] = (rd, wr)
         if rd + wr > 0.05:
             lines.append(f"| {k} | {len(fv)} | {rd:.3f} | {wr:.3f} |")
+    rd, wr = out[names["owner"]]
+    if "worker" in names:
+        rd += per * out[names["worker"]][0]
+        wr += per * out[names["worker"]][1]
+    what = f"owner pass + {per:.2f} worker passes" if per > 0 else "one pass"
+    lines += ["", f"Step pass ({what}): {rd:.3f} GB read, {wr:.3f} GB written."]
     with open(a.out + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
-    rd, wr = out[step_name]
-    doc = {"workload": a.workload, "kernel": step_name, "source_hash": step_pass_source_hash(),
-           "hbm_read_bytes_per_launch": rd * 1e9, "hbm_write_bytes_per_launch": wr * 1e9,
-           "hbm_bytes_per_launch": (rd + wr) * 1e9, "fetch_scale": f_scale, "write_scale": w_scale,
-           "step_pass_avg_ms_per_process": [av for av, _, _ in step_ms]}
+    doc = {"workload": a.workload, "kernels": names, "worker_passes_per_step": per,
+           "source_hash": step_pass_source_hash(),
+           "hbm_read_bytes_per_step_pass": rd * 1e9, "hbm_write_bytes_per_step_pass": wr * 1e9,
+           "hbm_bytes_per_step_pass": (rd + wr) * 1e9, "fetch_scale": f_scale, "write_scale": w_scale,
+           "step_pass_ms_per_process": [tot for _, _, _, tot in step_ms]}
     with open(a.out + "_counters.json", "w") as f:
         json.dump(doc, f, indent=1)
     print(json.dumps(doc, indent=1))

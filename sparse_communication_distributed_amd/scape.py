@@ -48,6 +48,7 @@ class ScapeError(RuntimeError):
 # name -> (restype, argtypes); mirrors include/scape.h
 _SIGS = {
     "scape_tile_elems": (c_int64, []),
+    "scape_step_pass_count": (ctypes.c_int32, [ctypes.POINTER(Dims), c_int64]),
     "scape_mask_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64]),
     "scape_mask_slot": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, c_int, ctypes.POINTER(MaskView)]),
     "scape_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64]),
@@ -161,6 +162,11 @@ def _stream(stream) -> int:
 
 def tile_elems() -> int:
     return int(lib().scape_tile_elems())
+
+
+def step_pass_count(d: Dims, k: int) -> int:
+    """1 or K: the passes over the flat buffer a step makes (-1: invalid)."""
+    return int(lib().scape_step_pass_count(ctypes.byref(d), k))
 
 
 def mask_bytes(d: Dims, k: int) -> int:

@@ -59,6 +59,18 @@ def test_layout_sizes():
     assert L.scape_mask_slot(ctypes.byref(d), k, FAKE, 2, ctypes.byref(mv0)) == 1
 
 
+def test_step_pass_count():
+    """K passes only where they measured faster: K >= 8 with the sparse
+    buffers' round trip at most 2% of the streams (Llama-500M at 99%), one
+    pass elsewhere (Llama-1.8B at K = 4, GPT-345M at 10% density)."""
+    assert S.step_pass_count(S.dims(557_774_080, 32, 8), 174_304) == 8
+    assert S.step_pass_count(S.dims(1_775_372_288, 32, 4), 554_803) == 1
+    assert S.step_pass_count(S.dims(354_823_168, 32, 8), 1_108_822) == 1
+    assert S.step_pass_count(S.dims(1 << 20, 4, 8), 2621) == 8   # 1% density, K = 8
+    assert S.step_pass_count(S.dims(1 << 20, 4, 8), 26214) == 1  # 10% density
+    assert S.step_pass_count(S.dims(100, 3, 1), 1) == -1
+
+
 @pytest.mark.parametrize("n,P,K,k", [(100, 3, 1, 1), (100, 4, 0, 1), (100, 0, 1, 1), (100, 4, 1, 0),
                                      (100, 4, 1, 26), (1 << 32, 1, 1, 1), (0, 1, 1, 1)])
 def test_invalid_shapes(n, P, K, k):

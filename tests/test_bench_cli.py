@@ -30,6 +30,12 @@ def test_algorithmic_bytes_formula():
     for v_out in (False, True):
         assert bench.alg_bytes_step_pass(n, P, K, k, v_out) < bench.alg_bytes_step(n, P, K, k, v_out)
     assert bench.alg_bytes_step_pass(n, P, K, k, True) - bench.alg_bytes_step_pass(n, P, K, k) == 4 * P * k
+    # as K passes: every pass reads the mask words, and the K - 1 non-owner
+    # sparse buffers are written and read back
+    for v_out in (False, True):
+        multi = bench.alg_bytes_step_pass(n, P, K, k, v_out, passes=K)
+        assert multi - bench.alg_bytes_step_pass(n, P, K, k, v_out) == (K - 1) * n / 8 + 8 * (K - 1) * P * k
+        assert multi < bench.alg_bytes_step(n, P, K, k, v_out)
 
 
 def _write_csv(path, header, rows):
@@ -39,45 +45,56 @@ def _write_csv(path, header, rows):
         w.writerows(rows)
 
 
-STEP = ("void scape::(anonymous namespace)::compress_kernel<true, true, true, false>(scape::Geom, float const*, "
-        "float*, unsigned long const*, unsigned int const*, float*, float*, float*, float*, float*, "
-        "scape::(anonymous namespace)::AdamsC, unsigned int const*, unsigned long*, unsigned int*, unsigned int*, "
-        "int, long, float const*)")
-STEP_V = STEP.replace("<true, true, true, false>", "<true, true, true, true>")
-COMP = STEP.replace("<true, true, true, false>", "<false, true, false, false>")
+OWNER = ("void scape::(anonymous namespace)::compress_kernel<true, true, true, false, 2>(scape::Geom, float const*, "
+         "float*, unsigned long const*, unsigned int const*, float*, float*, float*, float*, float*, "
+         "scape::(anonymous namespace)::AdamsC, unsigned int const*, unsigned long*, unsigned int*, unsigned int*, "
+         "int, long, float const*, int)")
+OWNER_V = OWNER.replace("<true, true, true, false, 2>", "<true, true, true, true, 2>")
+WORKER = OWNER.replace("<true, true, true, false, 2>", "<false, true, false, false, 1>")
+COMP = OWNER.replace("<true, true, true, false, 2>", "<false, true, false, false, 0>")
+HDR_S = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
 
 
-def test_prof_summary_short_names():
-    from sparse_communication_distributed_amd.prof_summary import is_step_pass, short_name
-    assert short_name(STEP) == "compress_kernel<true, true, true, false>"
+def test_prof_summary_short_names_and_roles():
+    from sparse_communication_distributed_amd.prof_summary import short_name, step_pass_role
+    assert short_name(OWNER) == "compress_kernel<true, true, true, false, 2>"
     assert short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
     assert short_name("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, "
                       "std::array<char*, 1ul> >(int, at::native::FillFunctor<float>, std::array<char*, 1ul>)") \
         == "vectorized_elementwise_kernel<…>"
     assert short_name("void scape::(anonymous namespace)::zero_u32_kernel(unsigned int*, long)") == "zero_u32_kernel"
-    assert is_step_pass(STEP) and not is_step_pass(STEP_V) and not is_step_pass(COMP)
+    assert [step_pass_role(x) for x in (OWNER, OWNER_V, WORKER, COMP)] == ["owner", "owner_v", "worker", None]
 
 
-def test_prof_summary_scales_counters_by_the_copy(tmp_path):
-    hdr_s = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
+def test_prof_summary_step_pass_of_k_launches(tmp_path):
+    """K = 4: three worker passes and one owner pass per step.  The step
+    pass time and traffic are the owner pass's plus three worker passes'."""
     stats = tmp_path / "stats.csv"
-    _write_csv(stats, hdr_s, [[STEP, 3, 60e6, 20e6, 80.0, 19e6, 21e6, 1.0],
-                              [STEP_V, 2, 50e6, 25e6, 10.0, 24e6, 26e6, 1.0],
-                              [COMP, 1, 5e6, 5e6, 10.0, 5e6, 5e6, 0.0]])
+    # 3 v-less steps and 2 v-storing steps: 15 worker launches
+    _write_csv(stats, HDR_S, [[OWNER, 3, 30e6, 10e6, 50.0, 9e6, 11e6, 1.0],
+                              [WORKER, 15, 60e6, 4e6, 40.0, 3.9e6, 4.1e6, 1.0],
+                              [OWNER_V, 2, 22e6, 11e6, 5.0, 11e6, 11e6, 0.0],
+                              [COMP, 1, 5e6, 5e6, 5.0, 5e6, 5e6, 0.0]])
+    stats2 = tmp_path / "stats2.csv"  # a second profiled process, slower placement
+    _write_csv(stats2, HDR_S, [[WORKER, 15, 75e6, 5e6, 40.0, 4.9e6, 5.1e6, 1.0],
+                               [OWNER, 3, 36e6, 12e6, 50.0, 11e6, 13e6, 1.0],
+                               [OWNER_V, 2, 26e6, 13e6, 10.0, 13e6, 13e6, 0.0]])
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     fetch = tmp_path / "fetch.csv"
     write = tmp_path / "write.csv"
-    # the calibration copy reads 1 GiB but its FETCH_SIZE counter shows half of it;
-    # the v-storing and component launches are not the step pass
-    _write_csv(fetch, hdr, [["__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288],
-                            [STEP, "FETCH_SIZE", 999], [STEP_V, "FETCH_SIZE", 5000], [STEP, "FETCH_SIZE", 1000],
-                            [COMP, "FETCH_SIZE", 7000], [STEP, "FETCH_SIZE", 1000]])
-    _write_csv(write, hdr, [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576],
-                            [STEP, "WRITE_SIZE", 7], [STEP, "WRITE_SIZE", 500], [STEP_V, "WRITE_SIZE", 9000],
-                            [STEP, "WRITE_SIZE", 500]])
-    stats2 = tmp_path / "stats2.csv"  # a second profiled process, slower placement
-    _write_csv(stats2, hdr_s, [[STEP_V, 2, 50e6, 25e6, 10.0, 24e6, 26e6, 1.0],
-                               [STEP, 3, 66e6, 22e6, 90.0, 21e6, 23e6, 1.0]])
+    # two steps: the first step's launches (1 owner, 3 workers) are dropped;
+    # the calibration copy reads 1 GiB but its FETCH_SIZE counter shows half of it
+    f_rows = [["__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288]]
+    w_rows = [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576]]
+    for step in range(2):
+        for _ in range(3):
+            f_rows.append([WORKER, "FETCH_SIZE", 9 if step == 0 else 300])
+            w_rows.append([WORKER, "WRITE_SIZE", 9 if step == 0 else 100])
+        f_rows.append([OWNER, "FETCH_SIZE", 9 if step == 0 else 1000])
+        w_rows.append([OWNER, "WRITE_SIZE", 9 if step == 0 else 500])
+    f_rows.append([COMP, "FETCH_SIZE", 7000])
+    _write_csv(fetch, hdr, f_rows)
+    _write_csv(write, hdr, w_rows)
     out = tmp_path / "prof"
     r = subprocess.run([sys.executable, "-m", "sparse_communication_distributed_amd.prof_summary", "--stats", str(stats),
                         "--stats", str(stats2),
@@ -85,16 +102,19 @@ def test_prof_summary_scales_counters_by_the_copy(tmp_path):
                        cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     doc = json.load(open(str(out) + "_counters.json"))
-    assert doc["kernel"] == "compress_kernel<true, true, true, false>"
+    assert doc["kernels"] == {"owner": "compress_kernel<true, true, true, false, 2>",
+                              "worker": "compress_kernel<false, true, false, false, 1>"}
+    assert doc["worker_passes_per_step"] == pytest.approx(3.0)
     assert doc["fetch_scale"] == pytest.approx(2.0)
     assert doc["write_scale"] == pytest.approx(1.0)
-    # first launch skipped; KiB -> bytes, scaled
-    assert doc["hbm_read_bytes_per_launch"] == pytest.approx(1000 * 1024 * 2.0)
-    assert doc["hbm_write_bytes_per_launch"] == pytest.approx(500 * 1024)
-    assert doc["step_pass_avg_ms_per_process"] == pytest.approx([20.0, 22.0])
+    # KiB -> bytes, scaled: owner + 3 workers
+    assert doc["hbm_read_bytes_per_step_pass"] == pytest.approx((1000 + 3 * 300) * 1024 * 2.0)
+    assert doc["hbm_write_bytes_per_step_pass"] == pytest.approx((500 + 3 * 100) * 1024)
+    # per process: owner average + 15 / 5 worker averages
+    assert doc["step_pass_ms_per_process"] == pytest.approx([10.0 + 3 * 4.0, 12.0 + 3 * 5.0])
     md = open(str(out) + ".md").read()
-    assert "compress_kernel (step pass, no v stored) in each profiled process" in md and "| 2 | 22.000 |" in md
-    assert "| compress_kernel<true, true, true, true> | 2 |" in md
+    assert "| 2 | 12.000 | 5.000 | 3.00 | 27.000 |" in md and "worker passes, then the owner pass" in md
+    assert "| compress_kernel<true, true, true, true, 2> | 2 |" in md
 
 
 def test_step_pass_hash_ignores_comments_only():

@@ -34,7 +34,9 @@ def test_bench_json_line_tiny():
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-9)
-    assert rf["achieved"] == pytest.approx(rf["bytes_alg_per_launch"] / (rf["ms_per_launch"] * 1e-3) / 1e9, rel=1e-9)
+    assert rf["achieved"] == pytest.approx(rf["bytes_alg_per_step_pass"] / (rf["ms_per_step_pass"] * 1e-3) / 1e9,
+                                           rel=1e-9)
+    assert rf["launches_per_step_pass"] in (1, d["config"]["workers"])
     assert len(d["profiled_step_ms"]) == 3 and all(x > 0 for x in d["profiled_step_ms"])
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]

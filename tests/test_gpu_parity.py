@@ -351,6 +351,21 @@ def test_step_small_shapes(S, n_p, P, K, sp, law):
     run_lockstep(S, cfg, cfg.steps)
 
 
+@pytest.mark.parametrize("n_p,P,K,sp,law,offset,store_v", [
+    (3 * 4096 + 100, 4, 8, "0.99", "tensor_sigma", 0, True),     # ragged tail, element-wise AdamS stores
+    (4096 * 4, 32, 8, "0.99", "tensor_sigma", 0, False),        # whole-segment AdamS stores, no v
+    (4096 * 4, 32, 8, "0.99", "tensor_sigma", 1, True),         # w, m, v off their 16-byte alignment
+    (10_007, 3, 9, "0.999", "stress_t3", 0, True),              # scalar path, K > P, exact ties
+    (2 * 4096, 5, 12, "0.995", "partition_scale", 0, False),    # 12 workers, P % K != 0
+])
+def test_step_multi_pass(S, n_p, P, K, sp, law, offset, store_v):
+    """Shapes the step runs as K passes (one per non-owner worker, then the
+    owner's): masks and state bitwise equal to the oracle's at every step."""
+    cfg = W.flat_config("multipass", P * n_p, P, K, sp, steps=4, grad_law=law, weight_decay=0.01)
+    assert S.step_pass_count(S.dims(cfg.n, P, K), cfg.k) == K
+    run_lockstep(S, cfg, cfg.steps, offset=offset, store_v=store_v)
+
+
 def _extreme_grads(cfg, t):
     """The workload's gradients with planted extremes: partition 1 wholly
     subnormal or nearly so (its selected entries run AdamS on subnormals),

@@ -372,10 +372,20 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             if (!((nib[u] >> q) & 1u) || o[u] + q >= tn) continue;
             float sum = S[u][q];
             if (MODE == kModeOwner) {  // ((x^0 + x^1) + ...) + x^{K-1}, x^owner in registers
+              // the other workers' values are loaded 8 at a time before
+              // they are added, so their loads overlap
               const float* bp = b + rbase + rr;
-              for (int i2 = 0; i2 < g.K; ++i2) {
-                const float xi = (i2 == owner) ? S[u][q] : (((int64_t)rr < rlim) ? bp[(int64_t)i2 * pk] : 0.0f);
-                sum = (i2 == 0) ? xi : sum + xi;
+              const bool inb = (int64_t)rr < rlim;
+              for (int i0 = 0; i0 < g.K; i0 += 8) {
+                float xs[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                  const int i2 = i0 + j;
+                  xs[j] = (i2 == owner) ? S[u][q] : ((i2 < g.K && inb) ? bp[(int64_t)i2 * pk] : 0.0f);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                  if (i0 + j < g.K) sum = (i0 + j == 0) ? xs[j] : sum + xs[j];
               }
             }
             const float x = sum * ac.invK;
@@ -596,10 +606,10 @@ hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg
 }
 
 bool multi_pass_pays(const Geom& g) {
-  // Measured on Llama-shaped workloads: at K = 8 and 1% density the K
-  // passes ran 5-7% faster than the single pass, at K = 4 they tied, and
-  // at K = 8 and 10% density (the sparse buffers' round trip, 8(K-1)Pk
-  // bytes, at 5.6% of the streams) they ran 10% slower.
+  // Measured on the model-shaped workloads: at K = 8 and 1% density the K
+  // passes ran 6.5% faster than the single pass on average; at K = 4, and
+  // at K = 8 with 10% density (the sparse buffers' round trip, 8(K-1)Pk
+  // bytes, at 5.6% of the streams), they ran 1-2% slower on average.
   const double trip = 8.0 * (g.K - 1) * (double)g.P * (double)g.k;
   const double streams = (12.0 * g.K + 4.0) * (double)g.n;
   return g.K >= 8 && trip <= 0.02 * streams;

@@ -34,12 +34,14 @@ def bits_of(t):
 @pytest.mark.parametrize("name,n_p,P,K,sp", [
     ("tiny", None, None, None, None),
     ("ragged", 10_007, 3, 3, "0.99"),  # scalar path, odd K
+    ("kpass", 4096 * 4, 32, 8, "0.99"),  # the step as K passes: 8 launches per step in the graph
 ])
 def test_step_graph_replays_match_eager(S, name, n_p, P, K, sp):
     cfg = W.CONFIGS["tiny"] if name == "tiny" else W.flat_config(name, P * n_p, P, K, sp, steps=7,
                                                                   weight_decay=0.01)
     n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
     print(f"[graph] {name} n={n} P={P} K={K} k={k}", flush=True)
+    assert S.step_pass_count(S.dims(n, P, K), k) == (K if name == "kpass" else 1)
     w0 = W.init_params(cfg, 0)
     args = (P, K, k, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
     eager = S.ScapeOptimizer(dev(w0), *args)

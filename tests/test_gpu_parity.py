@@ -366,6 +366,16 @@ def test_step_multi_pass(S, n_p, P, K, sp, law, offset, store_v):
     run_lockstep(S, cfg, cfg.steps, offset=offset, store_v=store_v)
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_step_multi_pass_60_steps(S):
+    """The K-pass form over 60 steps (residuals accumulate, masks drift):
+    masks and state bitwise equal to the oracle's at every step."""
+    cfg = W.flat_config("multipass60", 32 * 4096 * 4, 32, 8, "0.99", steps=60, weight_decay=0.01)
+    assert S.step_pass_count(S.dims(cfg.n, cfg.P, cfg.K), cfg.k) == cfg.K
+    run_lockstep(S, cfg, cfg.steps, rtol_end=1e-6)
+
+
 def _extreme_grads(cfg, t):
     """The workload's gradients with planted extremes: partition 1 wholly
     subnormal or nearly so (its selected entries run AdamS on subnormals),

@@ -7,7 +7,9 @@
 //    and the capture of the selection candidates: owner keys at or above a
 //    per-partition bound `lo` are written, as unique (key, index)
 //    composites, to a per-tile candidate slot, and a level-1 histogram of
-//    the captured keys is kept.
+//    the captured keys is kept.  The step runs it as one pass over all
+//    workers, or as one pass per non-owner worker followed by the owner's
+//    pass (MODE below).
 //  * stat_kernel: the statistic alone, for the step-1 bootstrap (from
 //    m, g^o, e^o), for scape_mask_topk (from a given array), and for the
 //    exact fallback when a partition captured fewer than k candidates (from

@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+CPU_WAIT_S = 600.0  # bound on every wait of the CPU baseline
 METRIC = "optimizer-step params/s + HBM GB/s (% peak), Llama-1.8B shape, 99% sparsity"
 
 
@@ -67,7 +68,7 @@ def _oracle_partition(name, p, seed, barrier, results):
     g = np.stack([W.grads_partition(cfg, 1, i, p, seed) for i in range(cfg.K)])
     st = O.PartitionState.fresh(W.init_params_partition(cfg, p, seed), cfg.K)
     hp = O.Hyper.make(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.lr)
-    barrier.wait()
+    barrier.wait(timeout=CPU_WAIT_S)
     t0 = time.perf_counter()
     O.step_partition(st, g, cfg.k, O.owner(p, cfg.P, cfg.K), hp, 1)
     results.put((p, time.perf_counter() - t0))
@@ -76,9 +77,10 @@ def _oracle_partition(name, p, seed, barrier, results):
 def cpu_baseline(cfg, seed, workers, log_fn):
     """The CPU oracle as it stands, on the host's cores: one process per
     partition (partitions are independent), `workers` partitions stepped at
-    once.  Runs before the GPU is initialised (the processes are forked)."""
+    once.  The processes are fresh interpreters (spawned), since this runs
+    after the GPU measurements, in a process that has initialised the GPU."""
     import multiprocessing as mp
-    ctx = mp.get_context("fork")
+    ctx = mp.get_context("spawn")
     parts = list(range(min(workers, cfg.P)))
     barrier = ctx.Barrier(len(parts) + 1)
     results = ctx.Queue()
@@ -86,10 +88,15 @@ def cpu_baseline(cfg, seed, workers, log_fn):
     for pr in procs:
         pr.start()
     log_fn(f"cpu baseline: {len(parts)} oracle processes generating inputs")
-    barrier.wait()
-    t0 = time.perf_counter()
-    times = [results.get() for _ in parts]
-    wall = time.perf_counter() - t0
+    try:  # a process that dies breaks the barrier or starves the queue: no wait is unbounded
+        barrier.wait(timeout=CPU_WAIT_S)
+        t0 = time.perf_counter()
+        times = [results.get(timeout=CPU_WAIT_S) for _ in parts]
+        wall = time.perf_counter() - t0
+    except Exception as exc:
+        for pr in procs:
+            pr.terminate()
+        raise RuntimeError(f"cpu baseline: an oracle process failed or stalled ({type(exc).__name__})") from exc
     for pr in procs:
         pr.join()
     n = len(parts) * cfg.n_p
@@ -313,11 +320,6 @@ def main():
         print(json.dumps(offload_bench(S, W, cfg, args, log)), flush=True)
         return
     args.overlap = args.overlap or cfg.grad_law == "stress_t3"
-    cpu = None
-    if not args.no_cpu_baseline:
-        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
-        cpu = cpu_baseline(cfg, args.seed, workers, log)
-        cpu["tiny_single_core"] = cpu_tiny_single_core(args.seed, log)
     n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -450,6 +452,17 @@ def main():
     ref = {"kernel": "torch add_: e[i] += g[i] for every worker", "bytes": 12 * K * n, "ms": ref_ms,
            "GBps": 12 * K * n / (ref_ms * 1e-3) / 1e9}
     log(f"reference stream (torch add_ over the e and g rows): {ref_ms:.3f} ms, {ref['GBps']:.0f} GB/s")
+
+    # the oracle on the host's cores, after every GPU measurement: run
+    # before them (forked, ahead of the GPU's initialisation), it left the
+    # Llama-1.8B step pass at 17.64-17.73 ms in six processes of six, where
+    # processes without it, and with it afterwards, ran 15.95-17.70 ms
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(cfg, args.seed, workers, log)
+        cpu["tiny_single_core"] = cpu_tiny_single_core(args.seed, log)
 
     b_step = alg_bytes_step(n, P, K, k, args.store_v)
     passes = S.step_pass_count(d, k)

@@ -101,17 +101,19 @@ def step_pass_ms(run):
     pass's average plus (K - 1) worker-pass averages, K - 1 being the
     worker launches per owner launch (v-storing owner launches count too:
     their steps run the same worker passes)."""
-    by = {}
+    tot = defaultdict(float)  # role -> total ms over its kernel variants
+    calls = defaultdict(int)
     for r in run:
         role = step_pass_role(r["Name"])
         if role:
-            by[role] = (float(r["AverageNs"]) / 1e6, int(r["Calls"]))
-    if "owner" not in by:
+            tot[role] += float(r["AverageNs"]) / 1e6 * int(r["Calls"])
+            calls[role] += int(r["Calls"])
+    if not calls["owner"]:
         return None
-    owners = by["owner"][1] + by.get("owner_v", (0.0, 0))[1]
-    wav, wcalls = by.get("worker", (0.0, 0))
-    per = wcalls / owners
-    return by["owner"][0], wav, per, by["owner"][0] + per * wav
+    owner = tot["owner"] / calls["owner"]
+    wav = tot["worker"] / calls["worker"] if calls["worker"] else 0.0
+    per = calls["worker"] / (calls["owner"] + calls["owner_v"])
+    return owner, wav, per, owner + per * wav
 
 
 def read_counter(path, counter):
@@ -145,7 +147,7 @@ def main():
     for r in rows:
         lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
-    step_ms = [step_pass_ms(run) for run in runs]
+    step_ms = [x for x in (step_pass_ms(run) for run in runs) if x is not None]
     multi = any(per > 0 for _, _, per, _ in step_ms)
     form = "worker passes, then the owner pass" if multi else "one pass"
     lines += ["", f"## Step pass ({STEP_KERNEL}, {form}; no v stored) in each profiled process", "",

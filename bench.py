@@ -296,6 +296,8 @@ def main():
                     help="also time two steps captured in a HIP graph (scape_step_graph) and replayed")
     ap.add_argument("--study", choices=["fillin"], default=None,
                     help="run a study instead of the step benchmark")
+    ap.add_argument("--grads-first", action="store_true",
+                    help="allocate the gradient sets before the optimizer state")
     ap.add_argument("--store-v", action="store_true",
                     help="the timed steps also store v_t at the masked entries (AdamS never reads it back)")
     ap.add_argument("--calib", action="store_true",
@@ -328,21 +330,33 @@ def main():
 
     d = S.dims(n, P, K)
     bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
-    params = torch.empty(n, dtype=torch.float32, device=dev)
-    W.device_init_params(cfg, args.seed, params)
-    m = torch.zeros(n, dtype=torch.float32, device=dev)
-    v = torch.zeros(n, dtype=torch.float32, device=dev) if args.store_v else None
-    e = torch.zeros((K, n), dtype=torch.float32, device=dev)
-    mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
-    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
-    sigma = W.device_sigma(cfg, args.seed, dev)
-    pool = []
-    for s in range(args.pool):
-        gset = torch.empty((K, n), dtype=torch.float32, device=dev)
-        W.device_grads(cfg, s + 1, args.seed, sigma, gset)
-        pool.append(gset)
-        log(f"gradient set {s + 1}/{args.pool} generated")
-    del sigma
+    def alloc_state():
+        params = torch.empty(n, dtype=torch.float32, device=dev)
+        W.device_init_params(cfg, args.seed, params)
+        m = torch.zeros(n, dtype=torch.float32, device=dev)
+        v = torch.zeros(n, dtype=torch.float32, device=dev) if args.store_v else None
+        e = torch.zeros((K, n), dtype=torch.float32, device=dev)
+        mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
+        ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+        return params, m, v, e, mask, ws
+
+    def alloc_grads():
+        sigma = W.device_sigma(cfg, args.seed, dev)
+        pool = []
+        for s in range(args.pool):
+            gset = torch.empty((K, n), dtype=torch.float32, device=dev)
+            W.device_grads(cfg, s + 1, args.seed, sigma, gset)
+            pool.append(gset)
+            log(f"gradient set {s + 1}/{args.pool} generated")
+        del sigma
+        return pool
+
+    if args.grads_first:
+        pool = alloc_grads()
+        params, m, v, e, mask, ws = alloc_state()
+    else:
+        params, m, v, e, mask, ws = alloc_state()
+        pool = alloc_grads()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     calib = stream_calibration(torch, dev, log) if args.calib else None

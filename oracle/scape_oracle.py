@@ -52,10 +52,14 @@ by default, equal contiguous partitions, owner = floor(p*K/P), and v holding
 the last uncorrected v_t at masked indices.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py``
-against brute force, closed forms and invariants.  The statistic's formula
-(O2) itself cannot be checked against any value on the pages: parity
-unpinned for the formula, although its owner mapping, sign handling and
-ordering are pinned.
+against brute force, closed forms and invariants.  The statistic of O2 is
+pinned where the pages fix it: at one worker and sparsity 0 it is the dense
+first moment m_t of §II-C eq. (2) bit for bit (also when a residual is
+carried into that regime), its residual term is pinned by a worked example
+of error-feedback re-injection (§II-B), and its owner mapping, sign
+handling and ordering are pinned.  Its general form for several workers
+(the owner's own error-compensated gradient) is a reading of the pages that
+no page value can check: parity unpinned for that choice alone.
 """
 
 from __future__ import annotations

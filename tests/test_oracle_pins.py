@@ -5,8 +5,15 @@ property that the pages' definitions fix (SCAPE paper §II-B and §II-C eq. (2),
 technical summary §2), written so that a plausible slip in the oracle (a tie
 broken the wrong way, the wrong worker's gradient in the statistic, m_t in
 place of m_{t-1} in the second moment, swapped or missing bias corrections, eps
-inside the square root, a different summation order, a missing one-step lag)
-fails at least one of them.
+inside the square root, a different summation order, a missing one-step lag,
+a statistic keyed on the gradient without its error-feedback residual) fails
+at least one of them.
+
+The statistic that keys the mask is pinned twice: at one worker and sparsity
+0 it must be the dense first moment of AdamS (§II-C eq. (2)) bit for bit,
+also when a residual is carried into that regime; and a worked example shows
+error feedback (§II-B) raising an element whose own gradient never ranks
+into the mask, which then sends its whole accumulated residual.
 """
 
 import math
@@ -104,6 +111,82 @@ def test_statistic_formula_worked_example():
     assert O.topk_indices(keys, 3).tolist() == [1, 2, 3]
     s = keys.view(F32)
     assert abs(float(s[0])) < 1e-6 and abs(float(s[3]) - 1.8) < 1e-6
+
+
+@pytest.mark.parametrize("P,n_p,T,residual", [(1, 700, 12, False), (3, 257, 8, False), (2, 300, 6, True)])
+def test_statistic_is_dense_first_moment_at_one_worker_sparsity_zero(P, n_p, T, residual):
+    """K = 1 and k = n_p: every element is sent every step and the
+    synchronised buffer is the worker's own error-compensated gradient, so
+    the statistic that keys M_{t+1} is the dense first moment m_t of AdamS
+    (SCAPE paper §II-C eq. (2)).  Its keys must equal bits(|m_t|) bit for bit
+    at every step, with m_t taken from the state after the step's update
+    (two different code paths of the oracle: O2 and O6).  With `residual`
+    the state enters the dense regime carrying a nonzero error-feedback
+    residual (as after a change of density): the first dense step sends it,
+    so the first moment, and with it the key, includes it."""
+    rng = np.random.default_rng(P * 100 + n_p)
+    hp = O.Hyper.make(weight_decay=0.01)
+    w0 = (rng.standard_normal(P * n_p) * 0.02).astype(F32)
+    opt = O.OracleOptimizer(w0, P, 1, n_p, hp)
+    if residual:  # enter at step 2 with M_2 = everything and e != 0
+        for st in opt.parts:
+            st.e[:] = (rng.standard_normal((1, n_p)) * 1e-2).astype(F32)
+            st.idx = np.arange(n_p)
+        opt.t = 1
+    for t in range(opt.t + 1, opt.t + T + 1):
+        e_in = opt.gather("e").copy()
+        g = (rng.standard_normal((1, P * n_p)) * 10.0 ** rng.integers(-6, -1, (1, P * n_p))).astype(F32)
+        outs = opt.step(g)
+        for p in range(P):
+            st = opt.parts[p]
+            assert np.all(st.e == 0)
+            assert outs[p]["cur"].size == n_p
+            assert np.array_equal(outs[p]["keys"], O.magnitude_keys(st.m)), f"step {t} partition {p}"
+        if residual and t == 2:  # m_1 = 0 here: a key of the gradient alone would be |c1*g|
+            assert np.any(e_in != 0)
+            assert not np.array_equal(outs[0]["keys"], O.magnitude_keys(hp.c1 * g[0, :n_p]))
+
+
+def test_residual_reinjection_worked_example():
+    """Error feedback re-injects what was not sent (SCAPE paper §II-B: the
+    dropped part is added back into later communication), and the mask is
+    keyed on the owner's error-compensated gradient.  One partition, one
+    worker, k = 1.  Element 0 receives a constant gradient c = 0.25 every
+    step and element 3 a constant h = 0.5 > c; the rest receive 0.  Element
+    3 takes the mask at step 1 and keeps it while element 0's residual
+    grows by c per step.  With m_0 = 0 off the mask, element 0's statistic
+    at step t is c1 * (t*c); element 3's is its dense first moment
+    h * (1 - b1^t).  Element 0 enters M_{T+1} at the first step T at which
+    the former exceeds the latter (found here from the float64 closed forms:
+    the margins are ~1e-2, far above fp32 rounding), although its own
+    gradient never would.  At step T + 1 it sends its whole accumulated
+    residual plus the step's gradient, (T + 1) * c exactly (multiples of
+    1/4 are exact in fp32), and its residual returns to 0."""
+    n = 8
+    hp = O.Hyper.make()
+    c, h = F32(0.25), F32(0.5)
+    b1, c1 = float(hp.b1), float(hp.c1)
+    T = next(t for t in range(1, 100) if c1 * t * float(c) > float(h) * (1 - b1 ** t))
+    assert T == 17
+    assert all(c1 * float(c) < float(h) * (1 - b1 ** t) for t in range(1, 100))  # never on its own
+    w0 = np.linspace(0.1, 0.8, n).astype(F32)
+    opt = O.OracleOptimizer(w0, 1, 1, 1, hp)
+    st = opt.parts[0]
+    for t in range(1, T + 3):
+        g = np.zeros(n, F32)
+        g[0], g[3] = c, h
+        out = opt.step(g[None])[0]
+        s = out["keys"].view(F32).astype(np.float64)
+        if t <= T:
+            assert out["cur"].tolist() == [3], f"step {t}"
+            assert st.e[0, 0] == F32(t * 0.25) and st.w[0] == w0[0], f"step {t}"
+            assert abs(s[0] - c1 * t * 0.25) < 1e-6 and abs(s[3] - 0.5 * (1 - b1 ** t)) < 1e-6, f"step {t}"
+            assert out["nxt"].tolist() == ([0] if t == T else [3]), f"step {t}"
+        if t == T + 1:
+            assert out["cur"].tolist() == [0]
+            assert out["bbar"][0] == F32((T + 1) * 0.25)  # the whole accumulated residual
+            assert st.e[0, 0] == 0 and st.w[0] != w0[0]
+            assert st.e[0, 3] == h                        # element 3 now accumulates
 
 
 @pytest.mark.parametrize("P,K", [(8, 4), (4, 4), (6, 4), (2, 4), (4, 2), (5, 3)])

@@ -21,7 +21,8 @@ Randomness:
   * device generator (large layouts only): torch's CUDA Philox seeded from the
     same tuple.  It produces different numbers than the host generator; a test
     that needs oracle inputs for a device-generated workload copies the slices
-    it checks back to the host.
+    it checks back to the host.  The stress law's duplicate positions and
+    donor picks come from the host stream 3 in both generators.
 """
 
 from __future__ import annotations
@@ -147,6 +148,35 @@ def flat_config(name: str, n: int, P: int, K: int, sparsity: str, steps: int = 3
                   grad_law=grad_law, **kw)
 
 
+# Tensor sizes cycled by mixed_config: small and large, odd and even, so
+# that every partition of a small layout spans several tensors (several
+# gradient scales) and the tensor boundaries fall at every alignment.
+_MIXED_SIZES = (1531, 64, 2903, 1, 777, 4099, 250, 17, 1024, 3)
+
+
+def mixed_config(name: str, n: int, P: int, K: int, sparsity: str, steps: int = 3,
+                 grad_law: str = "tensor_sigma", config_id: int = 101, **kw) -> Config:
+    """n parameters as a list of many tensors of mixed sizes (each with its
+    own gradient scale), for small parity cases in which one partition holds
+    several scales, as the model layouts' partitions do."""
+    tensors, left, i = [], n, 0
+    while left > 0:
+        sz = min(_MIXED_SIZES[i % len(_MIXED_SIZES)], left)
+        tensors.append((f"t{i}", sz))
+        left -= sz
+        i += 1
+    return Config(name=name, config_id=config_id, tensors=tuple(tensors), num_partitions=P,
+                  num_workers=K, sparsity=sparsity, steps=steps, grad_law=grad_law, **kw)
+
+
+def partition_tensor_count(cfg: Config, p: int) -> int:
+    """How many tensors partition p spans."""
+    off = cfg.tensor_offsets()
+    first = int(np.searchsorted(off, p * cfg.n_p, side="right")) - 1
+    last = int(np.searchsorted(off, (p + 1) * cfg.n_p - 1, side="right")) - 1
+    return last - first + 1
+
+
 def _cfgs():
     tiny = Config("tiny", 0, (("flat", 1 << 20),), 4, 2, "0.9", 20, grad_law="partition_scale")
     gpt = Config("gpt345m", 1, tuple(gpt_tensors(24, 1024, 4096, 50257, 1024)), 32, 8, "0.9", 10)
@@ -207,24 +237,37 @@ def init_params(cfg: Config, seed: int = 0, partitions: Optional[Iterable[int]] 
     return np.concatenate([init_params_partition(cfg, p, seed) for p in parts])
 
 
+def donor_count(cfg: Config) -> int:
+    """Number of donor magnitudes of the stress law: the |g| values ranked
+    k-8 .. k+7 of a partition (fewer where that range leaves the partition)."""
+    return min(cfg.n_p, cfg.k + 8) - max(0, cfg.k - 8)
+
+
+def duplicate_draws(cfg: Config, seed: int, step: int, worker: int, p: int):
+    """Stress law's random choices for one (step, worker, partition), from
+    the host stream STREAM_DUPS: floor(1% n_p) distinct positions (drawn
+    without replacement) and, for each, which donor it copies.  Both the
+    host and the device generator plant duplicates from these draws."""
+    ndup = cfg.n_p // 100
+    r = rng(seed, cfg.config_id, STREAM_DUPS, step, worker, p)
+    pos = r.choice(cfg.n_p, size=ndup, replace=False)
+    pick = r.integers(0, donor_count(cfg), size=ndup)
+    return pos.astype(np.int64), pick.astype(np.int64)
+
+
 def _duplicate_magnitudes(cfg: Config, g: np.ndarray, seed: int, step: int, worker: int, p: int) -> None:
     """Stress law: floor(1% n_p) positions, chosen without replacement, take
     sign-preserving copies of 16 donor magnitudes (the |g| values ranked
     k-8 .. k+7 in the partition) so that exact key ties straddle the
     selection boundary."""
     n_p, k = g.shape[0], cfg.k
-    ndup = n_p // 100
-    if ndup == 0:
+    if n_p // 100 == 0:
         return
-    r = rng(seed, cfg.config_id, STREAM_DUPS, step, worker, p)
     mag = np.abs(g)
-    lo_rank = max(0, k - 8)
-    hi_rank = min(n_p, k + 8)
     order = np.argsort(-mag.astype(np.float64), kind="stable")
-    donors = mag[order[lo_rank:hi_rank]]
-    pos = r.choice(n_p, size=ndup, replace=False)
-    pick = donors[r.integers(0, donors.shape[0], size=ndup)]
-    g[pos] = np.where(g[pos] < 0, -pick, pick).astype(np.float32)
+    donors = mag[order[max(0, k - 8):min(n_p, k + 8)]]
+    pos, pick = duplicate_draws(cfg, seed, step, worker, p)
+    g[pos] = np.where(g[pos] < 0, -donors[pick], donors[pick]).astype(np.float32)
 
 
 def grads_partition(cfg: Config, step: int, worker: int, p: int, seed: int = 0) -> np.ndarray:
@@ -285,12 +328,10 @@ def device_init_params(cfg: Config, seed: int, out) -> None:
     out.normal_(0.0, 1.0, generator=gen).mul_(0.02)
 
 
-def device_grads(cfg: Config, step: int, seed: int, sigma, out) -> None:
-    """Fill out[K][n] (device, fp32) with the step's gradients.
-
-    Normal laws: sigma * z.  Stress law: sigma * t_3 with t_3 = z0 /
-    sqrt((z1^2 + z2^2 + z3^2) / 3), then the duplicate-magnitude planting of
-    the host law, per (worker, partition)."""
+def device_base_grads(cfg: Config, step: int, seed: int, sigma, out) -> None:
+    """Fill out[K][n] (fp32, on out's device) with the step's gradients
+    before any duplicate planting: sigma * z for the normal laws, sigma * t_3
+    with t_3 = z0 / sqrt((z1^2 + z2^2 + z3^2) / 3) for the stress law."""
     import torch
     for i in range(cfg.K):
         gen = torch.Generator(device=out.device)
@@ -306,23 +347,30 @@ def device_grads(cfg: Config, step: int, seed: int, sigma, out) -> None:
             row.div_(chi.div_(3.0).sqrt_())
             del chi, tmp
         row.mul_(sigma)
-        if cfg.grad_law == "stress_t3":
-            _device_duplicates(cfg, row, gen)
 
 
-def _device_duplicates(cfg: Config, row, gen) -> None:
+def device_grads(cfg: Config, step: int, seed: int, sigma, out) -> None:
+    """Fill out[K][n] (fp32, on out's device) with the step's gradients:
+    device_base_grads, then for the stress law the duplicate-magnitude
+    planting of the host law, per (worker, partition), at the positions and
+    donor picks of duplicate_draws (drawn on the host)."""
+    device_base_grads(cfg, step, seed, sigma, out)
+    if cfg.grad_law == "stress_t3":
+        for i in range(cfg.K):
+            _device_duplicates(cfg, out[i], seed, step, i)
+
+
+def _device_duplicates(cfg: Config, row, seed: int, step: int, worker: int) -> None:
     import torch
     n_p, k = cfg.n_p, cfg.k
-    ndup = n_p // 100
-    if ndup == 0:
+    if n_p // 100 == 0:
         return
     for p in range(cfg.P):
         seg = row[p * n_p:(p + 1) * n_p]
-        mag = seg.abs()
-        top = torch.topk(mag, min(n_p, k + 8), largest=True, sorted=True).values
+        top = torch.topk(seg.abs(), min(n_p, k + 8), largest=True, sorted=True).values
         donors = top[max(0, k - 8):]
-        pos = torch.randperm(n_p, generator=gen, device=row.device)[:ndup]
-        pick = donors[torch.randint(0, donors.numel(), (ndup,), generator=gen, device=row.device)]
-        sgn = torch.where(seg[pos] < 0, -1.0, 1.0)
-        seg[pos] = pick * sgn
-        del mag, top, pos, pick, sgn
+        pos_h, pick_h = duplicate_draws(cfg, seed, step, worker, p)
+        pos = torch.from_numpy(pos_h).to(row.device)
+        pick = donors[torch.from_numpy(pick_h).to(row.device)]
+        seg[pos] = torch.where(seg[pos] < 0, -pick, pick)
+        del top, donors, pos, pick

@@ -351,6 +351,22 @@ def test_step_small_shapes(S, n_p, P, K, sp, law):
     run_lockstep(S, cfg, cfg.steps)
 
 
+@pytest.mark.parametrize("n_p,P,K,sp,law", [
+    (7652, 3, 2, "0.9", "tensor_sigma"),          # n_p % 16 == 4: vector streams, element-wise AdamS
+    (3 * 4096 + 100, 4, 4, "0.99", "tensor_sigma"),  # several tiles and a ragged tail
+    (5003, 2, 3, "0.95", "tensor_sigma"),         # odd n_p: scalar path
+    (12_000, 2, 2, "0.999", "stress_t3"),         # duplicate magnitudes across tensor scales
+])
+def test_step_mixed_tensors(S, n_p, P, K, sp, law):
+    """Layouts of many small tensors, each with its own gradient scale, so
+    that every partition holds several scales (as the model layouts'
+    partitions do, where captures crowd into the largest-scale tiles)."""
+    cfg = W.mixed_config("mixed", P * n_p, P, K, sp, steps=5, grad_law=law, weight_decay=0.01)
+    assert min(W.partition_tensor_count(cfg, p) for p in range(P)) >= 3
+    assert len(set(W.tensor_sigmas(cfg).tolist())) == len(cfg.tensors)
+    run_lockstep(S, cfg, cfg.steps)
+
+
 @pytest.mark.parametrize("n_p,P,K,sp,law,offset,store_v", [
     (3 * 4096 + 100, 4, 8, "0.99", "tensor_sigma", 0, True),     # ragged tail, element-wise AdamS stores
     (4096 * 4, 32, 8, "0.99", "tensor_sigma", 0, False),        # whole-segment AdamS stores, no v
@@ -364,6 +380,20 @@ def test_step_multi_pass(S, n_p, P, K, sp, law, offset, store_v):
     cfg = W.flat_config("multipass", P * n_p, P, K, sp, steps=4, grad_law=law, weight_decay=0.01)
     assert S.step_pass_count(S.dims(cfg.n, P, K), cfg.k) == K
     run_lockstep(S, cfg, cfg.steps, offset=offset, store_v=store_v)
+
+
+@pytest.mark.parametrize("n_p,P,K,sp,store_v", [
+    (8228, 8, 8, "0.99", True),       # n_p % 16 == 4: element-wise AdamS stores
+    (5003, 4, 8, "0.995", True),      # odd n_p: scalar path, K > P
+    (8192, 16, 8, "0.99", False),     # whole-segment AdamS stores, no v
+])
+def test_step_multi_pass_mixed_tensors(S, n_p, P, K, sp, store_v):
+    """The K-pass form (the form Llama-500M runs) on layouts whose
+    partitions each hold several tensors with their own gradient scales."""
+    cfg = W.mixed_config("mixedmp", P * n_p, P, K, sp, steps=5, weight_decay=0.01)
+    assert S.step_pass_count(S.dims(cfg.n, P, K), cfg.k) == K
+    assert min(W.partition_tensor_count(cfg, p) for p in range(P)) >= 3
+    run_lockstep(S, cfg, cfg.steps, store_v=store_v)
 
 
 @pytest.mark.slow
@@ -609,15 +639,22 @@ def _poison_bounds(S, value_fn):
     return hook
 
 
+@pytest.mark.parametrize("form", ["one_pass", "k_passes"])
 @pytest.mark.parametrize("mode", ["nothing", "everything", "mixed"])
-def test_step_capture_bound_fallback(S, mode):
+def test_step_capture_bound_fallback(S, mode, form):
     """A bound that captures fewer than k keys (here: none) sends the
     partition through the exact recount; a zero bound captures every key.
-    Both give the oracle's result bit for bit."""
-    cfg = W.flat_config("fallback", 5 * 30_000, 5, 2, "0.99", steps=4)
+    Both give the oracle's result bit for bit, in the single-pass step and
+    in the K-pass form (whose owner pass leaves the owner's sparse buffer
+    and the saved pre-update m for the recount)."""
+    if form == "one_pass":
+        cfg = W.flat_config("fallback", 5 * 30_000, 5, 2, "0.99", steps=4)
+    else:
+        cfg = W.mixed_config("fallbackmp", 32 * 4096 * 4, 32, 8, "0.99", steps=4)
+    assert S.step_pass_count(S.dims(cfg.n, cfg.P, cfg.K), cfg.k) == (1 if form == "one_pass" else cfg.K)
     inf_bits = 0x7F800000
     fn = {"nothing": lambda p: inf_bits, "everything": lambda p: 0,
-          "mixed": lambda p: (inf_bits, 0, 1 << 30, 0x3A800000, inf_bits)[p]}[mode]
+          "mixed": lambda p: (inf_bits, 0, 1 << 30, 0x3A800000, inf_bits)[p % 5]}[mode]
     run_lockstep(S, cfg, cfg.steps, before_step=_poison_bounds(S, fn))
 
 

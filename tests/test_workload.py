@@ -52,3 +52,51 @@ def test_partition_scale_law_and_stress_duplicates():
         vals, counts = np.unique(mag, return_counts=True)
         assert counts.max() >= 5          # planted duplicate magnitudes
         assert np.all(np.isfinite(mag))
+
+
+def test_device_stress_law_plants_host_drawn_duplicates():
+    """The device generator's stress law, run here on a CPU tensor through
+    the same code: it is the base draw (sigma * t_3) except at the
+    floor(1% n_p) distinct positions that duplicate_draws gives for each
+    (step, worker, partition), which hold sign-preserving copies of the
+    donor magnitudes ranked k-8 .. k+7 of that partition's base draw."""
+    torch = pytest.importorskip("torch")
+    cfg = W.flat_config("dstress", 3 * 30_000, 3, 2, "0.999", grad_law="stress_t3")
+    n_p, k = cfg.n_p, cfg.k
+    sigma = W.device_sigma(cfg, 0, "cpu")
+    base = torch.empty((cfg.K, cfg.n), dtype=torch.float32)
+    g = torch.empty_like(base)
+    W.device_base_grads(cfg, 2, 0, sigma, base)
+    W.device_grads(cfg, 2, 0, sigma, g)
+    b, gg = base.numpy(), g.numpy()
+    assert W.donor_count(cfg) == 16
+    for i in range(cfg.K):
+        for p in range(cfg.P):
+            sl = slice(p * n_p, (p + 1) * n_p)
+            bs, gs = b[i, sl], gg[i, sl]
+            pos, pick = W.duplicate_draws(cfg, 0, 2, i, p)
+            assert pos.size == n_p // 100 == np.unique(pos).size
+            assert pos.min() >= 0 and pos.max() < n_p and pick.min() >= 0 and pick.max() < 16
+            off = np.ones(n_p, bool)
+            off[pos] = False
+            assert np.array_equal(gs[off].view(np.uint32), bs[off].view(np.uint32))
+            donors = np.sort(np.abs(bs))[::-1][k - 8:k + 8]
+            assert np.array_equal(np.abs(gs[pos]), donors[pick])
+            assert np.all(np.signbit(gs[pos]) == (bs[pos] < 0))
+            # the planted magnitudes straddle the k-th largest: exact ties there
+            assert np.count_nonzero(np.abs(gs) == donors[7]) >= 2
+
+
+def test_duplicate_draws_are_the_host_law_draws():
+    """The host law plants at duplicate_draws' positions and picks too."""
+    cfg = W.flat_config("hstress", 2 * 20_000, 2, 2, "0.99", grad_law="stress_t3")
+    g = W.grads_partition(cfg, 1, 1, 1)
+    r = W.rng(0, cfg.config_id, W.STREAM_GRADS, 1, 1, 1)
+    base = (W.sigma_per_element(cfg, 0, cfg.n_p, 2 * cfg.n_p) *
+            r.standard_t(3, size=cfg.n_p).astype(np.float32)).astype(np.float32)
+    pos, pick = W.duplicate_draws(cfg, 0, 1, 1, 1)
+    off = np.ones(cfg.n_p, bool)
+    off[pos] = False
+    assert np.array_equal(g[off], base[off])
+    donors = np.sort(np.abs(base))[::-1][cfg.k - 8:cfg.k + 8]
+    assert np.array_equal(np.abs(g[pos]), donors[pick])

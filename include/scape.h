@@ -50,7 +50,10 @@ typedef enum {
   SCAPE_EINVAL = 1,     /* null pointer, bad hyper-parameter, step < 1     */
   SCAPE_ESHAPE = 2,     /* n, P, K or k outside the limits above           */
   SCAPE_EWORKSPACE = 3, /* workspace smaller than scape_workspace_bytes()  */
-  SCAPE_EHIP = 4        /* a HIP launch or event call failed               */
+  SCAPE_EHIP = 4,       /* a HIP launch or event call failed               */
+  SCAPE_EMASK = 5       /* scape_mask_check: a mask breaks the partitioned
+                           top-k contract (k bits per partition, index list
+                           and tile offsets on the bits, no selection fault) */
 } scape_status;
 
 /* n = total parameters, num_partitions = P, num_workers = K. */
@@ -79,13 +82,18 @@ typedef struct {
  *   tile_off u32[P * T], T = ceil(n_p / scape_tile_elems()): for tile t of
  *            partition p, the number of selected elements of p that lie
  *            before local index t*scape_tile_elems().
- *   meta     u32[2 * P] threshold record (may be null where a call does not
+ *   meta     u32[3 * P] threshold record (may be null where a call does not
  *            need it): meta[p] = the k-th largest key of partition p in the
  *            selection that produced this mask; meta[P + p] = the key bound
- *            at which the next step captures selection candidates.  Any
+ *            at which the next step captures selection candidates (any
  *            value is safe: a bound that captures fewer than k keys of a
- *            partition sends it through an exact recount, so the record only
- *            affects speed, never the result.
+ *            partition sends it through an exact recount, so it only
+ *            affects speed, never the result); meta[2P + p] = fault bits of
+ *            that selection, 0 when it selected exactly k elements (bit 0:
+ *            the threshold search found no digit holding the k-th key; bit
+ *            1: the emitted count was not k).  A nonzero fault word only
+ *            arises from corrupted inputs or workspace; scape_mask_check
+ *            reports it.
  * The sparse buffers b are laid out like idx: entry r of a buffer belongs to
  * element idx[r].
  */
@@ -187,10 +195,13 @@ scape_status scape_adams_update(const scape_dims* dims, int64_t k, float* params
  *   (see scape_mask_view) to bound its candidate capture, and writes the
  *   record of slot t&1.
  *   1. a^i = grads[i] + e[i]; error-feedback compression at M_t; e updated
- *      in place; every worker's sparse buffer is written to the workspace.
- *      The step runs as K passes over the flat buffer: for every partition,
- *      one pass per non-owner worker, then the owner's pass (steps 2 and 3),
- *      which reads the other workers' sparse buffers back.
+ *      in place.  The step makes one pass or K passes over the flat buffer
+ *      (scape_step_pass_count; the same results bit for bit).  One pass
+ *      walks every worker's rows of a tile together, sums the workers'
+ *      values of each masked element in registers and writes only the
+ *      owner's sparse buffer.  K passes compress, for every partition, one
+ *      non-owner worker per pass into its sparse buffer in the workspace,
+ *      then the owner's pass (steps 2 and 3) reads those buffers back.
  *   2. statistic per partition p with owner o: s = b1*m + (1-b1)*a^o, using
  *      m before this step's update; M_{t+1} = per-partition top-k of |s|.
  *   3. b_bar = worker mean of the sparse buffers; AdamS at M_t.
@@ -294,6 +305,22 @@ scape_status scape_mask_overlap(const scape_dims* dims, int64_t k, scape_mask_vi
  */
 scape_status scape_mask_union(const scape_dims* dims, int64_t k, uint64_t* acc_bits, scape_mask_view m,
                               uint64_t* count_out, hipStream_t stream);
+
+/*
+ * Validation of one mask against the partitioned top-k contract ([S] §2:
+ * exactly k selected elements per partition, one mask shared by every
+ * worker): in every partition the bits hold exactly k elements and none
+ * past n_p, tile_off matches the bits, idx lists the set bits in ascending
+ * order, and (when m.meta is not null) the selection's fault word is 0.
+ * result is a device buffer of u32[P] that receives per-partition reason
+ * bits (1: fault word set; 2: bit count or tile offsets differ from k; 4:
+ * idx does not match the bits; 8: bits past n_p).  Reads m.bits, m.idx,
+ * m.tile_off and m.meta; SYNCHRONOUS: it waits for `stream` (and so for
+ * any step that wrote the mask on it) and returns SCAPE_OK, or SCAPE_EMASK
+ * with the first offending partition named in scape_last_error().
+ */
+scape_status scape_mask_check(const scape_dims* dims, int64_t k, scape_mask_view m, uint32_t* result,
+                              hipStream_t stream);
 
 /* -------------------------------------------------------------- utility */
 

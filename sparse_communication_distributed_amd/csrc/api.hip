@@ -53,12 +53,12 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
     rem -= nb;
   }
   r.nlevels = nl;
-  // mask slot: bits, idx, tile_off, then the threshold record u32[2P]
+  // mask slot: bits, idx, tile_off, then the threshold record u32[3P]
   r.off_bits = 0;
   r.off_idx = align256((size_t)P * r.wpp * 8);
   r.off_toff = align256(r.off_idx + (size_t)P * k * 4);
   r.off_meta = align256(r.off_toff + (size_t)P * r.tpp * 4);
-  r.slot_bytes = align256(r.off_meta + (size_t)P * 2 * 4);
+  r.slot_bytes = align256(r.off_meta + (size_t)P * 3 * 4);
   // workspace
   size_t o = 0;
   r.ws_b = o;       o = align256(o + (size_t)K * P * k * 4);
@@ -673,6 +673,35 @@ scape_status scape_mask_union(const scape_dims* dims, int64_t k, uint64_t* acc_b
   return hip_check(launch_union(g, acc_bits, m.bits, count_out, stream), "union");
 }
 
+scape_status scape_mask_check(const scape_dims* dims, int64_t k, scape_mask_view m, uint32_t* result,
+                              hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (!m.bits || !m.idx || !m.tile_off || !result) return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = hip_check(launch_mask_check(g, m.bits, m.idx, m.tile_off, m.meta, result, stream), "mask check")))
+    return st;
+  std::vector<uint32_t> res((size_t)g.P);
+  if ((st = hip_check(hipMemcpyAsync(res.data(), result, (size_t)g.P * 4, hipMemcpyDeviceToHost, stream),
+                      "mask check copy")))
+    return st;
+  if ((st = hip_check(hipStreamSynchronize(stream), "mask check sync"))) return st;
+  int64_t nbad = 0, first = -1;
+  for (int p = 0; p < g.P; ++p)
+    if (res[p]) {
+      if (first < 0) first = p;
+      ++nbad;
+    }
+  if (!nbad) return SCAPE_OK;
+  const uint32_t r = res[first];
+  return fail(SCAPE_EMASK,
+              "%lld of %d partitions violate the partitioned top-k contract; first: partition %lld:%s%s%s%s",
+              (long long)nbad, g.P, (long long)first, (r & kMaskBadFault) ? " selection fault recorded;" : "",
+              (r & kMaskBadCount) ? " bit count or tile offsets differ from k;" : "",
+              (r & kMaskBadIdx) ? " index list does not match the bits;" : "",
+              (r & kMaskBadPad) ? " bits set past the partition end;" : "");
+}
+
 const char* scape_status_string(scape_status s) {
   switch (s) {
     case SCAPE_OK: return "ok";
@@ -680,6 +709,7 @@ const char* scape_status_string(scape_status s) {
     case SCAPE_ESHAPE: return "invalid shape";
     case SCAPE_EWORKSPACE: return "workspace too small";
     case SCAPE_EHIP: return "HIP error";
+    case SCAPE_EMASK: return "mask violates the partitioned top-k contract";
   }
   return "unknown status";
 }

@@ -55,7 +55,7 @@ struct PartSel {
   uint32_t r;      // rank still needed among composites matching prefix
   uint32_t done;   // 1: every composite matching prefix is selected
   uint32_t bin1;   // level-1 digit of the threshold
-  uint32_t fault;  // bit 0: rank not found; bit 1: emitted count != k
+  uint32_t fault;  // bit 0: rank not found; bit 1: emitted count != k (recorded in the slot's meta)
   uint32_t fb;     // 1: the captured candidates cannot hold the top k
   uint32_t lo_fb;  // capture bound of the fallback (lowest key of bin1)
   uint32_t kth;      // smallest selected key (the k-th largest key)
@@ -185,6 +185,14 @@ hipError_t launch_bias_step(scape_bias_state* st, float b1, float b2, hipStream_
 hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float* m, float* v, float b1,
                               float b2, float c1, float c2, float ibc1, float ibc2, float eps, float wd,
                               float lr, bool vec, hipStream_t s);
+// Reason bits of the mask check, per partition.
+constexpr uint32_t kMaskBadFault = 1;  // the selection's fault word is set
+constexpr uint32_t kMaskBadCount = 2;  // bit count != k, or tile offsets off
+constexpr uint32_t kMaskBadIdx = 4;    // index list off the bits, out of order or range
+constexpr uint32_t kMaskBadPad = 8;    // bits set past n_p
+// res: u32[P], per-partition reason bits (zeroed first).
+hipError_t launch_mask_check(const Geom& g, const uint64_t* bits, const uint32_t* idx, const uint32_t* tile_off,
+                             const uint32_t* meta, uint32_t* res, hipStream_t s);
 hipError_t launch_union(const Geom& g, uint64_t* acc, const uint64_t* m, uint64_t* out, hipStream_t s);
 hipError_t launch_overlap(const Geom& g, const uint64_t* a, const uint64_t* b, uint64_t* out,
                           hipStream_t s);

@@ -526,6 +526,7 @@ scan_tiles_kernel(Geom g, const uint32_t* __restrict__ tilecnt, uint32_t* __rest
     if (meta_out) {
       meta_out[p] = state[p].kth;
       meta_out[g.P + p] = state[p].lo_next;
+      meta_out[2 * g.P + p] = state[p].fault;
     }
   }
 }
@@ -634,6 +635,56 @@ union_kernel(uint64_t* __restrict__ acc, const uint64_t* __restrict__ m, int64_t
   if (lane_id() == 0 && c) atomicAdd(out, (unsigned long long)c);
 }
 
+// ---- validation of a mask against the partitioned top-k contract ----
+// One wave per tile: the tile's selected count must equal the step between
+// its offset and the next tile's (k after the last tile; the first offset
+// is 0), so the offsets are right and the partition holds exactly k bits;
+// bits past n_p must be clear; the selection's fault word must be 0.
+__global__ void __launch_bounds__(kThreads)
+check_tiles_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
+                   const uint32_t* __restrict__ meta, uint32_t* __restrict__ res) {
+  const int p = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= g.tpp) return;  // wave-uniform
+  const uint32_t lane = lane_id();
+  const int64_t w = t * kWordsPerTile + lane;
+  const uint64_t word = (w < g.wpp) ? bits[(int64_t)p * g.wpp + w] : 0ull;
+  uint32_t bad = 0;
+  const int tail = (int)(g.n_p & 63);
+  if (w == g.wpp - 1 && tail && (word >> tail)) bad |= kMaskBadPad;
+  uint32_t c = (uint32_t)__popcll(word);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+  if (lane == 0) {
+    const uint32_t* to = tile_off + (int64_t)p * g.tpp;
+    const uint32_t here = to[t];
+    const uint32_t next = (t + 1 < g.tpp) ? to[t + 1] : (uint32_t)g.k;
+    if ((t == 0 && here != 0u) || next < here || next - here != c) bad |= kMaskBadCount;
+    if (t == 0 && meta && meta[2 * g.P + p] != 0u) bad |= kMaskBadFault;
+  }
+  if (bad) atomicOr(res + p, bad);
+}
+
+// Every index entry lies in its partition, ascends, and sits on a set bit
+// (with exactly k bits per partition this makes the list the set bits).
+__global__ void __launch_bounds__(kThreads)
+check_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __restrict__ idx,
+                 uint32_t* __restrict__ res) {
+  const int64_t total = (int64_t)g.P * g.k;
+  for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < total; r += (int64_t)gridDim.x * kThreads) {
+    const int64_t p = r / g.k;
+    const int64_t lo = p * g.n_p;
+    const int64_t j = (int64_t)idx[r];
+    bool ok = j >= lo && j < lo + g.n_p;
+    if (ok) {
+      const int64_t loc = j - lo;
+      ok = ((bits[p * g.wpp + (loc >> 6)] >> (loc & 63)) & 1ull) != 0ull;
+    }
+    if (ok && r % g.k != 0) ok = (int64_t)idx[r - 1] < j;
+    if (!ok) atomicOr(res + p, kMaskBadIdx);
+  }
+}
+
 // kCaptureMargin * k, at most n_p.
 uint32_t capture_target(const Geom& g) {
   double t = kCaptureMargin * (double)g.k;
@@ -686,6 +737,17 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
     write_idx_kernel<true><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
   else
     write_idx_kernel<false><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_check(const Geom& g, const uint64_t* bits, const uint32_t* idx, const uint32_t* tile_off,
+                             const uint32_t* meta, uint32_t* res, hipStream_t s) {
+  hipError_t e = launch_zero_u32(res, g.P, s);
+  if (e != hipSuccess) return e;
+  check_tiles_kernel<<<dim3((unsigned)((g.tpp + 3) / 4), g.P), kThreads, 0, s>>>(g, bits, tile_off, meta, res);
+  int64_t blocks = ((int64_t)g.P * g.k + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  check_idx_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(g, bits, idx, res);
   return hipGetLastError();
 }
 

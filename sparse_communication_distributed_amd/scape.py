@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("SCAPE_LIB") or os.path.join(_PKG, "libscape.so")
 c_int64, c_int32, c_int, c_size_t = ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
 c_float, c_void_p, c_char_p = ctypes.c_float, ctypes.c_void_p, ctypes.c_char_p
 
-STATUS = {0: "SCAPE_OK", 1: "SCAPE_EINVAL", 2: "SCAPE_ESHAPE", 3: "SCAPE_EWORKSPACE", 4: "SCAPE_EHIP"}
+STATUS = {0: "SCAPE_OK", 1: "SCAPE_EINVAL", 2: "SCAPE_ESHAPE", 3: "SCAPE_EWORKSPACE", 4: "SCAPE_EHIP",
+          5: "SCAPE_EMASK"}
 
 
 class Dims(ctypes.Structure):
@@ -70,6 +71,7 @@ _SIGS = {
     "scape_mask_union": (c_int, [ctypes.POINTER(Dims), c_int64, c_void_p, MaskView, c_void_p, c_void_p]),
     "scape_dense_adams_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, Betas, c_float,
                                        c_int64, c_void_p]),
+    "scape_mask_check": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, c_void_p, c_void_p]),
     "scape_status_string": (c_char_p, [c_int]),
     "scape_last_error": (c_char_p, []),
     "scape_profile_stages": (c_int, []),
@@ -202,12 +204,12 @@ def mask_slot_tensors(d: Dims, k: int, blob, slot: int):
 
 
 def mask_slot_meta(d: Dims, k: int, blob, slot: int):
-    """The slot's threshold record as an int32 view [2P] (k-th keys, then
-    the next capture bounds)."""
+    """The slot's threshold record as an int32 view [3P] (k-th keys, the
+    next capture bounds, then the selection's fault words)."""
     import torch
     mv = mask_slot(d, k, blob, slot)
     off = mv.meta - blob.data_ptr()
-    return blob[off:off + 2 * d.num_partitions * 4].view(torch.int32)
+    return blob[off:off + 3 * d.num_partitions * 4].view(torch.int32)
 
 
 def view_from_tensors(bits=None, idx=None, tile_off=None, meta=None) -> MaskView:
@@ -315,6 +317,18 @@ def dense_adams_step(d: Dims, params, grads, m, v, bt: Betas, lr: float, step_no
                                         step_no, _stream(stream)))
 
 
+def mask_check(d: Dims, k: int, m: MaskView, result=None, stream=None) -> None:
+    """scape_mask_check (synchronous): raises ScapeError (SCAPE_EMASK) if the
+    mask breaks the partitioned top-k contract.  `result` is a device int32
+    tensor of at least P entries (allocated here if None); it receives the
+    per-partition reason bits."""
+    import torch
+    if result is None:
+        result = torch.empty(d.num_partitions, dtype=torch.int32, device=torch.cuda.current_device())
+    _need(result, "result", d.num_partitions, dtype="int32")
+    _check(lib().scape_mask_check(ctypes.byref(d), k, m, _ptr(result), _stream(stream)))
+
+
 def mask_overlap(d: Dims, k: int, a: MaskView, b: MaskView, count_out, stream=None) -> None:
     _need(count_out, "count_out", 8, dtype=None)
     _check(lib().scape_mask_overlap(ctypes.byref(d), k, a, b, _ptr(count_out), _stream(stream)))
@@ -381,6 +395,13 @@ class ScapeOptimizer:
         step(self.d, self.params, grads, self.m, self.v, self.e, self.mask, self.k, self.bt, self.lr,
              t, self.ws, stream)
         self.t = t  # a rejected call leaves the step count unchanged
+
+    def check(self, which: str = "next", stream=None) -> None:
+        """Validates mask M_{t+1} ("next") or M_t ("current") against the
+        partitioned top-k contract (waits for the stream); raises on a
+        violation."""
+        s = (self.t & 1) if which == "next" else ((self.t - 1) & 1)
+        mask_check(self.d, self.k, mask_slot(self.d, self.k, self.mask, s), stream=stream)
 
     def slot(self, which: str = "next"):
         """Mask views (bits, idx, tile_off): "next" = M_{t+1}, "current" = M_t."""

@@ -308,6 +308,8 @@ def run_lockstep(S, cfg, steps, seed=0, rtol_step=1e-6, rtol_end=1e-5, grad_fn=N
         torch.cuda.synchronize()
         check_mask(*opt.slot("next"), [o["nxt"] for o in outs], n_p)
         check_mask(*opt.slot("current"), [o["cur"] for o in outs], n_p)
+        opt.check("next")
+        opt.check("current")
         rt = rtol_end if t == steps else rtol_step
         for name in ("w", "m", "v", "e") if store_v else ("w", "m", "e"):
             got = host(getattr(opt, "params" if name == "w" else name))
@@ -774,3 +776,97 @@ def test_step_offload_two_host_threads(S):
             for name in ("w", "m", "v", "e"):
                 assert np.array_equal(g_[name].view(np.uint32), w_[name].view(np.uint32)), f"thread {tid} step {t} {name}"
 
+
+
+# ------------------------------------------------------------- mask check
+
+
+def _malformed(kind, loc, n_p, P, k, meta):
+    """A valid packed mask (host) with one planted violation; returns the
+    blob parts, the partition it breaks and the reason bits expected."""
+    bits, idx, toff = pack_mask(loc, n_p)
+    W_ = (n_p + 63) // 64
+    T = (n_p + 4095) // 4096
+    bits, idx, toff, meta = bits.copy(), idx.copy(), toff.copy(), meta.copy()
+    if kind == "bit_dropped":      # k - 1 bits in partition 1; its list names an unset bit
+        j = int(loc[1][5])
+        bits[W_ + j // 64] &= ~np.uint64(1 << (j % 64))
+        return (bits, idx, toff, meta), 1, 2 | 4
+    if kind == "bit_added":        # k + 1 bits in partition 2
+        j = int(np.setdiff1d(np.arange(n_p), loc[2])[3])
+        bits[2 * W_ + j // 64] |= np.uint64(1 << (j % 64))
+        return (bits, idx, toff, meta), 2, 2
+    if kind == "tile_off":         # a tile offset off by one
+        toff[T + 1] += 1
+        return (bits, idx, toff, meta), 1, 2
+    if kind == "idx_order":        # two index entries swapped
+        idx[3 * k + 7], idx[3 * k + 8] = idx[3 * k + 8], idx[3 * k + 7]
+        return (bits, idx, toff, meta), 3, 4
+    if kind == "idx_range":        # an entry outside its partition
+        idx[2 * k] = np.uint32(n_p - 1)  # partition 0's last element
+        return (bits, idx, toff, meta), 2, 4
+    if kind == "padding":          # a bit past n_p in partition 0's last word
+        bits[W_ - 1] |= np.uint64(1 << 63)
+        return (bits, idx, toff, meta), 0, 2 | 8
+    if kind == "fault_word":       # the selection recorded a fault
+        meta[2 * P + 3] = 2
+        return (bits, idx, toff, meta), 3, 1
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["bit_dropped", "bit_added", "tile_off", "idx_order", "idx_range", "padding",
+                                  "fault_word"])
+def test_mask_check_rejects_malformed_masks(S, kind):
+    """scape_mask_check returns SCAPE_EMASK for a mask that breaks the
+    partitioned top-k contract, naming the first offending partition, with
+    per-partition reason bits; the same mask unbroken passes.  The masks are
+    host-built data: nothing here can fault the device."""
+    P, n_p, k = 4, 3 * 4096 + 37, 500
+    rng = np.random.default_rng(31)
+    loc = [np.sort(rng.choice(n_p, k, replace=False)) for _ in range(P)]
+    d = S.dims(P * n_p, P, 1)
+    meta = np.zeros(3 * P, np.uint32)
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    bits_t, idx_t, toff_t = S.mask_slot_tensors(d, k, blob, 0)
+    meta_t = S.mask_slot_meta(d, k, blob, 0)
+    res = torch.full((P,), -1, dtype=torch.int32, device=DEV)
+
+    def load(parts):
+        b_, i_, t_, m_ = parts
+        bits_t.copy_(dev(b_.view(np.int64)))
+        idx_t.copy_(dev(i_.view(np.int32)))
+        toff_t.copy_(dev(t_.view(np.int32)))
+        meta_t.copy_(dev(m_.view(np.int32)))
+
+    good = pack_mask(loc, n_p)
+    load((*good, meta))
+    S.mask_check(d, k, S.mask_slot(d, k, blob, 0), res)
+    assert torch.all(res == 0)
+    parts, bad_p, reasons = _malformed(kind, loc, n_p, P, k, meta)
+    load(parts)
+    with pytest.raises(S.ScapeError) as ei:
+        S.mask_check(d, k, S.mask_slot(d, k, blob, 0), res)
+    assert ei.value.status == 5
+    assert f"partition {bad_p}:" in str(ei.value)
+    got = host(res).view(np.uint32)
+    want = np.zeros(P, np.uint32)
+    want[bad_p] = reasons
+    assert np.array_equal(got, want), (got.tolist(), want.tolist())
+
+
+def test_mask_check_passes_the_steps_masks(S):
+    """Masks written by the step and by mask_topk pass the check, and a
+    mask_topk call without a threshold record is checked without one."""
+    cfg = W.flat_config("chk", 3 * 20_000, 3, 2, "0.99", steps=3)
+    opt = S.ScapeOptimizer(dev(W.init_params(cfg)), cfg.P, cfg.K, cfg.k)
+    for t in range(1, 4):
+        opt.step(dev(W.grads(cfg, t)))
+        opt.check("next")
+        opt.check("current")
+        assert torch.all(S.mask_slot_meta(opt.d, opt.k, opt.mask, t & 1)[2 * cfg.P:] == 0)
+    d = opt.d
+    blob = torch.zeros(S.mask_bytes(d, cfg.k), dtype=torch.uint8, device=DEV)
+    mv = S.mask_slot(d, cfg.k, blob, 1)
+    mv.meta = None
+    S.mask_topk(d, cfg.k, dev(W.grads(cfg, 9)[0]), mv, opt.ws)
+    S.mask_check(d, cfg.k, mv)

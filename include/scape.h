@@ -215,6 +215,27 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
                         int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * scape_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments minus the
+ * workspace, same results bit for bit.  The scratch is a static device
+ * array inside the library: scape_step_noalloc_max_bytes() bytes (64 MiB)
+ * per device, held from the library's first use on that device until the
+ * process ends; its address is looked up on the first call on each device
+ * (`stream` must belong to the current device).  Dims whose workspace
+ * (scape_workspace_bytes) exceeds it are rejected with SCAPE_EWORKSPACE
+ * before anything is enqueued.  The call allocates nothing; its scratch
+ * needs no clearing between calls (the step initialises what it reads).
+ * Every call on a device shares that device's scratch: calls that overlap
+ * on one device (several streams or host threads) race and must not be
+ * issued.  Stage timing records nothing for these calls.
+ */
+size_t scape_step_noalloc_max_bytes(void);
+scape_status scape_step_noalloc(const scape_dims* dims, float* params, const float* grads, float* m,
+                                float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
+                                int64_t step, hipStream_t stream);
+
+/*
  * Bias-correction state of the graph-capturable step, in DEVICE memory
  * (8-byte aligned): beta1_pow = beta1^t and beta2_pow = beta2^t after t
  * steps, as binary64 products of binary64(beta) taken one step at a time

@@ -401,7 +401,7 @@ struct StepCtx {
 scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const float* grads, float* m,
                         float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
                         int64_t step, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                        scape_bias_state* bias = nullptr, int cur_slot = 0) {
+                        scape_bias_state* bias = nullptr, int cur_slot = 0, bool timing = true) {
   scape_status st = check_dims(dims, k, &c.g);
   if (st) return st;
   const Geom& g = c.g;
@@ -414,7 +414,7 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
   if (workspace_bytes < g.ws_total)
     return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
 
-  c.prof = g_prof.on && !bias;
+  c.prof = g_prof.on && !bias && timing;
   c.w = ws_view(g, workspace);
   const int cs = bias ? cur_slot : (int)((step - 1) & 1);
   c.cur = slot_view(g, mask_blob, cs);
@@ -513,6 +513,31 @@ scape_status offload_events(OffloadEvents** out) {
   return SCAPE_OK;
 }
 
+// Scratch of scape_step_noalloc: a file-scope device array, one copy per
+// device, held until the process ends.  Host code never passes `scratch`
+// itself (a host-side stand-in for the symbol) to a kernel: each device's
+// address is looked up once, with that device current, and kept.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_lock;
+
+scape_status static_scratch(void** out) {
+  int dev = -1;
+  scape_status st = hip_check(hipGetDevice(&dev), "static scratch device");
+  if (st) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(SCAPE_EHIP, "static scratch: device %d out of range", dev);
+  std::lock_guard<std::mutex> hold(g_scratch_lock);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((st = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "static scratch address"))) return st;
+    if (!ptr) return fail(SCAPE_EHIP, "static scratch address: null on device %d", dev);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SCAPE_OK;
+}
+
 int64_t chunk_parts_of(const Geom& g, int32_t chunk_parts) {
   return chunk_parts < 1 ? 0 : (chunk_parts > g.P ? g.P : chunk_parts);
 }
@@ -528,6 +553,31 @@ scape_status scape_step(const scape_dims* dims, float* params, const float* grad
   scape_status st = step_begin(c, dims, params, grads, m, v, e, mask_blob, k, betas, lr, step, workspace,
                                workspace_bytes, stream);
   if (st) return st;
+  const bool vec = c.vec && aligned16(params) && aligned16(v);
+  const bool seg = vec && seg_ok(c.g, params, m, v);
+  if ((st = hip_check(launch_step_passes(c.g, c.sa, vec, seg, stream), "step pass"))) return st;
+  return step_end(c, stream);
+}
+
+size_t scape_step_noalloc_max_bytes(void) { return kStaticScratchBytes; }
+
+scape_status scape_step_noalloc(const scape_dims* dims, float* params, const float* grads, float* m,
+                                float* v, float* e, void* mask_blob, int64_t k, scape_betas betas, float lr,
+                                int64_t step, hipStream_t stream) {
+  Geom g;
+  scape_status st = check_dims(dims, k, &g);
+  if (st) return st;
+  if (g.ws_total > kStaticScratchBytes)
+    return fail(SCAPE_EWORKSPACE,
+                "scape_step_noalloc: n=%lld P=%d K=%d k=%lld needs %zu bytes of scratch, more than the %zu bytes "
+                "of static scratch; call scape_step with a workspace",
+                (long long)g.n, g.P, g.K, (long long)g.k, g.ws_total, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws))) return st;
+  StepCtx c;
+  if ((st = step_begin(c, dims, params, grads, m, v, e, mask_blob, k, betas, lr, step, ws, g.ws_total, stream,
+                       nullptr, 0, false)))
+    return st;
   const bool vec = c.vec && aligned16(params) && aligned16(v);
   const bool seg = vec && seg_ok(c.g, params, m, v);
   if ((st = hip_check(launch_step_passes(c.g, c.sa, vec, seg, stream), "step pass"))) return st;

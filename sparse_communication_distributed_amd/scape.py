@@ -60,6 +60,9 @@ _SIGS = {
                                    MaskView, Betas, c_float, c_int64, c_void_p]),
     "scape_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p]),
+    "scape_step_noalloc_max_bytes": (c_size_t, []),
+    "scape_step_noalloc": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_int64, Betas, c_float, c_int64, c_void_p]),
     "scape_bias_state_at": (c_int, [Betas, c_int64, ctypes.POINTER(BiasState)]),
     "scape_step_graph": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_int64, Betas, c_float, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -255,6 +258,20 @@ def step(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: floa
     _check(lib().scape_step(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
                             _ptr(mask_blob), k, bt, lr, step_no, _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def step_noalloc_max_bytes() -> int:
+    return int(lib().scape_step_noalloc_max_bytes())
+
+
+def step_noalloc(d: Dims, params, grads, m, v, e, mask_blob, k: int, bt: Betas, lr: float, step_no: int,
+                 stream=None) -> None:
+    """scape_step_noalloc: scape_step with the library's static device
+    scratch in place of a workspace (allocates nothing)."""
+    _need_state(d, params, m, v, grads, e)
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _check(lib().scape_step_noalloc(ctypes.byref(d), _ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(e),
+                                    _ptr(mask_blob), k, bt, lr, step_no, _stream(stream)))
 
 
 def bias_state_at(bt: Betas, steps_done: int) -> BiasState:

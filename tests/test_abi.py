@@ -272,3 +272,23 @@ def test_optimizer_step_count_unchanged_by_a_rejected_call():
     with pytest.raises(ValueError, match="device tensor"):
         opt.step(torch.zeros((2, 4096)))
     assert opt.t == 0
+
+
+def test_step_noalloc_rejects_dims_beyond_its_static_scratch():
+    """scape_step_noalloc refuses, before any HIP call, dims whose workspace
+    exceeds the static scratch, and names both sizes; dims that fit pass
+    that check (they then need a device, so are not called here)."""
+    L = S.lib()
+    cap = S.step_noalloc_max_bytes()
+    assert cap == 64 << 20
+    big = S.dims(1 << 24, 4, 2)  # candidate slots alone: 8 bytes per element
+    assert S.workspace_bytes(big, 1000) > cap
+    st = L.scape_step_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, S.betas(), 1e-3, 1, None)
+    assert st == 3
+    msg = L.scape_last_error().decode()
+    assert "static scratch" in msg and str(cap) in msg
+    assert S.workspace_bytes(S.dims(4 * 60_000, 4, 3), 600) < cap
+    # argument checks come first, as in scape_step
+    assert L.scape_step_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, S.betas(), 1e-3, 1, None) == 1
+    assert L.scape_step_noalloc(ctypes.byref(S.dims(100, 3, 1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                S.betas(), 1e-3, 1, None) == 2

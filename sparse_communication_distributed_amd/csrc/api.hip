@@ -69,6 +69,8 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   r.ws_cnt2 = o;    o = align256(o + (size_t)P * r.tpp * 4);
   r.ws_state = o;   o = align256(o + (size_t)P * sizeof(PartSel));
   r.ws_tilecnt = o; o = align256(o + (size_t)P * r.tpp * 4);
+  r.ws_surv = o;    o = align256(o + (size_t)P * kSurvivorCap * 8);
+  r.ws_nsurv = o;   o = align256(o + (size_t)P * 4);
   r.ws_total = o;
   *g = r;
   return true;
@@ -182,6 +184,8 @@ Ws ws_view(const Geom& g, void* ws) {
   w.sel.cnt2 = reinterpret_cast<uint32_t*>(c + g.ws_cnt2);
   w.sel.state = reinterpret_cast<PartSel*>(c + g.ws_state);
   w.sel.tilecnt = reinterpret_cast<uint32_t*>(c + g.ws_tilecnt);
+  w.sel.surv = reinterpret_cast<uint64_t*>(c + g.ws_surv);
+  w.sel.nsurv = reinterpret_cast<uint32_t*>(c + g.ws_nsurv);
   return w;
 }
 

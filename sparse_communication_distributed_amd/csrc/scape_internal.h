@@ -25,8 +25,10 @@ constexpr int kL1Shift = 19;
 // Target number of blocks of the statistic passes (the bootstrap, and the
 // fallback, which usually has nothing to do and should cost little).
 constexpr int kStatBlocks = 8192;
-// Tiles each wave of the passes over candidate slots walks.
+// Tiles each wave of the passes over candidate slots walks, at most; fewer
+// where the layout has fewer than kSelectWaves * kSelectTilesPerWave tiles.
 constexpr int kSelectTilesPerWave = 8;
+constexpr int64_t kSelectWaves = 8192;
 constexpr int kThreads = 256;
 
 // Statistic sources and phases of stat_kernel.
@@ -36,8 +38,7 @@ constexpr int kSrcMasked = 2;  // b1*m + c1*a^o, a^o rebuilt from e' and b^o
 constexpr int kPhaseHist = 0;
 constexpr int kPhaseCapture = 1;
 
-// Modes of the level scan.
-constexpr int kScanLevel = 0;  // a later level, on candidates
+// Modes of the level-1 scan.
 constexpr int kScanCheck = 1;  // level 1 on captured keys; flags a fallback if fewer than k
 constexpr int kScanBound = 2;  // fallback: level 1 on all keys -> capture bound
 constexpr int kScanFinal = 3;  // fallback: level 1 on the recaptured keys
@@ -61,6 +62,8 @@ struct PartSel {
   uint32_t kth;      // smallest selected key (the k-th largest key)
   uint32_t c1;       // captured keys in the level-1 threshold bin
   uint32_t lo_next;  // capture bound proposed for the next step
+  uint32_t bin2;     // level-2 digit of the threshold (once level 2 is resolved)
+  uint32_t done2;    // 1: every candidate at the level-2 digit is selected
   uint32_t pad;
 };
 
@@ -72,6 +75,11 @@ constexpr double kCaptureMargin = 1.25;
 // kSampleStep-th tile, aiming at kSampleMargin * k keys above it.
 constexpr int kSampleStep = 16;
 constexpr double kSampleMargin = 1.5;
+// Candidates of the threshold bin that still match the prefix after level 2
+// (ties and near-ties at the threshold): at most this many are kept per
+// partition for the later levels; beyond it those levels walk the tile
+// slots again (exact, slower).
+constexpr int kSurvivorCap = 4096;
 
 struct Level {
   int shift;  // bit position of the digit in the composite
@@ -92,7 +100,7 @@ struct Geom {
   // mask slot: offsets inside one slot, slot size
   size_t off_bits, off_idx, off_toff, off_meta, slot_bytes;
   // workspace offsets and total
-  size_t ws_b, ws_mold, ws_hist, ws_cand, ws_cnt1, ws_cnt2, ws_state, ws_tilecnt, ws_total;
+  size_t ws_b, ws_mold, ws_hist, ws_cand, ws_cnt1, ws_cnt2, ws_state, ws_tilecnt, ws_surv, ws_nsurv, ws_total;
 };
 
 // Returns false if dims/k are outside the limits.
@@ -123,7 +131,9 @@ struct SelectBufs {
   uint32_t* cnt1;
   uint32_t* cnt2;
   PartSel* state;
-  uint32_t* tilecnt;
+  uint32_t* tilecnt;  // [P][tiles] selected elements per tile
+  uint64_t* surv;     // [P][kSurvivorCap] candidates at the level-2 threshold digit
+  uint32_t* nsurv;    // [P] their counts
 };
 
 // ---- launch wrappers (each returns hipGetLastError() of its launches) ----
@@ -168,8 +178,12 @@ hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
 // target 0: the capture target of a step (kCaptureMargin * k)
 hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target = 0);
 // From level-1 digits to the mask: candidate select pass (writes every mask
-// word), the later levels, marking, tile counts, offsets, index list and the
-// slot's threshold record.
+// word, counts each tile's selection, compacts the threshold bin's
+// candidates), level 2, a pass over the bin's candidates (tile counts, the
+// next histogram, the few candidates left at the threshold digit), the
+// later levels and the tile offsets, and the emission (the bin's selected
+// candidates ORed into the words, the index list), plus the slot's
+// threshold record.
 hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits, uint32_t* idx,
                               uint32_t* tile_off, uint32_t* meta_out, hipStream_t s,
                               void (*mark)(void*, int), void* mark_ctx);

@@ -11,12 +11,15 @@
 // at least k keys, its top k lie among the captures; otherwise an exact
 // fallback recounts all its keys to find the level-1 digit and recaptures
 // from there.  A first capture, with no previous bound, takes its bound
-// from a histogram of a sample of tiles (kScanSample).  The candidate select pass then reads only the captures:
-// digits above the threshold digit are selected and written as whole mask
-// words, the threshold digit's captures are compacted in place and
-// histogrammed on the next digit.  The remaining levels (key bits 6..0, then
-// the index bits) run on those few; marking sets their bits; emission turns
-// the words into the ascending index list and per-tile offsets.
+// from a histogram of a sample of tiles (kScanSample).  The candidate
+// select pass then reads only the captures: digits above the threshold
+// digit are selected and written as whole mask words, the threshold
+// digit's captures are compacted in place and histogrammed on the level-2
+// digit (key bits 18..7).  One block per partition then resolves the
+// remaining levels (key bits 6..0, then the index bits) on those few.  The
+// emission marks the threshold bin's selected candidates, turns the words
+// into per-tile offsets (a single-pass scan with decoupled lookback) and
+// writes the ascending index list.
 #include "scape_internal.h"
 
 namespace scape {
@@ -52,7 +55,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, 
 __device__ __forceinline__ PartSel fresh_sel(uint32_t k) {
   PartSel s;
   s.prefix = 0; s.mask = 0; s.r = k; s.done = 0; s.bin1 = 0; s.fault = 0; s.fb = 0; s.lo_fb = 0;
-  s.kth = 0xffffffffu; s.c1 = 0; s.lo_next = 0; s.pad = 0;
+  s.kth = 0xffffffffu; s.c1 = 0; s.lo_next = 0; s.bin2 = 0; s.done2 = 0; s.pad = 0;
   return s;
 }
 
@@ -82,47 +85,39 @@ __global__ void init_state_kernel(PartSel* state, int P, uint32_t k) {
   }
 }
 
-// One level of the threshold search for partition blockIdx.x: find the
-// digit d (scanning from the largest) whose bin holds the r-th largest
-// composite among those matching the current prefix, and narrow the prefix.
-// Level-1 modes start from r = k and an empty prefix (see kScan*).  Always
-// leaves the partition's bins zeroed.
+// Level 1 of the threshold search for partition blockIdx.x, on the level-1
+// histogram (key bits 30..19; see kScan* for the modes): find the digit
+// (scanning from the largest) whose bin holds the k-th largest key, and
+// record the capture bound of the next step (the digit at which the count
+// from the top reaches `target`).  Always leaves the partition's bins
+// zeroed.
 __global__ void __launch_bounds__(kThreads)
-level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, int shift,
-                  int nbits, int mode, uint32_t target) {
+level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, int mode, uint32_t target) {
   __shared__ uint32_t wtot[kThreads / 64];
   __shared__ int found;
   __shared__ uint32_t s_lo;
   __shared__ int s_dmin;
   const int p = blockIdx.x;
   uint32_t* h = hist + (int64_t)p * kBins;
-  const int nb = 1 << nbits;
+  constexpr int nb = kBins;
+  constexpr int shift = 32 + kL1Shift;
   const PartSel cur = state[p];
-  bool active;
-  if (mode == kScanCheck) active = true;
-  else if (mode == kScanLevel) active = !cur.done && !cur.fb;
-  else active = cur.fb != 0;  // kScanBound, kScanFinal, kScanSample
-  const bool first = mode != kScanLevel;
-  const PartSel st = first ? fresh_sel((uint32_t)g.k) : cur;
+  const bool active = (mode == kScanCheck) || cur.fb != 0;  // the other modes: fallback partitions only
+  const PartSel st = fresh_sel((uint32_t)g.k);
+  constexpr int per = (nb + kThreads - 1) / kThreads;
   if (active && mode == kScanSample) {
     // The bound for a first capture: the digit at which the count of the
     // sampled keys from the top reaches `target` (scaled to the sample), or
     // 0 (capture every key) if the sample holds fewer.
-    const int per = (nb + kThreads - 1) / kThreads;
     uint32_t s = 0;
-    for (int q = 0; q < per; ++q) {
-      const int pos = threadIdx.x * per + q;
-      if (pos < nb) s += h[nb - 1 - pos];
-    }
+    for (int q = 0; q < per; ++q) s += h[nb - 1 - (threadIdx.x * per + q)];
     uint32_t tot;
     const uint32_t above = block_excl_scan(s, wtot, &tot);
     if (threadIdx.x == 0 && tot < target) state[p].lo_fb = 0u;
     if (tot >= target && above < target && target <= above + s) {
       uint32_t acc = above;
       for (int q = 0; q < per; ++q) {
-        const int pos = threadIdx.x * per + q;
-        if (pos >= nb) break;
-        const int d = nb - 1 - pos;
+        const int d = nb - 1 - (threadIdx.x * per + q);
         acc += h[d];
         if (acc >= target) {
           state[p].lo_fb = (uint32_t)d << kL1Shift;
@@ -131,13 +126,9 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
       }
     }
   } else if (active) {
-    const int per = (nb + kThreads - 1) / kThreads;
     // thread t owns descending positions [t*per, (t+1)*per): bin = nb-1-pos
     uint32_t s = 0;
-    for (int q = 0; q < per; ++q) {
-      const int pos = threadIdx.x * per + q;
-      if (pos < nb) s += h[nb - 1 - pos];
-    }
+    for (int q = 0; q < per; ++q) s += h[nb - 1 - (threadIdx.x * per + q)];
     uint32_t tot;
     const uint32_t above = block_excl_scan(s, wtot, &tot);
     if (threadIdx.x == 0) {
@@ -147,36 +138,26 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
     }
     __syncthreads();
     // Capture bound for the next step: the digit at which the count of keys
-    // from the top reaches `need` (level 1: target; level 2: the part of the
-    // target that falls inside the threshold bin).
-    const bool bound_l1 = (mode == kScanCheck || mode == kScanFinal);
-    const bool bound_l2 = (mode == kScanLevel && shift == g.levels[0].shift);
-    int64_t need = -1;
-    if (bound_l1) need = (tot >= target) ? (int64_t)target : -2;
-    if (bound_l2) {
-      const int64_t above_bin = (int64_t)g.k - (int64_t)cur.r;  // selected above the threshold bin
-      const int64_t in_bin = (int64_t)target - above_bin;
-      if (in_bin > 0 && in_bin <= (int64_t)tot) need = in_bin;
-    }
+    // from the top reaches the target.
+    const bool bound = (mode == kScanCheck || mode == kScanFinal);
+    const int64_t need = bound ? ((tot >= target) ? (int64_t)target : -2) : -1;
     if (need >= 1 && above < (uint64_t)need && (uint64_t)need <= (uint64_t)above + s) {
       uint32_t acc = above;
       for (int q = 0; q < per; ++q) {
-        const int pos = threadIdx.x * per + q;
-        if (pos >= nb) break;
-        const int d = nb - 1 - pos;
+        const int d = nb - 1 - (threadIdx.x * per + q);
         acc += h[d];
         if (acc >= (uint32_t)need) {
-          s_lo = (uint32_t)(((st.prefix & ~(((1ull << nbits) - 1ull) << shift)) | ((uint64_t)d << shift)) >> 32);
+          s_lo = (uint32_t)d << kL1Shift;
           break;
         }
       }
     }
-    if (bound_l1 && need == -2) {
+    if (need == -2) {
       // fewer keys than the target were captured: one bin below the lowest
       // captured digit
       for (int q = per - 1; q >= 0; --q) {
         const int pos = threadIdx.x * per + q;
-        if (pos < nb && h[nb - 1 - pos]) {
+        if (h[nb - 1 - pos]) {
           atomicMin(&s_dmin, nb - 1 - pos);
           break;
         }
@@ -195,9 +176,7 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
     } else if (above < st.r && st.r <= above + s) {
       uint32_t acc = above;
       for (int q = 0; q < per; ++q) {
-        const int pos = threadIdx.x * per + q;
-        if (pos >= nb) break;
-        const int d = nb - 1 - pos;
+        const int d = nb - 1 - (threadIdx.x * per + q);
         const uint32_t c = h[d];
         if (acc + c >= st.r) {
           if (mode == kScanBound) {
@@ -207,15 +186,11 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
           } else {
             PartSel o = st;
             o.r = st.r - acc;
-            o.prefix = st.prefix | ((uint64_t)d << shift);
-            uint64_t dm = ((1ull << nbits) - 1ull) << shift;
-            if (first) dm |= (1ull << 63);  // bit 63 of every composite is zero
-            o.mask = st.mask | dm;
+            o.prefix = (uint64_t)d << shift;
+            o.mask = ((uint64_t)(nb - 1) << shift) | (1ull << 63);  // bit 63 of every composite is zero
             o.done = (c == o.r) ? 1u : 0u;
-            if (first) {
-              o.bin1 = (uint32_t)d;
-              o.c1 = c;
-            }
+            o.bin1 = (uint32_t)d;
+            o.c1 = c;
             o.fb = 0;
             state[p] = o;
           }
@@ -234,11 +209,7 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
       state[p] = o;
     }
     __syncthreads();
-    // record the bound (level 1 sets it; level 2 may raise it inside the bin)
-    if (threadIdx.x == 0 && (bound_l1 || bound_l2) && mode != kScanBound) {
-      if (bound_l1) state[p].lo_next = (s_lo == 0xffffffffu) ? 0u : s_lo;
-      else if (s_lo != 0xffffffffu && s_lo > state[p].lo_next) state[p].lo_next = s_lo;
-    }
+    if (threadIdx.x == 0 && bound) state[p].lo_next = (s_lo == 0xffffffffu) ? 0u : s_lo;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0u;
@@ -258,9 +229,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // One wave per tile: reads the tile's captured candidates in rounds of
 // kCandChunks chunks of 64; selects the digits above the level-1 threshold
 // digit into the tile's 64 mask words (written whole, so every word of the
-// partition is written); compacts the threshold digit's candidates in
-// place, in order (a write position never passes the candidates already
-// read), and histograms their level-2 digit.
+// partition is written) and counts them; compacts the threshold digit's
+// candidates in place, in order (a write position never passes the
+// candidates already read), and histograms their level-2 digit.
 __global__ void __launch_bounds__(kThreads)
 cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ cand,
                    const uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2,
@@ -371,8 +342,7 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   if (done) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
 
-// The compacted candidate lists are walked one wave per tile (each wave
-// takes tiles wave_id, wave_id + nwaves, ...).
+// The compacted candidate lists are walked one wave per tile.
 // Candidates 0 .. ct-1 of a slot, read by the wave in rounds of
 // kCandChunks chunks of 64 (all loaded before any is used); f(c) runs on
 // the lanes that hold a candidate.
@@ -392,8 +362,10 @@ __device__ __forceinline__ void for_each_cand(const uint64_t* __restrict__ slot,
   }
 }
 
-// The counts are loaded 64 tiles at a time (lane i: the batch's i-th tile)
-// and only tiles with candidates are visited, in ascending order.
+// The tiles of partition p with compacted candidates, one wave per tile
+// (each wave takes tiles wave_id, wave_id + nwaves, ...): the counts are
+// loaded 64 tiles at a time (lane i: the batch's i-th tile) and only tiles
+// with candidates are visited, in ascending order.
 template <typename F>
 __device__ __forceinline__ void for_each_tile(const Geom& g, int p, const uint32_t* __restrict__ cnt2,
                                               F&& f) {
@@ -413,120 +385,401 @@ __device__ __forceinline__ void for_each_tile(const Geom& g, int p, const uint32
   }
 }
 
-// Histogram of one digit over the compacted candidates matching the prefix.
+// ---- the threshold search inside the level-1 threshold bin ----
+// One block of kResolveThreads per partition.
+constexpr int kResolveThreads = 1024;
+constexpr int kResolveWaves = kResolveThreads / 64;
+
+// Exclusive scan over a block of kResolveThreads; `wtot` is LDS [waves].
+__device__ __forceinline__ uint32_t resolve_excl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if ((int)lane >= d) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kResolveWaves; ++w) {
+    if (w < (int)wave) off += wtot[w];
+    tot += wtot[w];
+  }
+  *total = tot;
+  return off + x - v;
+}
+
+struct DigitFind {
+  int d;           // digit holding the rank, -1 if none
+  uint32_t c;      // its count
+  uint32_t above;  // count above it
+  uint32_t tot;    // count of all bins
+};
+
+// In bins h[0 .. nb) scanned from the largest digit, the digit in which the
+// cumulative count first reaches `rank` (1-based).  Block-wide; every
+// thread gets the result.
+__device__ DigitFind find_digit(const uint32_t* h, int nb, uint32_t rank, uint32_t* wtot, DigitFind* out) {
+  const int per = (nb + kResolveThreads - 1) / kResolveThreads;
+  uint32_t s = 0;
+  for (int q = 0; q < per; ++q) {
+    const int pos = threadIdx.x * per + q;
+    if (pos < nb) s += h[nb - 1 - pos];
+  }
+  uint32_t tot;
+  const uint32_t above = resolve_excl_scan(s, wtot, &tot);
+  if (threadIdx.x == 0) *out = DigitFind{-1, 0u, 0u, tot};
+  __syncthreads();
+  if (rank >= 1 && above < rank && rank <= above + s) {
+    uint32_t acc = above;
+    for (int q = 0; q < per; ++q) {
+      const int pos = threadIdx.x * per + q;
+      if (pos >= nb) break;
+      const int d = nb - 1 - pos;
+      const uint32_t c = h[d];
+      if (acc + c >= rank) {
+        *out = DigitFind{d, c, acc, tot};
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  const DigitFind r = *out;
+  __syncthreads();
+  return r;
+}
+
+// The threshold bin's candidates of partition p (compacted in place in the
+// tile slots), walked by the block's waves.  A wave takes 64 tiles at a
+// time (wave w: tiles w, w + W, ..., W waves), scans their counts and walks
+// the 64 slots as one flattened sequence: lane i takes entries i, i + 64,
+// ... and finds its tile by a binary search over the 64 prefixes in LDS, so
+// kWalkBatch loads per lane are in flight at once whatever the tiles' sizes.
+// f(c, j) runs for each candidate c of the batch's tile j; after a batch,
+// end(t, j) runs on the lane of each tile t with candidates (j = the lane).
+constexpr int kWalkBatch = 8;
+template <typename F, typename E>
+__device__ __forceinline__ void walk_bin(const Geom& g, int p, const uint64_t* __restrict__ cand,
+                                         const uint32_t* __restrict__ cnt2, uint32_t* spre, F&& f, E&& end) {
+  const int64_t nw = kResolveWaves;
+  const uint32_t lane = lane_id();
+  for (int64_t tb = threadIdx.x >> 6; tb < g.tpp; tb += 64 * nw) {
+    const int64_t tl = tb + (int64_t)lane * nw;
+    uint32_t ct = (tl < g.tpp) ? cnt2[(int64_t)p * g.tpp + tl] : 0u;
+    if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
+    uint32_t x = ct;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(x, d, 64);
+      if ((int)lane >= d) x += y;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
+    if (total == 0) continue;  // wave-uniform
+    spre[lane] = x - ct;
+    wave_lds_sync();
+    for (uint32_t i0 = 0; i0 < total; i0 += 64 * kWalkBatch) {
+      uint64_t cc[kWalkBatch];
+      uint32_t jj[kWalkBatch];
+#pragma unroll
+      for (int u = 0; u < kWalkBatch; ++u) {
+        const uint32_t i = i0 + 64 * u + lane;
+        uint32_t j = 0;
+#pragma unroll
+        for (uint32_t step = 32; step >= 1; step >>= 1)
+          if (spre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
+        jj[u] = j;
+        cc[u] = (i < total) ? cand[((int64_t)p * g.tpp + tb + (int64_t)j * nw) * kTile + (i - spre[j])] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kWalkBatch; ++u)
+        if (i0 + 64 * u + lane < total) f(cc[u], jj[u]);
+    }
+    wave_lds_sync();
+    if (ct) end(tl, lane);
+    wave_lds_sync();
+  }
+}
+
+constexpr int kScanBatch = 16;
+
+// ---- the threshold search inside the level-1 bin, and the tile offsets ----
+// Level 2 (key bits 18..7) for partition blockIdx.x, on the histogram of
+// the threshold bin's candidates that the candidate select pass built:
+// the digit holding the remaining rank narrows the prefix (the search is
+// done when that digit's candidates are exactly the rank still needed),
+// and the next step's capture bound is refined to the level-2 digit at
+// which the count from the top reaches the part of the target inside the
+// bin.  Leaves the partition's histogram bins zeroed and its survivor
+// count at zero.
 __global__ void __launch_bounds__(kThreads)
-cand_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
-                 const PartSel* __restrict__ state, uint32_t* __restrict__ hist, int shift, int nbits) {
-  __shared__ uint32_t sh[kBins];
+l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, uint32_t* __restrict__ nsurv,
+               uint32_t target) {
+  __shared__ uint32_t wtot[kThreads / 64];
+  __shared__ uint32_t s_d, s_c, s_above, s_lo;
+  const int p = blockIdx.x;
+  uint32_t* h = hist + (int64_t)p * kBins;
+  const PartSel cur = state[p];
+  if (threadIdx.x == 0) nsurv[p] = 0u;
+  if (!cur.done && !cur.fb) {
+    const int shift = g.levels[0].shift;
+    constexpr int nb = kBins, per = kBins / kThreads;
+    uint32_t s = 0;
+    for (int q = 0; q < per; ++q) s += h[nb - 1 - (threadIdx.x * per + q)];
+    uint32_t tot;
+    const uint32_t above = block_excl_scan(s, wtot, &tot);
+    if (threadIdx.x == 0) {
+      s_d = 0xffffffffu;
+      s_lo = 0xffffffffu;
+    }
+    __syncthreads();
+    const int64_t in_bin = (int64_t)target - ((int64_t)g.k - (int64_t)cur.r);
+    uint32_t acc = above;
+    for (int q = 0; q < per; ++q) {
+      const int d = nb - 1 - (threadIdx.x * per + q);
+      const uint32_t c = h[d];
+      if (acc < cur.r && acc + c >= cur.r) {
+        s_d = (uint32_t)d;
+        s_c = c;
+        s_above = acc;
+      }
+      if (in_bin > 0 && in_bin <= (int64_t)tot && (int64_t)acc < in_bin && (int64_t)(acc + c) >= in_bin)
+        s_lo = (uint32_t)d;
+      acc += c;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      PartSel o = cur;
+      const uint64_t dmask = (uint64_t)(kBins - 1) << shift;
+      if (s_lo != 0xffffffffu) {
+        const uint32_t lo = (uint32_t)(((cur.prefix & ~dmask) | ((uint64_t)s_lo << shift)) >> 32);
+        if (lo > o.lo_next) o.lo_next = lo;
+      }
+      if (s_d == 0xffffffffu) {  // the rank lies in no bin: corrupted input
+        o.fault |= 1u;
+        o.done = 1;
+      } else {
+        o.r = cur.r - s_above;
+        o.prefix = cur.prefix | ((uint64_t)s_d << shift);
+        o.mask = cur.mask | dmask;
+        o.bin2 = s_d;
+        o.done2 = (s_c == o.r) ? 1u : 0u;
+      }
+      state[p] = o;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
+}
+
+// One wave per tile over the threshold bin's compacted candidates, after
+// level 2: adds to the tile's count the candidates above the level-2
+// threshold digit (and those at it, when that digit decides the search);
+// when it does not, histograms the level-3 digit (key bits 6..0) of the
+// candidates at it and appends them to the partition's survivor list (at
+// most kSurvivorCap kept; the count goes on).  When the level-2 digit
+// decides, the smallest key at it is folded into the state's k-th key.
+__global__ void __launch_bounds__(kThreads)
+bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict__ cand,
+                const uint32_t* __restrict__ cnt2, uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ hist,
+                uint64_t* __restrict__ surv, uint32_t* __restrict__ nsurv) {
+  __shared__ uint32_t sh[1 << (kL1Shift - kDigitBits)];
+  __shared__ uint32_t smin;
+  constexpr int nb3 = 1 << (kL1Shift - kDigitBits);
   const int p = blockIdx.y;
   const PartSel st = state[p];
-  if (st.done || st.fb) return;
-  const int nb = 1 << nbits;
-  for (int i = threadIdx.x; i < nb; i += kThreads) sh[i] = 0;
+  if (st.fb || !st.mask || st.done) return;  // block-uniform: nothing left in the bin to walk
+  const bool done2 = st.done2 != 0;
+  const int sh2 = g.levels[0].shift, sh3 = g.levels[1].shift;
+  const uint32_t d2 = st.bin2;
+  for (int i = threadIdx.x; i < nb3; i += kThreads) sh[i] = 0u;
+  if (threadIdx.x == 0) smin = 0xffffffffu;
   __syncthreads();
   const uint32_t lane = lane_id();
+  uint32_t kmin = 0xffffffffu;
+  uint64_t* sl = surv + (int64_t)p * kSurvivorCap;
+  uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
   for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
     const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-    for_each_cand(slot, ct, lane, [&](uint64_t c) {
-      if ((c & st.mask) == st.prefix) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
-    });
+    uint32_t add = 0;
+    for (uint32_t base = 0; base < ct; base += 64 * kCandChunks) {
+      uint64_t cc[kCandChunks];
+#pragma unroll
+      for (int u = 0; u < kCandChunks; ++u) {
+        const uint32_t i = base + 64 * u + lane;
+        cc[u] = (i < ct) ? slot[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kCandChunks; ++u) {
+        if (base + 64 * u >= ct) break;  // wave-uniform
+        const uint64_t c = cc[u];
+        const bool valid = base + 64 * u + lane < ct;
+        const uint32_t dd = (uint32_t)(c >> sh2) & (uint32_t)(kBins - 1);
+        const bool at = valid && dd == d2;
+        add += (valid && (dd > d2 || (done2 && at))) ? 1u : 0u;
+        if (at && done2) {
+          const uint32_t key = (uint32_t)(c >> 32);
+          kmin = key < kmin ? key : kmin;
+        }
+        const bool keep = at && !done2;
+        const uint64_t kb = __ballot(keep);
+        if (kb) {  // wave-uniform
+          uint32_t pos = 0;
+          if (lane == 0) pos = atomicAdd(nsurv + p, (uint32_t)__popcll(kb));
+          pos = (uint32_t)__shfl((int)pos, 0, 64) + mbcnt(kb);
+          if (keep) {
+            atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
+            if (pos < (uint32_t)kSurvivorCap) sl[pos] = c;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) add += __shfl_xor(add, dd, 64);
+    if (lane == 0 && add) tc[t] += add;  // this wave alone walks tile t here
   });
   __syncthreads();
   uint32_t* h = hist + (int64_t)p * kBins;
-  for (int i = threadIdx.x; i < nb; i += kThreads) {
+  for (int i = threadIdx.x; i < nb3; i += kThreads) {
     const uint32_t c = sh[i];
     if (c) atomicAdd(h + i, c);
   }
+  if (done2) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
 
-// Sets the bits of the compacted candidates at or above the threshold: the
-// wave of a tile assembles the tile's words in LDS and ORs each non-zero
-// word into the mask (it is the only writer of its tile's words here, so a
-// plain read-modify-write suffices), and adds their count to the tile's.
-__global__ void __launch_bounds__(kThreads)
-mark_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
-            PartSel* __restrict__ state, uint64_t* __restrict__ bits, uint32_t* __restrict__ tilecnt) {
-  __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
-  __shared__ uint32_t smin;
-  const int p = blockIdx.y;
-  const uint64_t T = state[p].prefix;
-  uint64_t* wb = bits + (int64_t)p * g.wpp;
-  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  unsigned long long* wd = words[wave];
-  uint32_t kmin = 0xffffffffu;
-  if (threadIdx.x == 0) smin = 0xffffffffu;
-  for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
-    const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-    const uint32_t tile_lo = (uint32_t)(t * kTile);
-    const int64_t w = t * kWordsPerTile + lane;
-    const uint64_t old = (w < g.wpp) ? wb[w] : 0ull;  // in flight while the candidates are read
-    wd[lane] = 0ull;
-    wave_lds_sync();
-    for_each_cand(slot, ct, lane, [&](uint64_t c) {
-      const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
-      if (c >= T && jl < (uint32_t)kTile) {
-        atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
-        const uint32_t key = (uint32_t)(c >> 32);
-        kmin = key < kmin ? key : kmin;
-      }
-    });
-    wave_lds_sync();
-    const unsigned long long word = wd[lane];
-    if (word && w < g.wpp) wb[w] = old | word;
-    // these elements were not selected by the candidate select pass, so the
-    // tile's count grows by exactly their number
-    uint32_t pc = (uint32_t)__popcll(word);
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
-    if (lane == 0 && pc) tilecnt[(int64_t)p * g.tpp + t] += pc;
-    wave_lds_sync();
-  });
-  __syncthreads();
-  block_min_into(kmin, &smin, &state[p].kth);
-}
-
-// Exclusive scan of the tile counts of partition blockIdx.x -> tile_off;
-// then the slot's threshold record: the k-th key and the capture bound
-// proposed by the level scans for the next step.
-__global__ void __launch_bounds__(kThreads)
-scan_tiles_kernel(Geom g, const uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ tile_off,
-                  PartSel* __restrict__ state, uint32_t* __restrict__ meta_out) {
-  __shared__ uint32_t wtot[kThreads / 64];
+// The remaining levels for partition blockIdx.x (after level 2: key bits
+// 6..0 from the walk's histogram, then the index bits) on the survivors, or
+// by walks over the tile slots when the survivors overflowed their list;
+// then the tile counts of the selected survivors (composite >= T), and the
+// exclusive scan of the partition's tile counts into tile_off.  Writes the
+// partition's search state and the slot's threshold record (k-th key, next
+// capture bound, fault word: bit 1 if the total is not k), and leaves the
+// partition's histogram bins zeroed.
+__global__ void __launch_bounds__(kResolveThreads)
+finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
+              const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
+              const uint64_t* __restrict__ surv, const uint32_t* __restrict__ nsurv,
+              uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ tile_off, uint32_t* __restrict__ meta_out) {
+  __shared__ uint32_t sh[kBins];
+  __shared__ unsigned long long ls[kSurvivorCap];
+  __shared__ uint32_t wtot[kResolveWaves];
+  __shared__ uint32_t spre[kResolveWaves][65];
+  __shared__ uint32_t scnt[kResolveWaves][64];
+  __shared__ DigitFind sfind;
   const int p = blockIdx.x;
-  const int64_t per = (g.tpp + kThreads - 1) / kThreads;
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
+  PartSel st = state[p];
+  if (lane == 0) spre[wave][64] = 0xffffffffu;  // above every index: ends the binary search
+  scnt[wave][lane] = 0u;
+  if (!st.done && !st.fb && st.mask && !st.done2) {
+    const uint32_t ns = nsurv[p];
+    const bool kept = ns <= (uint32_t)kSurvivorCap;
+    for (uint32_t i = threadIdx.x; kept && i < ns; i += kResolveThreads) ls[i] = surv[(int64_t)p * kSurvivorCap + i];
+    uint32_t* gh = hist + (int64_t)p * kBins;
+    const int nb3 = 1 << g.levels[1].nbits;
+    for (int i = threadIdx.x; i < nb3; i += kResolveThreads) {
+      sh[i] = gh[i];
+      gh[i] = 0u;
+    }
+    __syncthreads();
+    for (int l = 1; l < g.nlevels; ++l) {
+      const int shift = g.levels[l].shift, nb = 1 << g.levels[l].nbits;
+      const uint64_t dmask = (uint64_t)(nb - 1) << shift;
+      if (l > 1) {
+        for (int i = threadIdx.x; i < nb; i += kResolveThreads) sh[i] = 0u;
+        __syncthreads();
+        const uint64_t pm = st.mask, pv = st.prefix;
+        if (kept) {
+          for (uint32_t i = threadIdx.x; i < ns; i += kResolveThreads) {
+            const uint64_t c = ls[i];
+            if ((c & pm) == pv) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+          }
+        } else {
+          walk_bin(g, p, cand, cnt2, spre[wave],
+                   [&](uint64_t c, uint32_t) {
+                     if ((c & pm) == pv) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+                   },
+                   [&](int64_t, uint32_t) {});
+        }
+        __syncthreads();
+      }
+      const DigitFind f = find_digit(sh, nb, st.r, wtot, &sfind);
+      if (f.d < 0) {  // corrupted input
+        st.fault |= 1u;
+        break;
+      }
+      st.r -= f.above;
+      st.prefix |= (uint64_t)f.d << shift;
+      st.mask |= dmask;
+      if (f.c == st.r) break;  // every composite matching the prefix is selected
+      __syncthreads();
+    }
+    st.kth = (uint32_t)(st.prefix >> 32);  // both key levels are resolved here
+    // tile counts of the selected candidates at the level-2 digit
+    const uint64_t T = st.prefix;
+    const uint32_t d2 = st.bin2;
+    const int sh2 = g.levels[0].shift;
+    if (kept) {
+      for (uint32_t i = threadIdx.x; i < ns; i += kResolveThreads) {
+        const uint64_t c = ls[i];
+        const uint32_t jl = g.idx_mask - (uint32_t)c;
+        if (c >= T && jl < (uint32_t)g.n_p) atomicAdd(tc + jl / kTile, 1u);
+      }
+    } else {
+      walk_bin(g, p, cand, cnt2, spre[wave],
+               [&](uint64_t c, uint32_t j) {
+                 if (((uint32_t)(c >> sh2) & (uint32_t)(kBins - 1)) == d2 && c >= T) atomicAdd(&scnt[wave][j], 1u);
+               },
+               [&](int64_t t, uint32_t j) {
+                 const uint32_t add = scnt[wave][j];
+                 if (add) atomicAdd(tc + t, add);
+                 scnt[wave][j] = 0u;
+               });
+    }
+  }
+  st.done = 1;
+  __syncthreads();
+  // ---- tile offsets: each thread sums a contiguous run of tile counts, the
+  // block scans the run sums, and each thread writes its run's offsets.  The
+  // counts may have been updated above by atomics, so they are read at
+  // device scope (not from a cache line another block of this CU loaded).
+  const int64_t per = (g.tpp + kResolveThreads - 1) / kResolveThreads;
   const int64_t lo = threadIdx.x * per;
   const int64_t hi = (lo + per < g.tpp) ? lo + per : g.tpp;
-  const uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
-  // a thread's counts are read in batches, all loads of a batch issued
-  // before any is used
-  constexpr int kBatch = 16;
   uint32_t s = 0;
-  for (int64_t t0 = lo; t0 < hi; t0 += kBatch) {
-    uint32_t x[kBatch];
+  for (int64_t t0 = lo; t0 < hi; t0 += kScanBatch) {
+    uint32_t x[kScanBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) x[u] = (t0 + u < hi) ? tc[t0 + u] : 0u;
+    for (int u = 0; u < kScanBatch; ++u)
+      x[u] = (t0 + u < hi) ? __hip_atomic_load(tc + t0 + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) s += x[u];
+    for (int u = 0; u < kScanBatch; ++u) s += x[u];
   }
   uint32_t tot;
-  uint32_t run = block_excl_scan(s, wtot, &tot);
+  uint32_t run = resolve_excl_scan(s, wtot, &tot);
   uint32_t* to = tile_off + (int64_t)p * g.tpp;
-  for (int64_t t0 = lo; t0 < hi; t0 += kBatch) {
-    uint32_t x[kBatch];
+  for (int64_t t0 = lo; t0 < hi; t0 += kScanBatch) {
+    uint32_t x[kScanBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) x[u] = (t0 + u < hi) ? tc[t0 + u] : 0u;
+    for (int u = 0; u < kScanBatch; ++u)
+      x[u] = (t0 + u < hi) ? __hip_atomic_load(tc + t0 + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < kScanBatch; ++u) {
       if (t0 + u < hi) to[t0 + u] = run;
       run += x[u];
     }
   }
   if (threadIdx.x == 0) {
-    if (tot != (uint32_t)g.k) state[p].fault |= 2u;
+    if (tot != (uint32_t)g.k) st.fault |= 2u;
+    state[p] = st;
     if (meta_out) {
-      meta_out[p] = state[p].kth;
-      meta_out[g.P + p] = state[p].lo_next;
-      meta_out[2 * g.P + p] = state[p].fault;
+      meta_out[p] = st.kth;
+      meta_out[g.P + p] = st.lo_next;
+      meta_out[2 * g.P + p] = st.fault;
     }
   }
 }
@@ -553,7 +806,11 @@ __device__ __forceinline__ uint32_t select_bit(uint64_t word, uint32_t r) {
   return pos;
 }
 
-// One wave per tile: write the tile's selected global indices in order.
+// One wave per tile: completes the tile's mask words and writes its global
+// indices in order.  The threshold bin's candidates of the tile at or above
+// T (the resolved threshold composite) are assembled in LDS and ORed into
+// the words (written back only where bits were added; this wave is the only
+// writer of its tile's words).  Then, with the tile's offset:
 // RANKS false (sparse masks): each lane walks the set bits of its own word.
 // RANKS true (denser masks, where a lane's word holds several indices): the
 // lanes take ranks r, r + 64, ... within the tile, so consecutive lanes
@@ -562,16 +819,40 @@ __device__ __forceinline__ uint32_t select_bit(uint64_t word, uint32_t r) {
 // tile's 64 prefixes in LDS), at that word's (r - prefix)-th set bit.
 template <bool RANKS>
 __global__ void __launch_bounds__(kThreads)
-write_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
-                 uint32_t* __restrict__ idx) {
-  __shared__ unsigned long long swords[RANKS ? kThreads / 64 : 1][kWordsPerTile];
+emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restrict__ cand,
+            const uint32_t* __restrict__ cnt2, uint64_t* __restrict__ bits,
+            const uint32_t* __restrict__ tile_off, uint32_t* __restrict__ idx) {
+  __shared__ unsigned long long swords[kThreads / 64][kWordsPerTile];
   __shared__ uint32_t spre[RANKS ? kThreads / 64 : 1][kWordsPerTile];
   const int p = blockIdx.y;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= g.tpp) return;  // wave-uniform; the waves synchronise only among their own lanes
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  unsigned long long* wd = swords[wave];
   const int64_t w = t * kWordsPerTile + lane;
-  uint64_t word = (w < g.wpp) ? bits[(int64_t)p * g.wpp + w] : 0ull;
+  uint64_t* wb = bits + (int64_t)p * g.wpp;
+  uint64_t word = (w < g.wpp) ? wb[w] : 0ull;
+  uint32_t ct = cnt2[(int64_t)p * g.tpp + t];
+  if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
+  const int64_t base = (int64_t)tile_off[(int64_t)p * g.tpp + t];
+  if (ct) {  // wave-uniform
+    const uint64_t T = state[p].prefix;
+    wd[lane] = 0ull;
+    wave_lds_sync();
+    const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    const uint32_t tile_lo = (uint32_t)(t * kTile);
+    for_each_cand(slot, ct, lane, [&](uint64_t c) {
+      const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
+      if (c >= T && jl < (uint32_t)kTile) atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+    });
+    wave_lds_sync();
+    const uint64_t add = wd[lane];
+    if (add && w < g.wpp) {
+      word |= add;
+      wb[w] = word;
+    }
+    wave_lds_sync();
+  }
   const uint32_t c = (uint32_t)__popcll(word);
   uint32_t x = c;
 #pragma unroll
@@ -579,7 +860,6 @@ write_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __re
     const uint32_t y = __shfl_up(x, d, 64);
     if ((int)lane >= d) x += y;
   }
-  const int64_t base = (int64_t)tile_off[(int64_t)p * g.tpp + t];
   uint32_t* out = idx + (int64_t)p * g.k;
   if (!RANKS) {
     int64_t pos = base + (x - c);
@@ -592,7 +872,7 @@ write_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __re
     return;
   }
   const uint32_t sw = RANKS ? wave : 0u;  // this wave's rows of the LDS arrays
-  swords[sw][lane] = word;
+  wd[lane] = word;
   spre[sw][lane] = x - c;
   const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
   wave_lds_sync();
@@ -602,7 +882,7 @@ write_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __re
 #pragma unroll
     for (uint32_t step = 32; step >= 1; step >>= 1)
       if (spre[sw][q + step] <= r) q += step;
-    const uint32_t j = select_bit(swords[sw][q], r - spre[sw][q]);
+    const uint32_t j = select_bit(wd[q], r - spre[sw][q]);
     if (base + r < g.k) out[base + r] = tbase + q * 64 + j;  // bound: malformed mask
   }
 }
@@ -708,35 +988,33 @@ hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s) {
 }
 
 hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target) {
-  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, 32 + kL1Shift, kDigitBits, mode,
-                                             target ? target : capture_target(g));
+  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, mode, target ? target : capture_target(g));
   return hipGetLastError();
 }
 
 hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits, uint32_t* idx,
                               uint32_t* tile_off, uint32_t* meta_out, hipStream_t s,
                               void (*mark)(void*, int), void* ctx) {
-  const unsigned sblocks = (unsigned)((g.tpp + 4 * kSelectTilesPerWave - 1) / (4 * kSelectTilesPerWave));
+  // tiles per wave of the passes over candidate slots: kSelectTilesPerWave
+  // on large layouts, fewer where that would leave too few waves
+  int64_t tpw = ((int64_t)g.P * g.tpp + kSelectWaves - 1) / kSelectWaves;
+  tpw = tpw < 1 ? 1 : (tpw > kSelectTilesPerWave ? kSelectTilesPerWave : tpw);
+  const unsigned sblocks = (unsigned)((g.tpp + 4 * tpw - 1) / (4 * tpw));
   cand_select_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits,
                                                               w.tilecnt);
   if (mark) mark(ctx, 1);
-  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[0].shift, g.levels[0].nbits,
-                                             kScanLevel, capture_target(g));
-  for (int l = 1; l < g.nlevels; ++l) {
-    cand_hist_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, w.hist,
-                                                             g.levels[l].shift, g.levels[l].nbits);
-    level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, g.levels[l].shift, g.levels[l].nbits,
-                                               kScanLevel, capture_target(g));
-  }
-  mark_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.cand, w.cnt2, w.state, bits, w.tilecnt);
+  l2_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, w.nsurv, capture_target(g));
+  bin_walk_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, w.tilecnt, w.hist, w.surv,
+                                                          w.nsurv);
+  finish_kernel<<<g.P, kResolveThreads, 0, s>>>(g, w.hist, w.state, w.cand, w.cnt2, w.surv, w.nsurv, w.tilecnt,
+                                                tile_off, meta_out);
   if (mark) mark(ctx, 2);
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
-  scan_tiles_kernel<<<g.P, kThreads, 0, s>>>(g, w.tilecnt, tile_off, w.state, meta_out);
   // rank-parallel emission pays from a mask density of about 5% on
   if (g.k * 20 >= g.n_p)
-    write_idx_kernel<true><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
+    emit_kernel<true><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
   else
-    write_idx_kernel<false><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, bits, tile_off, idx);
+    emit_kernel<false><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
   return hipGetLastError();
 }
 

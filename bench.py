@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 CPU_WAIT_S = 600.0  # bound on every wait of the CPU baseline
+# the other workloads measured after the headline one (each at most this many
+# timed and warmup steps)
+EXTRA_STEPS = 10
+EXTRA_WARMUP = 3
+CPU_SHARE = 16  # host cores per GPU on the benchmark host
 METRIC = "optimizer-step params/s + HBM GB/s (% peak), Llama-1.8B shape, 99% sparsity"
 
 
@@ -276,6 +281,225 @@ def graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, lr, steps_done,
     return {"ms_per_step": ms, "replays": steps, "steps_per_replay": 2}
 
 
+def counters_traffic(name, store_v):
+    """HBM bytes per step pass from the committed counter summary of this
+    workload, while it was taken from the step-pass code as it stands (the
+    summary carries a hash of that code); None otherwise."""
+    prof_path = os.path.join(ROOT, "profiles", f"step_pass_{name}_counters.json")
+    if store_v or not os.path.exists(prof_path):  # the counters come from the v-less step
+        return None
+    from sparse_communication_distributed_amd.prof_summary import step_pass_source_hash
+    with open(prof_path) as f:
+        doc = json.load(f)
+    if doc.get("source_hash") != step_pass_source_hash():
+        return None
+    return doc.get("hbm_bytes_per_step_pass")
+
+
+def measure_workload(S, W, torch, cfg, args, steps, warmup, full, log_fn):
+    """One workload on cuda:0: state and a pool of gradient sets generated on
+    the device, `warmup` untimed steps, `steps` timed steps between two
+    synchronisations, then a second (profiled) pass of `steps` steps with
+    HIP-event stage timing on the launch stream and, for the stress law,
+    the mask overlap of every step.  With `full`, also the dense AdamS
+    baseline, the steps storing v, the graph replay (--graph), a step-1 call
+    and the torch stream reference on the same tensors.  Everything is freed
+    before returning."""
+    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
+    dev = torch.device("cuda:0")
+    overlap = args.overlap or cfg.grad_law == "stress_t3"
+    log_fn(f"config {cfg.name}: n={n} P={P} K={K} k={k} pool={args.pool} steps={steps} warmup={warmup}")
+    d = S.dims(n, P, K)
+    bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
+
+    def alloc_state():
+        params = torch.empty(n, dtype=torch.float32, device=dev)
+        W.device_init_params(cfg, args.seed, params)
+        m = torch.zeros(n, dtype=torch.float32, device=dev)
+        v = torch.zeros(n, dtype=torch.float32, device=dev) if args.store_v else None
+        e = torch.zeros((K, n), dtype=torch.float32, device=dev)
+        mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
+        ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+        return params, m, v, e, mask, ws
+
+    def alloc_grads():
+        sigma = W.device_sigma(cfg, args.seed, dev)
+        pool = []
+        for s in range(args.pool):
+            gset = torch.empty((K, n), dtype=torch.float32, device=dev)
+            W.device_grads(cfg, s + 1, args.seed, sigma, gset)
+            pool.append(gset)
+            log_fn(f"{cfg.name}: gradient set {s + 1}/{args.pool} generated")
+        del sigma
+        return pool
+
+    if args.grads_first:
+        pool = alloc_grads()
+        params, m, v, e, mask, ws = alloc_state()
+    else:
+        params, m, v, e, mask, ws = alloc_state()
+        pool = alloc_grads()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    rec = {}
+    if args.calib and full:
+        rec["stream_calibration"] = stream_calibration(torch, dev, log_fn)
+
+    t = 0
+
+    def one_step(v_out=v):
+        nonlocal t
+        t += 1
+        S.step(d, params, pool[(t - 1) % len(pool)], m, v_out, e, mask, k, bt, cfg.lr, t, ws, stream)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log_fn(f"{cfg.name}: warmup done ({warmup} steps)")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    log_fn(f"{cfg.name}: timed {steps} steps: {ms:.3f} ms/step")
+
+    # per-stage durations of the same steps, recorded with HIP events on the
+    # stream the kernels run on (a second, profiled pass of `steps` steps)
+    S.profile_enable(True)
+    overlaps = []
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        step_ev[i].record(stream)
+        one_step()
+        step_ev[i + 1].record(stream)
+        if overlap:  # |M_t ∩ M_{t+1}| / (P k), outside the timed region
+            S.mask_overlap(d, k, S.mask_slot(d, k, mask, (t - 1) & 1), S.mask_slot(d, k, mask, t & 1), cnt, stream)
+            overlaps.append(cnt.item() / (P * k))
+    torch.cuda.synchronize()
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(steps)]
+    stages = S.profile_collect()
+    S.profile_enable(False)
+    stage_ms = {name: tot / c for name, (tot, c) in stages.items() if c}
+    log_fn(f"{cfg.name}: stage ms: " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in stage_ms.items()))
+    # the masks the steps left are valid partitioned top-k masks (synchronous check)
+    S.mask_check(d, k, S.mask_slot(d, k, mask, t & 1))
+    S.mask_check(d, k, S.mask_slot(d, k, mask, (t - 1) & 1))
+
+    b_step = alg_bytes_step(n, P, K, k, args.store_v)
+    passes = S.step_pass_count(d, k)
+    b_pass = alg_bytes_step_pass(n, P, K, k, args.store_v, passes)
+    gbps = b_step / (ms * 1e-3) / 1e9
+    pass_ms = stage_ms.get("step_pass", float("nan"))
+    pass_gbps = b_pass / (pass_ms * 1e-3) / 1e9
+    traffic = counters_traffic(cfg.name, args.store_v)
+    rec.update({
+        "workload": cfg.name, "n_params": n, "tensors": len(cfg.tensors), "partitions": P, "workers": K,
+        "k_per_partition": k, "sparsity": cfg.sparsity, "gradient_law": cfg.grad_law,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms, "params_per_s": n / (ms * 1e-3),
+        "hbm_gbps_alg": gbps, "hbm_frac_alg": gbps / HBM_PEAK_GBPS, "bytes_alg_per_step": b_step,
+        "stage_ms": stage_ms, "profiled_step_ms": step_ms,
+        "step_pass": {"kernel": "compress_kernel (step pass" + (": K - 1 worker passes, then the owner pass)"
+                                                                 if passes > 1 else ")"),
+                      "achieved": pass_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pass_gbps / HBM_PEAK_GBPS,
+                      "traffic": traffic, "bytes_alg_per_step_pass": b_pass, "ms_per_step_pass": pass_ms,
+                      "launches_per_step_pass": passes,
+                      "traffic_gbps": None if traffic is None else traffic / (pass_ms * 1e-3) / 1e9},
+    })
+    if overlaps:
+        rec["mask_overlap"] = overlaps
+
+    if full:
+        # the pages' comparison point: dense AdamS on the worker mean, same
+        # tensors, same number of steps (after the SCAPE measurements)
+        ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev2.record(stream)
+        for s_ in range(steps):
+            S.dense_adams_step(d, params, pool[s_ % len(pool)], m, v, bt, cfg.lr, t + 1 + s_, stream)
+        ev3.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = ev2.elapsed_time(ev3) / steps
+        log_fn(f"dense AdamS: {dense_ms:.3f} ms/step")
+        b_dense = (4 * K + (20 if args.store_v else 16)) * n
+        rec["dense_adams"] = {"ms_per_step": dense_ms, "params_per_s": n / (dense_ms * 1e-3),
+                              "hbm_gbps_alg": b_dense / (dense_ms * 1e-3) / 1e9,
+                              "hbm_frac_alg": b_dense / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                              "bytes_alg_per_step": b_dense, "note": "local cost only: no collective runs on one GPU"}
+
+        # the same steps storing v_t as well (an output AdamS never reads back)
+        if v is None:
+            v_keep = torch.zeros(n, dtype=torch.float32, device=dev)
+            one_step(v_keep)
+            torch.cuda.synchronize()
+            ev2.record(stream)
+            for _ in range(steps):
+                one_step(v_keep)
+            ev3.record(stream)
+            torch.cuda.synchronize()
+            vs_ms = ev2.elapsed_time(ev3) / steps
+            del v_keep
+            log_fn(f"steps storing v: {vs_ms:.3f} ms/step")
+            rec["step_storing_v"] = {"ms_per_step": vs_ms, "params_per_s": n / (vs_ms * 1e-3),
+                                     "hbm_gbps_alg": alg_bytes_step(n, P, K, k, True) / (vs_ms * 1e-3) / 1e9}
+
+        if args.graph:  # continues the SCAPE steps: t steps done, M_{t+1} in slot t & 1
+            rec["graph"] = graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, cfg.lr, t, ws, steps, log_fn)
+
+        # a step-1 call (the bootstrap: statistic pass and fresh select of M_1
+        # before the step pass), timed warm on the same tensors after
+        # everything else, since its state afterwards is no longer used
+        S.profile_enable(True)
+        ev2.record(stream)
+        S.step(d, params, pool[0], m, v, e, mask, k, bt, cfg.lr, 1, ws, stream)
+        ev3.record(stream)
+        torch.cuda.synchronize()
+        boot_ms = ev2.elapsed_time(ev3)
+        boot_stages = {name: tot for name, (tot, c) in S.profile_collect().items() if c}
+        S.profile_enable(False)
+        log_fn(f"bootstrap step (t = 1): {boot_ms:.3f} ms")
+        rec["bootstrap_step"] = {"ms": boot_ms, "stage_ms": boot_stages}
+
+        # a reference rate for the same allocations: torch's own elementwise
+        # kernel adding every worker's gradient row into its error-feedback
+        # row (read g, read e, write e: the step pass's 12K bytes per
+        # element); last, since it changes e
+        for i in range(K):
+            e[i].add_(pool[0][i])
+        ev2.record(stream)
+        for _ in range(2):
+            for i in range(K):
+                e[i].add_(pool[0][i])
+        ev3.record(stream)
+        torch.cuda.synchronize()
+        ref_ms = ev2.elapsed_time(ev3) / 2
+        rec["stream_reference"] = {"kernel": "torch add_: e[i] += g[i] for every worker", "bytes": 12 * K * n,
+                                   "ms": ref_ms, "GBps": 12 * K * n / (ref_ms * 1e-3) / 1e9}
+        log_fn(f"reference stream (torch add_ over the e and g rows): {ref_ms:.3f} ms, "
+               f"{rec['stream_reference']['GBps']:.0f} GB/s")
+    del params, m, v, e, mask, ws, pool
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def extra_workloads(spec, head, names):
+    """The workloads --extra-configs names, in the order of `names`, without
+    the headline one."""
+    if spec == "none":
+        return []
+    if spec == "all":
+        return [n for n in names if n != head]
+    want = [x.strip() for x in spec.split(",") if x.strip()]
+    bad = [x for x in want if x not in names]
+    if bad:
+        raise SystemExit(f"unknown workload(s) in --extra-configs: {', '.join(bad)}")
+    return [n for n in names if n in want and n != head]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,8 +509,11 @@ def main():
     ap.add_argument("--pool", type=int, default=3, help="distinct gradient sets cycled through")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-workers", type=int, default=0,
-                    help="oracle processes for the CPU baseline (default: usable cores, at most 16)")
+                    help="oracle processes for the CPU baseline (default: the usable cores, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-configs", default="all", metavar="all|none|NAME[,NAME...]",
+                    help="workloads measured after --config, at most "
+                         f"{EXTRA_STEPS} steps each, reported under 'configs' (default: all the others)")
     ap.add_argument("--overlap", action="store_true",
                     help="report |M_t ∩ M_{t+1}| / (P k) per step (untimed; on by default for the stress workload)")
     ap.add_argument("--offload", default="", metavar="CHUNK_PARTS[,CHUNK_PARTS...]",
@@ -321,223 +548,66 @@ def main():
         S.lib()
         print(json.dumps(offload_bench(S, W, cfg, args, log)), flush=True)
         return
-    args.overlap = args.overlap or cfg.grad_law == "stress_t3"
-    n, P, K, k = cfg.n, cfg.P, cfg.K, cfg.k
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    torch.cuda.set_device(torch.device("cuda:0"))
     S.lib()
-    log(f"config {cfg.name}: n={n} P={P} K={K} k={k} pool={args.pool}")
-
-    d = S.dims(n, P, K)
-    bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
-    def alloc_state():
-        params = torch.empty(n, dtype=torch.float32, device=dev)
-        W.device_init_params(cfg, args.seed, params)
-        m = torch.zeros(n, dtype=torch.float32, device=dev)
-        v = torch.zeros(n, dtype=torch.float32, device=dev) if args.store_v else None
-        e = torch.zeros((K, n), dtype=torch.float32, device=dev)
-        mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
-        ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
-        return params, m, v, e, mask, ws
-
-    def alloc_grads():
-        sigma = W.device_sigma(cfg, args.seed, dev)
-        pool = []
-        for s in range(args.pool):
-            gset = torch.empty((K, n), dtype=torch.float32, device=dev)
-            W.device_grads(cfg, s + 1, args.seed, sigma, gset)
-            pool.append(gset)
-            log(f"gradient set {s + 1}/{args.pool} generated")
-        del sigma
-        return pool
-
-    if args.grads_first:
-        pool = alloc_grads()
-        params, m, v, e, mask, ws = alloc_state()
-    else:
-        params, m, v, e, mask, ws = alloc_state()
-        pool = alloc_grads()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    calib = stream_calibration(torch, dev, log) if args.calib else None
-
-    t = 0
-
-    def one_step(v_out=v):
-        nonlocal t
-        t += 1
-        S.step(d, params, pool[(t - 1) % len(pool)], m, v_out, e, mask, k, bt, cfg.lr, t, ws, stream)
-
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        one_step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
-
-    # per-stage durations of the same steps, recorded with HIP events on the
-    # stream the kernels run on (a second, profiled pass of --steps steps)
-    S.profile_enable(True)
-    overlaps = []
-    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    step_ms = []
-    for i in range(args.steps):
-        step_ev[i].record(stream)
-        one_step()
-        step_ev[i + 1].record(stream)
-        if args.overlap:  # |M_t ∩ M_{t+1}| / (P k), outside the timed region
-            S.mask_overlap(d, k, S.mask_slot(d, k, mask, (t - 1) & 1), S.mask_slot(d, k, mask, t & 1), cnt, stream)
-            overlaps.append(cnt.item() / (P * k))
-    torch.cuda.synchronize()
-    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
-    stages = S.profile_collect()
-    S.profile_enable(False)
-    stage_ms = {name: tot / cnt for name, (tot, cnt) in stages.items() if cnt}
-    log("stage ms: " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in stage_ms.items()))
-    log("profiled steps ms: " + ", ".join(f"{x:.3f}" for x in step_ms))
-
-    # the pages' comparison point: dense AdamS on the worker mean, same
-    # tensors, same number of steps (after the SCAPE measurements)
-    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev2.record(stream)
-    for s_ in range(args.steps):
-        S.dense_adams_step(d, params, pool[s_ % len(pool)], m, v, bt, cfg.lr, t + 1 + s_, stream)
-    ev3.record(stream)
-    torch.cuda.synchronize()
-    dense_ms = ev2.elapsed_time(ev3) / args.steps
-    log(f"dense AdamS: {dense_ms:.3f} ms/step")
-
-    # the same steps storing v_t as well (an output AdamS never reads back)
-    vstore = None
-    if v is None:
-        v_keep = torch.zeros(n, dtype=torch.float32, device=dev)
-        one_step(v_keep)
-        torch.cuda.synchronize()
-        ev2.record(stream)
-        for _ in range(args.steps):
-            one_step(v_keep)
-        ev3.record(stream)
-        torch.cuda.synchronize()
-        vs_ms = ev2.elapsed_time(ev3) / args.steps
-        del v_keep
-        log(f"steps storing v: {vs_ms:.3f} ms/step")
-        vstore = {"ms_per_step": vs_ms, "params_per_s": n / (vs_ms * 1e-3),
-                  "hbm_gbps_alg": alg_bytes_step(n, P, K, k, True) / (vs_ms * 1e-3) / 1e9}
-
-    graph_rec = None
-    if args.graph:  # continues the SCAPE steps: t steps done, M_{t+1} in slot t & 1
-        graph_rec = graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, cfg.lr, t, ws, args.steps, log)
-
-    # a step-1 call (the bootstrap: statistic pass and fresh select of M_1
-    # before the step pass), timed warm on the same tensors after everything
-    # else, since its state afterwards is no longer used
-    S.profile_enable(True)
-    ev2.record(stream)
-    S.step(d, params, pool[0], m, v, e, mask, k, bt, cfg.lr, 1, ws, stream)
-    ev3.record(stream)
-    torch.cuda.synchronize()
-    boot_ms = ev2.elapsed_time(ev3)
-    boot_stages = {name: tot for name, (tot, c) in S.profile_collect().items() if c}
-    S.profile_enable(False)
-    log(f"bootstrap step (t = 1): {boot_ms:.3f} ms")
-
-    # a reference rate for the same allocations: torch's own elementwise
-    # kernel adding every worker's gradient row into its error-feedback row
-    # (read g, read e, write e: the step pass's 12K bytes per element);
-    # last, since it changes e
-    for i in range(K):
-        e[i].add_(pool[0][i])
-    ev2.record(stream)
-    for _ in range(2):
-        for i in range(K):
-            e[i].add_(pool[0][i])
-    ev3.record(stream)
-    torch.cuda.synchronize()
-    ref_ms = ev2.elapsed_time(ev3) / 2
-    ref = {"kernel": "torch add_: e[i] += g[i] for every worker", "bytes": 12 * K * n, "ms": ref_ms,
-           "GBps": 12 * K * n / (ref_ms * 1e-3) / 1e9}
-    log(f"reference stream (torch add_ over the e and g rows): {ref_ms:.3f} ms, {ref['GBps']:.0f} GB/s")
+    head = measure_workload(S, W, torch, cfg, args, args.steps, args.warmup, True, log)
+    extras = {}
+    for name in extra_workloads(args.extra_configs, cfg.name, W.CONFIGS):
+        extras[name] = measure_workload(S, W, torch, W.CONFIGS[name], args, min(args.steps, EXTRA_STEPS),
+                                        min(args.warmup, EXTRA_WARMUP), False, log)
 
     # the oracle on the host's cores, after every GPU measurement: run
     # before them (forked, ahead of the GPU's initialisation), it left the
     # Llama-1.8B step pass at 17.64-17.73 ms in six processes of six, where
     # processes without it, and with it afterwards, ran 15.95-17.70 ms
-    torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu_baseline:
-        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        # at most CPU_SHARE processes: the CPU share of one GPU on the
+        # benchmark host, whatever the affinity mask shows (an oracle process
+        # at the Llama-1.8B shape holds 3-4 GB)
+        affinity = len(os.sched_getaffinity(0))
+        workers = args.cpu_workers or min(CPU_SHARE, affinity)
         cpu = cpu_baseline(cfg, args.seed, workers, log)
+        cpu["affinity_cores"] = affinity
         cpu["tiny_single_core"] = cpu_tiny_single_core(args.seed, log)
 
-    b_step = alg_bytes_step(n, P, K, k, args.store_v)
-    passes = S.step_pass_count(d, k)
-    b_comp = alg_bytes_step_pass(n, P, K, k, args.store_v, passes)
-    gbps = b_step / (ms * 1e-3) / 1e9
-    comp_ms = stage_ms.get("step_pass", float("nan"))
-    comp_gbps = b_comp / (comp_ms * 1e-3) / 1e9
-    traffic = None
-    prof_path = os.path.join(ROOT, "profiles", f"step_pass_{cfg.name}_counters.json")
-    if os.path.exists(prof_path) and not args.store_v:  # the counters come from the default (v-less) bench
-        from sparse_communication_distributed_amd.prof_summary import step_pass_source_hash
-        with open(prof_path) as f:
-            doc = json.load(f)
-        if doc.get("source_hash") == step_pass_source_hash():  # counters of this very kernel
-            traffic = doc.get("hbm_bytes_per_step_pass")
-
+    sp = head["step_pass"]
     out = {
         "metric": METRIC,
-        "value": n / (ms * 1e-3),
+        "value": head["params_per_s"],
         "unit": "params/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "n_params": n, "tensors": len(cfg.tensors), "partitions": P,
-                   "workers": K, "k_per_partition": k, "sparsity": cfg.sparsity,
+        "config": {"workload": cfg.name, "n_params": cfg.n, "tensors": len(cfg.tensors), "partitions": cfg.P,
+                   "workers": cfg.K, "k_per_partition": cfg.k, "sparsity": cfg.sparsity,
                    "gradient_law": cfg.grad_law, "gradient_sets": args.pool, "v_stored": bool(args.store_v)},
-        "hbm_gbps_alg": gbps,
-        "hbm_frac_alg": gbps / HBM_PEAK_GBPS,
-        "bytes_alg_per_step": b_step,
-        "stage_ms": stage_ms,
-        "profiled_step_ms": step_ms,
-        "bootstrap_step": {"ms": boot_ms, "stage_ms": boot_stages},
-        "roofline": {"bound": "hbm", "kernel": "compress_kernel (step pass" + (": K - 1 worker passes, then the owner pass)" if passes > 1 else ")"), "achieved": comp_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": comp_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "bytes_alg_per_step_pass": b_comp, "ms_per_step_pass": comp_ms,
-                     "launches_per_step_pass": passes,
+        "hbm_gbps_alg": head["hbm_gbps_alg"],
+        "hbm_frac_alg": head["hbm_frac_alg"],
+        "bytes_alg_per_step": head["bytes_alg_per_step"],
+        "stage_ms": head["stage_ms"],
+        "profiled_step_ms": head["profiled_step_ms"],
+        "roofline": {"bound": "hbm", "kernel": sp["kernel"], "achieved": sp["achieved"], "peak": sp["peak"],
+                     "unit": "GB/s", "frac": sp["frac"], "traffic": sp["traffic"],
+                     "bytes_alg_per_step_pass": sp["bytes_alg_per_step_pass"],
+                     "ms_per_step_pass": sp["ms_per_step_pass"],
+                     "launches_per_step_pass": sp["launches_per_step_pass"],
                      # counter-measured bytes over the same launch time
-                     "traffic_gbps": None if traffic is None else traffic / (comp_ms * 1e-3) / 1e9},
+                     "traffic_gbps": sp["traffic_gbps"]},
         "cpu_baseline": None,
     }
-    b_dense = (4 * K + (20 if args.store_v else 16)) * n
-    out["dense_adams"] = {"ms_per_step": dense_ms, "params_per_s": n / (dense_ms * 1e-3),
-                          "hbm_gbps_alg": b_dense / (dense_ms * 1e-3) / 1e9,
-                          "hbm_frac_alg": b_dense / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                          "bytes_alg_per_step": b_dense,
-                          "note": "local cost only: no collective runs on one GPU"}
-    if vstore is not None:
-        out["step_storing_v"] = vstore
-    out["stream_reference"] = ref
-    if calib is not None:
-        out["stream_calibration"] = calib
-    if overlaps:
-        out["mask_overlap"] = overlaps
-    if graph_rec is not None:
-        out["graph"] = graph_rec
+    for key in ("bootstrap_step", "dense_adams", "step_storing_v", "stream_reference", "stream_calibration",
+                "mask_overlap", "graph"):
+        if key in head:
+            out[key] = head[key]
+    if extras:
+        out["configs"] = extras
     if cpu is not None:
         cpu["gpu_over_cpu"] = out["value"] / cpu["value"]
     out["cpu_baseline"] = cpu

@@ -17,6 +17,7 @@ its variant; bench.py ignores it once they change.
 
 import argparse
 import csv
+import gzip
 import hashlib
 import json
 import os
@@ -116,9 +117,23 @@ def step_pass_ms(run):
     return owner, wav, per, owner + per * wav
 
 
+def _open(path):
+    """A CSV file, gzip-compressed or not."""
+    return gzip.open(path, "rt") if path.endswith(".gz") else open(path)
+
+
+def calibration_values(vals):
+    """The counter values of the 1 GiB calibration copies among all copy
+    dispatches of a run: those within a factor of two of the largest (the
+    workload's own small copies, such as uploads of host-drawn indices or a
+    mask check's read-back, use the same copy kernel)."""
+    top = max(vals)
+    return [v for v in vals if v >= 0.5 * top]
+
+
 def read_counter(path, counter):
     per = defaultdict(list)
-    for r in csv.DictReader(open(path)):
+    for r in csv.DictReader(_open(path)):
         if r["Counter_Name"] == counter:
             per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return per
@@ -136,7 +151,7 @@ def main():
                     help="step-pass launches to drop from the counter average (the first step)")
     a = ap.parse_args()
 
-    runs = [list(csv.DictReader(open(path))) for path in a.stats]
+    runs = [list(csv.DictReader(_open(path))) for path in a.stats]
     rows = runs[0]
     lines = [f"# Kernel profile — {a.workload}", ""]
     if a.command:
@@ -161,10 +176,12 @@ def main():
         return
     fetch = read_counter(a.fetch, "FETCH_SIZE")
     write = read_counter(a.write, "WRITE_SIZE")
-    f_scale = GIB_KIB / (sum(fetch[CALIB_KERNEL]) / len(fetch[CALIB_KERNEL]))
-    w_scale = GIB_KIB / (sum(write[CALIB_KERNEL]) / len(write[CALIB_KERNEL]))
+    fcal, wcal = calibration_values(fetch[CALIB_KERNEL]), calibration_values(write[CALIB_KERNEL])
+    f_scale = GIB_KIB / (sum(fcal) / len(fcal))
+    w_scale = GIB_KIB / (sum(wcal) / len(wcal))
     lines += ["", "## HBM bytes (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
-              f"Calibration copy of 1 GiB: FETCH_SIZE scale {f_scale:.3f}, WRITE_SIZE scale {w_scale:.3f}.", "",
+              f"Calibration copy of 1 GiB ({len(fcal)} and {len(wcal)} dispatches): FETCH_SIZE scale {f_scale:.3f}, "
+              f"WRITE_SIZE scale {w_scale:.3f}.", "",
               "| kernel | launches | read GB / launch (scaled) | write GB / launch (scaled) |", "|---|---|---|---|"]
     out, names = {}, {}
     roles = {k: step_pass_role(k) for k in set(fetch) | set(write)}

@@ -126,3 +126,25 @@ def test_step_pass_hash_ignores_comments_only():
     c = "int f(int x) { return 3 * x; }"
     assert _code_only(a) == _code_only(b)
     assert _code_only(a) != _code_only(c)
+
+
+def test_extra_workloads_selection():
+    sys.path.insert(0, ROOT)
+    import bench
+    names = ["tiny", "gpt345m", "llama500m", "llama1.8b", "stress"]
+    assert bench.extra_workloads("all", "llama1.8b", names) == ["tiny", "gpt345m", "llama500m", "stress"]
+    assert bench.extra_workloads("none", "llama1.8b", names) == []
+    assert bench.extra_workloads("stress, tiny", "llama1.8b", names) == ["tiny", "stress"]
+    assert bench.extra_workloads("tiny", "tiny", names) == []
+    with pytest.raises(SystemExit):
+        bench.extra_workloads("gpt2", "tiny", names)
+
+
+def test_counter_calibration_ignores_small_copies():
+    """The calibration uses the 1 GiB copies only, not the workload's own
+    small copies through the same copy kernel."""
+    from sparse_communication_distributed_amd.prof_summary import calibration_values
+    gib = [2097152.0, 2097150.0, 2097160.0]
+    small = [3.0, 12.5, 0.0, 400.0]
+    assert sorted(calibration_values(gib + small)) == sorted(gib)
+    assert calibration_values([5.0]) == [5.0]

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.mark.timeout(600)
 def test_bench_json_line_tiny():
     print("[bench-line] tiny, 3 steps, graph replay", flush=True)
-    r = subprocess.run([sys.executable, "bench.py", "--config", "tiny", "--steps", "3", "--warmup", "1", "--graph"],
+    r = subprocess.run([sys.executable, "bench.py", "--config", "tiny", "--steps", "3", "--warmup", "1", "--graph",
+                        "--extra-configs", "gpt345m"],
                        cwd=ROOT, capture_output=True, text=True, timeout=540)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [x for x in r.stdout.splitlines() if x.strip()]
@@ -47,3 +48,14 @@ def test_bench_json_line_tiny():
     sr = d["stream_reference"]
     assert sr["bytes"] == 12 * d["config"]["workers"] * n and sr["ms"] > 0
     assert sr["GBps"] == pytest.approx(sr["bytes"] / (sr["ms"] * 1e-3) / 1e9, rel=1e-9)
+    ex = d["configs"]["gpt345m"]
+    assert set(d["configs"]) == {"gpt345m"}
+    assert ex["steps"] == 3 and ex["warmup"] == 1 and ex["workers"] == 8
+    assert ex["params_per_s"] == pytest.approx(ex["n_params"] / (ex["ms_per_step"] * 1e-3), rel=1e-9)
+    assert ex["hbm_frac_alg"] == pytest.approx(ex["hbm_gbps_alg"] / 8000.0, rel=1e-9)
+    sp = ex["step_pass"]
+    assert sp["frac"] == pytest.approx(sp["achieved"] / 8000.0, rel=1e-9)
+    assert sp["achieved"] == pytest.approx(sp["bytes_alg_per_step_pass"] / (sp["ms_per_step_pass"] * 1e-3) / 1e9,
+                                           rel=1e-9)
+    assert 0 < sp["frac"] < 1 and len(ex["profiled_step_ms"]) == 3
+    assert cb["cores"] <= cb["affinity_cores"]

@@ -281,6 +281,112 @@ def graph_bench(S, torch, d, params, pool, m, v, e, mask, k, bt, lr, steps_done,
     return {"ms_per_step": ms, "replays": steps, "steps_per_replay": 2}
 
 
+def shard_bench(S, W, torch, cfg, args, log_fn):
+    """One rank's share of the sharded step at the workload's layout with
+    --shard ranks: the rank's compression of its own rows over every
+    partition with the statistic and selection on its own partitions
+    (scape_shard_compress), then AdamS on those partitions
+    (scape_shard_update).  The reduction of the ranks' sparse buffers and
+    the all-gathers run over the network in a multi-GPU run and are not
+    timed; here the rank's own values stand in for the reduced buffer, and
+    the other ranks' parts of the next mask are the current mask's (copied
+    outside the timed region).  Rank 0 is timed."""
+    K = args.shard
+    cfg = cfg.with_(num_workers=K)
+    n, P, k, n_p = cfg.n, cfg.P, cfg.k, cfg.n_p
+    dev = torch.device("cuda:0")
+    d = S.dims(n, P, K)
+    bt = S.betas(cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay)
+    rank = 0
+    first, count = S.shard_partitions(d, rank)
+    log_fn(f"shard: {cfg.name} layout, {K} ranks: rank {rank} owns partitions {first}..{first + count - 1}")
+    params = torch.empty(n, dtype=torch.float32, device=dev)
+    W.device_init_params(cfg, args.seed, params)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    e = torch.zeros(n, dtype=torch.float32, device=dev)
+    b = torch.zeros(P * k, dtype=torch.float32, device=dev)
+    mask = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+    sigma = W.device_sigma(cfg, args.seed, dev)
+    rows = torch.empty((K, n), dtype=torch.float32, device=dev)
+    pool = []
+    for s_ in range(args.pool):  # the rank's gradient row of steps 1, 2, ...
+        W.device_grads(cfg, s_ + 1, args.seed, sigma, rows)
+        pool.append(rows[rank].clone())
+    del rows, sigma
+    torch.cuda.empty_cache()
+    stream = torch.cuda.current_stream()
+    # M_1 for every partition (each rank's part from the same row)
+    for r in range(K):
+        S.shard_select_initial(d, k, r, pool[0], e, m, mask, bt, ws, stream)
+    views = [S.mask_slot_tensors(d, k, mask, sl) + (S.mask_slot_meta(d, k, mask, sl),) for sl in (0, 1)]
+    Wp, T = (n_p + 63) // 64, (n_p + 4095) // 4096
+
+    def gather_other_parts(t):
+        """The other ranks' parts of M_{t+1}: those of M_t (stand-in)."""
+        src, dst = views[(t - 1) & 1], views[t & 1]
+        for lo, hi in ((0, first), (first + count, P)):
+            if hi <= lo:
+                continue
+            for (a_, b_), per in zip(zip(src[:3], dst[:3]), (Wp, k, T)):
+                b_[lo * per:hi * per].copy_(a_[lo * per:hi * per])
+            for j in range(3):
+                dst[3][j * P + lo:j * P + hi].copy_(src[3][j * P + lo:j * P + hi])
+
+    t = 0
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    c_ms, u_ms = [], []
+
+    def one(timed):
+        nonlocal t
+        t += 1
+        evs[0].record(stream)
+        S.shard_compress(d, k, rank, pool[(t - 1) % len(pool)], e, m, b, mask, bt, t, ws, stream)
+        evs[1].record(stream)
+        S.shard_update(d, k, rank, params, m, None, b[first * k:(first + count) * k], mask, bt, cfg.lr, t, stream)
+        evs[2].record(stream)
+        gather_other_parts(t)
+        if timed:
+            torch.cuda.synchronize()
+            c_ms.append(evs[0].elapsed_time(evs[1]))
+            u_ms.append(evs[1].elapsed_time(evs[2]))
+
+    for _ in range(args.warmup):
+        one(False)
+    torch.cuda.synchronize()
+    S.profile_enable(True)
+    for _ in range(args.steps):
+        one(True)
+    stages = S.profile_collect()
+    S.profile_enable(False)
+    stage_ms = {name: tot / c for name, (tot, c) in stages.items() if c}
+    S.mask_check(d, k, S.mask_slot(d, k, mask, t & 1))
+    cm, um = float(np.median(c_ms)), float(np.median(u_ms))
+    n_own = count * n_p
+    # the rank's pass: its rows (g read, e read and written), the mask
+    # words, its sparse buffer written, m read on its partitions
+    b_pass = 12 * n + n / 8 + 4 * P * k + 4 * n_own
+    # the update: per entry of its partitions, b_bar and the index read, w
+    # and m read and written
+    b_upd = 24 * count * k
+    pass_ms = stage_ms.get("step_pass", float("nan"))
+    log_fn(f"shard: compress+select {cm:.3f} ms (pass {pass_ms:.3f} ms), update {um:.3f} ms")
+    return {"metric": "one rank's share of the sharded SCAPE step (compression of its rows, selection and AdamS "
+                      "on its partitions), ms per step",
+            "value": cm + um, "unit": "ms", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+            "config": {"workload": cfg.name, "n_params": n, "partitions": P, "ranks": K, "rank": rank,
+                       "owned_partitions": [first, count], "k_per_partition": k, "sparsity": cfg.sparsity},
+            "compress_select_ms": cm, "update_ms": um, "stage_ms": stage_ms,
+            "roofline": {"bound": "hbm", "kernel": "shard_pass_kernel", "achieved": b_pass / (pass_ms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": b_pass / (pass_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "bytes_alg_per_launch": b_pass, "ms_per_launch": pass_ms, "traffic": None},
+            "update": {"bytes_alg": b_upd, "GBps_alg": b_upd / (um * 1e-3) / 1e9},
+            "dtype": "f32", "data": "synthetic",
+            "note": "local work only: the reduce-scatter of the sparse buffers and the all-gathers of "
+                    "parameters and mask bits run over the network in a multi-GPU run"}
+
+
 def counters_traffic(name, store_v):
     """HBM bytes per step pass from the committed counter summary of this
     workload, while it was taken from the step-pass code as it stands (the
@@ -529,6 +635,8 @@ def main():
                     help="the timed steps also store v_t at the masked entries (AdamS never reads it back)")
     ap.add_argument("--calib", action="store_true",
                     help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
+    ap.add_argument("--shard", type=int, default=0, metavar="RANKS",
+                    help="time one rank's share of the sharded step at --config's layout with this many ranks")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the simulated workers share one device and no "
@@ -547,6 +655,10 @@ def main():
     if args.offload:
         S.lib()
         print(json.dumps(offload_bench(S, W, cfg, args, log)), flush=True)
+        return
+    if args.shard:
+        S.lib()
+        print(json.dumps(shard_bench(S, W, torch, cfg, args, log)), flush=True)
         return
     torch.cuda.set_device(torch.device("cuda:0"))
     S.lib()

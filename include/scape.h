@@ -285,6 +285,59 @@ scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const
                                    float* v, scape_betas betas, float lr, int64_t step, hipStream_t stream);
 
 /*
+ * ---- One rank's share of the sharded step ----
+ * In a run over K GPUs each rank is one worker and the owner of the
+ * partitions p with floor(p*K/P) == rank; the mask generation is
+ * distributed like the optimizer's shards ([P] abstract and §I; [S] §2,
+ * partitioned mask synchronisation).  Per step t a rank calls, in order:
+ *   scape_shard_compress  its own rows at M_t over every partition, and the
+ *                         selection of M_{t+1} on its own partitions;
+ *   (the caller reduces the ranks' sparse buffers b over the K ranks, a
+ *    sparse reduce-scatter: each rank receives b_bar for its partitions)
+ *   scape_shard_update    AdamS on its partitions from that b_bar;
+ *   (the caller all-gathers the updated parameters at M_t, and the ranks'
+ *    parts of M_{t+1} (bits, idx, tile_off, meta) into every rank's blob,
+ *    before step t+1's compression reads M_{t+1})
+ * At t = 1 every rank first calls scape_shard_select_initial, and the
+ * ranks' parts of M_1 are all-gathered, before the compression.  The
+ * arithmetic equals scape_step's bit for bit: on one device, K ranks called
+ * in turn on shared params/m/v/mask blob, with b_bar from
+ * scape_reduce_sparse, reproduce scape_step.
+ * grads and e are the rank's rows ([n] each; e in/out); b is the rank's
+ * sparse buffer [P*k] (laid out like idx); m and params are [n] (a rank
+ * reads and writes only its partitions' entries of m, params and v); the
+ * workspace is scape_workspace_bytes() (a rank uses its partitions' parts).
+ * A rank that owns no partition (K > P) only compresses.
+ */
+
+/* The partitions rank `rank` owns: *first, *count (possibly 0). */
+scape_status scape_shard_partitions(const scape_dims* dims, int32_t rank, int32_t* first, int32_t* count);
+
+/* Step-1 mask M_1 on the rank's partitions, written to slot 0: the top-k of
+ * |b1*m + (1-b1)*(grads + e)| (the bootstrap of scape_step). */
+scape_status scape_shard_select_initial(const scape_dims* dims, int64_t k, int32_t rank, const float* grads,
+                                        const float* e, const float* m, void* mask_blob, scape_betas betas,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Step t (>= 1): a = grads + e; at M_t (slot (t-1)&1, every partition):
+ * b[r] = a at idx[r], e <- 0 there and a elsewhere.  On the rank's
+ * partitions: statistic b1*m + (1-b1)*a with m before this step's update,
+ * and M_{t+1} written to slot t&1 (those partitions only).  Stage timing,
+ * while on, records its pass and its selection like scape_step's. */
+scape_status scape_shard_compress(const scape_dims* dims, int64_t k, int32_t rank, const float* grads, float* e,
+                                  const float* m, float* b, void* mask_blob, scape_betas betas, int64_t step,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Step t: AdamS at M_t on the rank's partitions (scape_adams_update's rule)
+ * with x = b_bar[r - first*k] for entries r in [first*k, (first+count)*k)
+ * of the index list: b_bar holds count*k entries, the synchronised buffer
+ * of the rank's partitions (NULL allowed when count is 0).  v is an
+ * optional output (NULL: not stored). */
+scape_status scape_shard_update(const scape_dims* dims, int64_t k, int32_t rank, float* params, float* m, float* v,
+                                const float* b_bar, void* mask_blob, scape_betas betas, float lr, int64_t step,
+                                hipStream_t stream);
+
+/*
  * Error-feedback buffers offloaded to pinned host memory, with double
  * buffering ([P] §I: the EF buffers live in CPU memory, moved over the
  * CPU-GPU link; [S] §2 "Ottimizzazione della Memoria": CPU offload with

@@ -152,8 +152,9 @@ hipError_t launch_reduce(const Geom& g, const float* b, float* bbar, hipStream_t
 
 hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, float* w, float* m,
                         float* v, float b1, float b2, float c1, float c2, float ibc1, float ibc2,
-                        float eps, float wd, float lr, hipStream_t s) {
-  const int64_t pk = (int64_t)g.P * g.k;
+                        float eps, float wd, float lr, hipStream_t s, int64_t count) {
+  const int64_t pk = count < 0 ? (int64_t)g.P * g.k : count;
+  if (pk < 1) return hipSuccess;
   AdamsK c{b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr, g.n};
   adams_kernel<<<grid_for(pk), kThreads, 0, s>>>(bbar, idx, pk, w, m, v, c);
   return hipGetLastError();

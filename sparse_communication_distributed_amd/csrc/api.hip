@@ -53,6 +53,8 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
     rem -= nb;
   }
   r.nlevels = nl;
+  r.sp0 = 0;
+  r.snp = P;
   // mask slot: bits, idx, tile_off, then the threshold record u32[3P]
   r.off_bits = 0;
   r.off_idx = align256((size_t)P * r.wpp * 8);
@@ -268,7 +270,8 @@ scape_status run_tail(const Geom& g, const Ws& w, scape_mask_view out, hipStream
 scape_status run_fresh_select(const Geom& g, const Ws& w, int src, const StatArgs& a, bool vec,
                               scape_mask_view out, hipStream_t s) {
   scape_status st;
-  if ((st = hip_check(launch_zero_u32(w.sel.hist, (int64_t)g.P * kBins, s), "zero"))) return st;
+  if ((st = hip_check(launch_zero_u32(w.sel.hist + (int64_t)g.sp0 * kBins, (int64_t)g.snp * kBins, s), "zero")))
+    return st;
   if ((st = hip_check(launch_init_state(g, w.sel.state, s), "init"))) return st;
   if (g.tpp >= 4 * kSampleStep) {
     StatArgs b = a;
@@ -474,7 +477,7 @@ scape_status step_begin(StepCtx& c, const scape_dims* dims, float* params, const
     if ((st = run_fresh_select(g, c.w, kSrcState, boot, c.vec, c.cur, stream))) return st;
   }
   if (c.prof) g_prof.begin(ST_PASS, stream);
-  return hip_check(launch_zero_u32(c.w.sel.hist, (int64_t)g.P * kBins, stream), "zero");
+  return hip_check(launch_zero_u32(c.w.sel.hist + (int64_t)g.sp0 * kBins, (int64_t)g.snp * kBins, stream), "zero");
 }
 
 scape_status step_end(StepCtx& c, hipStream_t stream) {
@@ -691,6 +694,132 @@ scape_status scape_step_offload(const scape_dims* dims, float* params, const flo
   for (int b = 0; b < 2 && b < nchunks; ++b)
     if ((st = hip_check(hipStreamWaitEvent(stream, oev.out[b], 0), "offload wait"))) return st;
   return step_end(c, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The partitions rank r owns, floor(p*K/P) == r: [ceil(r*P/K), ceil((r+1)*P/K)).
+void owned_range(const Geom& g, int r, int* lo, int* hi) {
+  *lo = (int)(((int64_t)r * g.P + g.K - 1) / g.K);
+  *hi = (int)(((int64_t)(r + 1) * g.P + g.K - 1) / g.K);
+}
+
+// Validation shared by the shard calls; on success g holds the geometry with
+// the selection restricted to the rank's partitions.
+scape_status shard_geom(const scape_dims* dims, int64_t k, int32_t rank, Geom* g) {
+  scape_status st = check_dims(dims, k, g);
+  if (st) return st;
+  if (rank < 0 || rank >= g->K) return fail(SCAPE_EINVAL, "rank %d outside [0, %d)", rank, g->K);
+  int lo, hi;
+  owned_range(*g, rank, &lo, &hi);
+  g->sp0 = lo;
+  g->snp = hi - lo;
+  return SCAPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+scape_status scape_shard_partitions(const scape_dims* dims, int32_t rank, int32_t* first, int32_t* count) {
+  Geom g;
+  scape_status st = shard_geom(dims, 1, rank, &g);
+  if (st) return st;
+  if (!first || !count) return fail(SCAPE_EINVAL, "null pointer argument");
+  *first = g.sp0;
+  *count = g.snp;
+  return SCAPE_OK;
+}
+
+scape_status scape_shard_select_initial(const scape_dims* dims, int64_t k, int32_t rank, const float* grads,
+                                        const float* e, const float* m, void* mask_blob, scape_betas betas,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geom g;
+  scape_status st = shard_geom(dims, k, rank, &g);
+  if (st) return st;
+  if (!grads || !e || !m || !mask_blob || !workspace) return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = check_betas(betas, 1.0f))) return st;
+  if (workspace_bytes < g.ws_total)
+    return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
+  if (g.snp < 1) return SCAPE_OK;  // this rank owns no partition
+  Ws w = ws_view(g, workspace);
+  StatArgs a{};
+  a.m = m;
+  a.grads = grads;
+  a.e = e;
+  a.b1 = betas.beta1;
+  a.c1 = 1.0f - betas.beta1;
+  a.single_row = true;
+  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m);
+  return run_fresh_select(g, w, kSrcState, a, vec, slot_view(g, mask_blob, 0), stream);
+}
+
+scape_status scape_shard_compress(const scape_dims* dims, int64_t k, int32_t rank, const float* grads, float* e,
+                                  const float* m, float* b, void* mask_blob, scape_betas betas, int64_t step,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geom g;
+  scape_status st = shard_geom(dims, k, rank, &g);
+  if (st) return st;
+  if (!grads || !e || !m || !b || !mask_blob || !workspace) return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = check_betas(betas, 1.0f))) return st;
+  if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  if (workspace_bytes < g.ws_total)
+    return fail(SCAPE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, g.ws_total);
+  Ws w = ws_view(g, workspace);
+  const scape_mask_view cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
+  const scape_mask_view nxt = slot_view(g, mask_blob, (int)(step & 1));
+  const float b1 = betas.beta1, c1 = 1.0f - betas.beta1;
+  const bool vec = (g.n_p % 4 == 0) && aligned16(grads) && aligned16(e) && aligned16(m);
+  const bool prof = g_prof.on;
+  if (g.snp > 0 &&
+      (st = hip_check(launch_zero_u32(w.sel.hist + (int64_t)g.sp0 * kBins, (int64_t)g.snp * kBins, stream), "zero")))
+    return st;
+  if (prof) g_prof.begin(ST_PASS, stream);
+  if ((st = hip_check(launch_shard_pass(g, rank, grads, e, cur.bits, cur.tile_off, b, m, b1, c1, cur.meta + g.P,
+                                        w.sel.cand, w.sel.cnt1, w.sel.hist, vec, stream),
+                      "shard pass")))
+    return st;
+  if (g.snp < 1) {  // this rank owns no partition: nothing to select
+    if (prof) g_prof.end();
+    return SCAPE_OK;
+  }
+  if (prof) g_prof.begin(ST_SELECT, stream);
+  if ((st = hip_check(launch_level1(g, w.sel, kScanCheck, stream), "level 1"))) return st;
+  StatArgs a{};
+  a.m = m;  // not yet updated: the update of this step comes after the reduction across ranks
+  a.grads = grads;
+  a.e = e;
+  a.b = b;
+  a.bits = cur.bits;
+  a.tile_off = cur.tile_off;
+  a.b1 = b1;
+  a.c1 = c1;
+  a.single_row = true;
+  if ((st = run_fallback(g, w, kSrcMasked, a, vec, stream))) return st;
+  st = run_tail(g, w, nxt, stream, prof);
+  if (prof) g_prof.end();
+  return st;
+}
+
+scape_status scape_shard_update(const scape_dims* dims, int64_t k, int32_t rank, float* params, float* m, float* v,
+                                const float* b_bar, void* mask_blob, scape_betas betas, float lr, int64_t step,
+                                hipStream_t stream) {
+  Geom g;
+  scape_status st = shard_geom(dims, k, rank, &g);
+  if (st) return st;
+  // v is optional, and b_bar may be null for a rank that owns no partition
+  if (!params || !m || !mask_blob || (g.snp > 0 && !b_bar)) return fail(SCAPE_EINVAL, "null pointer argument");
+  if ((st = check_betas(betas, lr))) return st;
+  if (step < 1) return fail(SCAPE_EINVAL, "step must be >= 1");
+  if (g.snp < 1) return SCAPE_OK;
+  const scape_mask_view cur = slot_view(g, mask_blob, (int)((step - 1) & 1));
+  const float b1 = betas.beta1, b2 = betas.beta2;
+  return hip_check(launch_adams(g, b_bar, cur.idx + (int64_t)g.sp0 * g.k, params, m, v, b1, b2, 1.0f - b1, 1.0f - b2,
+                                bias_reciprocal(b1, step), bias_reciprocal(b2, step), betas.eps, betas.weight_decay,
+                                lr, stream, (int64_t)g.snp * g.k),
+                   "shard update");
 }
 
 scape_status scape_dense_adams_step(const scape_dims* dims, float* params, const float* grads, float* m,

@@ -430,6 +430,115 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
   }
 }
 
+// One rank's pass in the sharded step (SCAPE paper abstract and §I: the
+// mask generation is distributed like the optimizer's shards): the rank is
+// one worker, so it compresses its own gradient row g^r with its own
+// error-feedback row e^r at the shared mask M_t over every partition, and
+// writes its sparse buffer b^r (the non-owner workers' job in the one-device
+// step).  On the partitions it owns it also forms the statistic
+// b1*m + c1*a^r from m before any update and captures the selection
+// candidates, as the step pass's owner does.  The AdamS update waits for the
+// synchronised buffer b_bar of the owned partitions (after the reduction
+// across ranks), so it is a call of its own.  grads, e: [n] (the rank's
+// rows); b: [P*k].
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads, kWorkerMinWaves)
+shard_pass_kernel(Geom g, int rank, const float* __restrict__ grads, float* __restrict__ e,
+                  const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
+                  float* __restrict__ b, const float* __restrict__ m, float b1, float c1,
+                  const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
+                  uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist) {
+  constexpr int CG = kWorkerChunkGroup;
+  __shared__ uint64_t sw[kWordsPerTile];
+  __shared__ uint32_t spre[kWordsPerTile];
+  __shared__ uint32_t sh[kBins];
+  __shared__ uint32_t tcnt;
+  const int p = block_part();
+  const bool own = (int)(((int64_t)p * g.K) / g.P) == rank;  // block-uniform
+  if (own) hist_zero(sh);
+  const int64_t pbase = (int64_t)p * g.n_p;
+  const int64_t wbase = (int64_t)p * g.wpp;
+  const uint32_t lo = own ? lo_in[p] : 0u;
+  const int lane16 = threadIdx.x & 15;
+  const int sh4 = 4 * lane16;
+  const uint64_t below = (sh4 == 0) ? 0ull : ((1ull << sh4) - 1ull);
+
+  for (int64_t t = block_in_part(); t < g.tpp; t += blocks_per_part()) {
+    __syncthreads();  // previous tile's LDS words and counter no longer in use
+    load_tile_words(bits, wbase, g.wpp, t, sw, spre);
+    if (threadIdx.x == 0) tcnt = 0;
+    __syncthreads();
+    const int64_t tb = t * kTile;
+    const uint32_t tn = (uint32_t)min<int64_t>(kTile, g.n_p - tb);
+    const int64_t rbase = (int64_t)p * g.k + tile_off[(int64_t)p * g.tpp + t];
+    const int64_t rlim = (int64_t)(p + 1) * g.k - rbase;  // a malformed mask stays in bounds
+    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    const float* gt = grads + pbase + tb;
+    float* et = e + pbase + tb;
+    const float* mt = m + pbase + tb;
+    float* bt = b + rbase;
+    for (int cg = 0; cg < 4; cg += CG) {
+      uint32_t nib[CG], rr0[CG], o[CG];
+      float ga[CG][4], ea[CG][4], ma[CG][4];
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const int c = cg + u;
+        const int q = c * 16 + (threadIdx.x >> 4);
+        const uint64_t word = sw[q];
+        nib[u] = (uint32_t)(word >> sh4) & 0xfu;
+        rr0[u] = spre[q] + (uint32_t)__popcll(word & below);
+        o[u] = c * 1024 + 4 * threadIdx.x;
+        if (o[u] < tn) {
+          load4(gt, o[u], tn, VEC, ga[u]);
+          load4(et, o[u], tn, VEC, ea[u]);
+          if (own) load4(mt, o[u], tn, VEC, ma[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        float a[4];
+        if (o[u] < tn) {
+          float eo[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a[q] = ga[u][q] + ea[u][q];
+            eo[q] = ((nib[u] >> q) & 1u) ? 0.0f : a[q];
+          }
+          store4(et, o[u], tn, VEC, eo);
+          if (nib[u]) {
+            uint32_t rr = rr0[u];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if ((nib[u] >> q) & 1u) {
+                if ((int64_t)rr < rlim) bt[rr] = a[q];
+                ++rr;
+              }
+          }
+        }
+        if (own) {  // all lanes of the wave take part in the capture
+          uint32_t kk[4];
+          bool f[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool valid = o[u] + q < tn;
+            kk[q] = valid ? stat_key(ma[u][q], a[q], b1, c1) : 0u;
+            f[q] = valid && kk[q] >= lo;
+          }
+          capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+        }
+      }
+    }
+    if (own) {
+      __syncthreads();
+      if (threadIdx.x == 0) cnt1[(int64_t)p * g.tpp + t] = tcnt;
+    }
+  }
+  if (own) {
+    __syncthreads();
+    hist_merge(sh, hist + (int64_t)p * kBins);
+  }
+}
+
 // SRC 0: key from stat[].  SRC 1: from b1*m + c1*(g^o + e^o).  SRC 2: from
 // b1*m + c1*a^o with a^o rebuilt from the compressed state: b^o at the
 // element's rank on the mask, e'^o off it.
@@ -442,22 +551,23 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
             const float* __restrict__ m, const float* __restrict__ grads, const float* __restrict__ e,
             const float* __restrict__ b, const float* __restrict__ mold, const uint64_t* __restrict__ bits,
             const uint32_t* __restrict__ tile_off, float b1, float c1, uint64_t* __restrict__ cand,
-            uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int tile_step) {
+            uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int tile_step, int64_t g_stride,
+            int64_t e_stride, int64_t b_stride) {
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[kBins];
   __shared__ uint32_t tcnt;
-  const int p = block_part();
+  const int p = g.sp0 + block_part();
   const PartSel st = state[p];
   if (only_fb && !st.fb) return;  // block-uniform
   hist_zero(sh);
   const int64_t pbase = (int64_t)p * g.n_p;
   const int64_t wbase = (int64_t)p * g.wpp;
-  const int64_t pk = (int64_t)g.P * g.k;
   const int o = (int)(((int64_t)p * g.K) / g.P);
-  const float* go = grads + (int64_t)o * g.n + pbase;
-  const float* eo = e + (int64_t)o * g.n + pbase;
-  const float* bo = b + (int64_t)o * pk;
+  // the owner's rows (a row stride of 0: the arrays are that one row)
+  const float* go = grads + (int64_t)o * g_stride + pbase;
+  const float* eo = e + (int64_t)o * e_stride + pbase;
+  const float* bo = b + (int64_t)o * b_stride;
   const uint32_t lo = st.lo_fb;
   const int lane16 = threadIdx.x & 15;
   const int sh4 = 4 * lane16;
@@ -535,15 +645,19 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
 
 template <int SRC, int PHASE>
 void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
-  const dim3 grid = stream_grid(g.P, g.Gs);
+  if (g.snp < 1) return;
+  const dim3 grid = stream_grid(g.snp, g.Gs);
+  const int ts = a.tile_step < 1 ? 1 : a.tile_step;
+  const int64_t pk = (int64_t)g.P * g.k;
+  const int64_t gs = a.single_row ? 0 : g.n, es = a.single_row ? 0 : g.n, bs = a.single_row ? 0 : pk;
   if (vec)
     stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist,
-                                                           a.tile_step < 1 ? 1 : a.tile_step);
+                                                           ts, gs, es, bs);
   else
     stat_kernel<SRC, PHASE, false><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                             a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist,
-                                                           a.tile_step < 1 ? 1 : a.tile_step);
+                                                            ts, gs, es, bs);
 }
 
 }  // namespace
@@ -604,6 +718,20 @@ void launch_step_mode(const Geom& g, const StepArgs& a, bool vec, bool seg, hipS
 
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
   launch_step_mode<kModeAll>(g, a, vec, seg, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_pass(const Geom& g, int rank, const float* grads, float* e, const uint64_t* bits,
+                             const uint32_t* tile_off, float* b, const float* m, float b1, float c1,
+                             const uint32_t* lo, uint64_t* cand, uint32_t* cnt1, uint32_t* hist, bool vec,
+                             hipStream_t s) {
+  const dim3 grid = stream_grid(g.P, g.G);
+  if (vec)
+    shard_pass_kernel<true><<<grid, kThreads, 0, s>>>(g, rank, grads, e, bits, tile_off, b, m, b1, c1, lo, cand, cnt1,
+                                                      hist);
+  else
+    shard_pass_kernel<false><<<grid, kThreads, 0, s>>>(g, rank, grads, e, bits, tile_off, b, m, b1, c1, lo, cand,
+                                                       cnt1, hist);
   return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ struct Geom {
   int idx_bits;       // bits of (n_p - 1), >= 1
   uint32_t idx_mask;  // (1 << idx_bits) - 1
   int nlevels;        // levels after level 1 (level 2 first)
+  int sp0, snp;       // partitions the selection kernels work on: [sp0, sp0 + snp)
   Level levels[8];
   // mask slot: offsets inside one slot, slot size
   size_t off_bits, off_idx, off_toff, off_meta, slot_bytes;
@@ -122,6 +123,7 @@ struct StatArgs {
   uint32_t* cnt1;
   uint32_t* hist;
   int tile_step;  // visit tiles 0, tile_step, 2*tile_step, ... (a sample when > 1)
+  bool single_row;  // grads, e, b are the owner's rows alone (a rank's share), not [K] rows
 };
 
 // Buffers of the selection pipeline (workspace views).
@@ -172,6 +174,13 @@ hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg
 // buffers in worker order, AdamS).  Both forms give the same results, bit
 // for bit.
 bool multi_pass_pays(const Geom& g);
+// One rank's pass of the sharded step: compression of the rank's rows
+// (grads, e: [n]; b: [P*k]) over every partition, statistic and capture on
+// the partitions the rank owns.
+hipError_t launch_shard_pass(const Geom& g, int rank, const float* grads, float* e, const uint64_t* bits,
+                             const uint32_t* tile_off, float* b, const float* m, float b1, float c1,
+                             const uint32_t* lo, uint64_t* cand, uint32_t* cnt1, uint32_t* hist, bool vec,
+                             hipStream_t s);
 hipError_t launch_step_passes(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
 
 hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
@@ -191,9 +200,10 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s);
 
 hipError_t launch_reduce(const Geom& g, const float* b, float* bbar, hipStream_t s);
+// AdamS at idx[0 .. count) with x = bbar[0 .. count) (count < 0: all P*k entries).
 hipError_t launch_adams(const Geom& g, const float* bbar, const uint32_t* idx, float* w, float* m,
                         float* v, float b1, float b2, float c1, float c2, float ibc1, float ibc2,
-                        float eps, float wd, float lr, hipStream_t s);
+                        float eps, float wd, float lr, hipStream_t s, int64_t count = -1);
 // Advances the device-resident bias-correction state by one step.
 hipError_t launch_bias_step(scape_bias_state* st, float b1, float b2, hipStream_t s);
 hipError_t launch_dense_adams(const Geom& g, const float* grads, float* w, float* m, float* v, float b1,

@@ -76,9 +76,9 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
     p[i] = 0u;
 }
 
-__global__ void init_state_kernel(PartSel* state, int P, uint32_t k) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p < P) {
+__global__ void init_state_kernel(PartSel* state, int p0, int np, uint32_t k) {
+  const int p = p0 + blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < p0 + np) {
     PartSel s = fresh_sel(k);
     s.fb = 1;
     state[p] = s;
@@ -97,7 +97,7 @@ level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ sta
   __shared__ int found;
   __shared__ uint32_t s_lo;
   __shared__ int s_dmin;
-  const int p = blockIdx.x;
+  const int p = g.sp0 + blockIdx.x;
   uint32_t* h = hist + (int64_t)p * kBins;
   constexpr int nb = kBins;
   constexpr int shift = 32 + kL1Shift;
@@ -240,7 +240,7 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
   __shared__ uint32_t sh[kBins];
   __shared__ uint32_t smin;
-  const int p = blockIdx.y;
+  const int p = g.sp0 + blockIdx.y;
   const PartSel st = state[p];
   const uint32_t B1 = st.bin1;
   const bool done = st.done != 0;
@@ -520,7 +520,7 @@ l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
                uint32_t target) {
   __shared__ uint32_t wtot[kThreads / 64];
   __shared__ uint32_t s_d, s_c, s_above, s_lo;
-  const int p = blockIdx.x;
+  const int p = g.sp0 + blockIdx.x;
   uint32_t* h = hist + (int64_t)p * kBins;
   const PartSel cur = state[p];
   if (threadIdx.x == 0) nsurv[p] = 0u;
@@ -589,7 +589,7 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
   __shared__ uint32_t sh[1 << (kL1Shift - kDigitBits)];
   __shared__ uint32_t smin;
   constexpr int nb3 = 1 << (kL1Shift - kDigitBits);
-  const int p = blockIdx.y;
+  const int p = g.sp0 + blockIdx.y;
   const PartSel st = state[p];
   if (st.fb || !st.mask || st.done) return;  // block-uniform: nothing left in the bin to walk
   const bool done2 = st.done2 != 0;
@@ -627,8 +627,16 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
         const bool keep = at && !done2;
         const uint64_t kb = __ballot(keep);
         if (kb) {  // wave-uniform
-          uint32_t pos = 0;
-          if (lane == 0) pos = atomicAdd(nsurv + p, (uint32_t)__popcll(kb));
+          // Once the count has passed the cap the list is abandoned and only
+          // "more than the cap" matters, which the count already shows: no
+          // further (contended) atomic.  A wave that reads a count at or
+          // below the cap adds, so the count exceeds the cap exactly when the
+          // candidates do.
+          uint32_t pos = (uint32_t)kSurvivorCap;
+          if (lane == 0) {
+            const uint32_t seen = __hip_atomic_load(nsurv + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (seen <= (uint32_t)kSurvivorCap) pos = atomicAdd(nsurv + p, (uint32_t)__popcll(kb));
+          }
           pos = (uint32_t)__shfl((int)pos, 0, 64) + mbcnt(kb);
           if (keep) {
             atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
@@ -669,7 +677,7 @@ finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
   __shared__ uint32_t spre[kResolveWaves][65];
   __shared__ uint32_t scnt[kResolveWaves][64];
   __shared__ DigitFind sfind;
-  const int p = blockIdx.x;
+  const int p = g.sp0 + blockIdx.x;
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
   PartSel st = state[p];
@@ -824,7 +832,7 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
             const uint32_t* __restrict__ tile_off, uint32_t* __restrict__ idx) {
   __shared__ unsigned long long swords[kThreads / 64][kWordsPerTile];
   __shared__ uint32_t spre[RANKS ? kThreads / 64 : 1][kWordsPerTile];
-  const int p = blockIdx.y;
+  const int p = g.sp0 + blockIdx.y;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= g.tpp) return;  // wave-uniform; the waves synchronise only among their own lanes
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
@@ -983,38 +991,41 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
 }
 
 hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s) {
-  init_state_kernel<<<(g.P + kThreads - 1) / kThreads, kThreads, 0, s>>>(state, g.P, (uint32_t)g.k);
+  if (g.snp < 1) return hipSuccess;
+  init_state_kernel<<<(g.snp + kThreads - 1) / kThreads, kThreads, 0, s>>>(state, g.sp0, g.snp, (uint32_t)g.k);
   return hipGetLastError();
 }
 
 hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target) {
-  level_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, mode, target ? target : capture_target(g));
+  if (g.snp < 1) return hipSuccess;
+  level_scan_kernel<<<g.snp, kThreads, 0, s>>>(g, w.hist, w.state, mode, target ? target : capture_target(g));
   return hipGetLastError();
 }
 
 hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits, uint32_t* idx,
                               uint32_t* tile_off, uint32_t* meta_out, hipStream_t s,
                               void (*mark)(void*, int), void* ctx) {
+  if (g.snp < 1) return hipSuccess;
   // tiles per wave of the passes over candidate slots: kSelectTilesPerWave
   // on large layouts, fewer where that would leave too few waves
-  int64_t tpw = ((int64_t)g.P * g.tpp + kSelectWaves - 1) / kSelectWaves;
+  int64_t tpw = ((int64_t)g.snp * g.tpp + kSelectWaves - 1) / kSelectWaves;
   tpw = tpw < 1 ? 1 : (tpw > kSelectTilesPerWave ? kSelectTilesPerWave : tpw);
   const unsigned sblocks = (unsigned)((g.tpp + 4 * tpw - 1) / (4 * tpw));
-  cand_select_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits,
+  cand_select_kernel<<<dim3(sblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits,
                                                               w.tilecnt);
   if (mark) mark(ctx, 1);
-  l2_scan_kernel<<<g.P, kThreads, 0, s>>>(g, w.hist, w.state, w.nsurv, capture_target(g));
-  bin_walk_kernel<<<dim3(sblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, w.tilecnt, w.hist, w.surv,
+  l2_scan_kernel<<<g.snp, kThreads, 0, s>>>(g, w.hist, w.state, w.nsurv, capture_target(g));
+  bin_walk_kernel<<<dim3(sblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, w.tilecnt, w.hist, w.surv,
                                                           w.nsurv);
-  finish_kernel<<<g.P, kResolveThreads, 0, s>>>(g, w.hist, w.state, w.cand, w.cnt2, w.surv, w.nsurv, w.tilecnt,
+  finish_kernel<<<g.snp, kResolveThreads, 0, s>>>(g, w.hist, w.state, w.cand, w.cnt2, w.surv, w.nsurv, w.tilecnt,
                                                 tile_off, meta_out);
   if (mark) mark(ctx, 2);
   const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
   // rank-parallel emission pays from a mask density of about 5% on
   if (g.k * 20 >= g.n_p)
-    emit_kernel<true><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
+    emit_kernel<true><<<dim3(tblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
   else
-    emit_kernel<false><<<dim3(tblocks, g.P), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
+    emit_kernel<false><<<dim3(tblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
   return hipGetLastError();
 }
 

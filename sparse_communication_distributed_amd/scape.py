@@ -75,6 +75,14 @@ _SIGS = {
     "scape_dense_adams_step": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, Betas, c_float,
                                        c_int64, c_void_p]),
     "scape_mask_check": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, c_void_p, c_void_p]),
+    "scape_shard_partitions": (c_int, [ctypes.POINTER(Dims), c_int32, ctypes.POINTER(c_int32),
+                                       ctypes.POINTER(c_int32)]),
+    "scape_shard_select_initial": (c_int, [ctypes.POINTER(Dims), c_int64, c_int32, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, Betas, c_void_p, c_size_t, c_void_p]),
+    "scape_shard_compress": (c_int, [ctypes.POINTER(Dims), c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, Betas, c_int64, c_void_p, c_size_t, c_void_p]),
+    "scape_shard_update": (c_int, [ctypes.POINTER(Dims), c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, Betas, c_float, c_int64, c_void_p]),
     "scape_status_string": (c_char_p, [c_int]),
     "scape_last_error": (c_char_p, []),
     "scape_profile_stages": (c_int, []),
@@ -344,6 +352,56 @@ def mask_check(d: Dims, k: int, m: MaskView, result=None, stream=None) -> None:
         result = torch.empty(d.num_partitions, dtype=torch.int32, device=torch.cuda.current_device())
     _need(result, "result", d.num_partitions, dtype="int32")
     _check(lib().scape_mask_check(ctypes.byref(d), k, m, _ptr(result), _stream(stream)))
+
+
+# ---------------------------------------------------- one rank's share
+
+
+def shard_partitions(d: Dims, rank: int):
+    """(first, count): the partitions rank `rank` owns."""
+    first, count = c_int32(), c_int32()
+    _check(lib().scape_shard_partitions(ctypes.byref(d), rank, ctypes.byref(first), ctypes.byref(count)))
+    return first.value, count.value
+
+
+def shard_select_initial(d: Dims, k: int, rank: int, grads, e, m, mask_blob, bt: Betas, workspace,
+                         stream=None) -> None:
+    """scape_shard_select_initial: M_1 on the rank's partitions (slot 0);
+    grads and e are the rank's rows [n]."""
+    _need(grads, "grads", d.n)
+    _need(e, "e", d.n)
+    _need(m, "m", d.n)
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _need(workspace, "workspace", workspace_bytes(d, k), dtype=None)
+    _check(lib().scape_shard_select_initial(ctypes.byref(d), k, rank, _ptr(grads), _ptr(e), _ptr(m), _ptr(mask_blob),
+                                            bt, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
+
+
+def shard_compress(d: Dims, k: int, rank: int, grads, e, m, b, mask_blob, bt: Betas, step_no: int, workspace,
+                   stream=None) -> None:
+    """scape_shard_compress: the rank's rows (grads, e [n]) compressed at
+    M_t into b [P*k]; M_{t+1} selected on the rank's partitions."""
+    _need(grads, "grads", d.n)
+    _need(e, "e", d.n)
+    _need(m, "m", d.n)
+    _need(b, "b", _pk(d, k))
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _need(workspace, "workspace", workspace_bytes(d, k), dtype=None)
+    _check(lib().scape_shard_compress(ctypes.byref(d), k, rank, _ptr(grads), _ptr(e), _ptr(m), _ptr(b),
+                                      _ptr(mask_blob), bt, step_no, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def shard_update(d: Dims, k: int, rank: int, params, m, v, b_bar, mask_blob, bt: Betas, lr: float, step_no: int,
+                 stream=None) -> None:
+    """scape_shard_update: AdamS at M_t on the rank's partitions from b_bar,
+    the synchronised buffer of those partitions (count*k entries)."""
+    _need_state(d, params, m, v)
+    _need(b_bar, "b_bar", shard_partitions(d, rank)[1] * int(k))
+    _need(mask_blob, "mask_blob", mask_bytes(d, k), dtype=None)
+    _check(lib().scape_shard_update(ctypes.byref(d), k, rank, _ptr(params), _ptr(m), _ptr(v), _ptr(b_bar),
+                                    _ptr(mask_blob), bt, lr, step_no, _stream(stream)))
 
 
 def mask_overlap(d: Dims, k: int, a: MaskView, b: MaskView, count_out, stream=None) -> None:

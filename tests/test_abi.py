@@ -292,3 +292,39 @@ def test_step_noalloc_rejects_dims_beyond_its_static_scratch():
     assert L.scape_step_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, S.betas(), 1e-3, 1, None) == 1
     assert L.scape_step_noalloc(ctypes.byref(S.dims(100, 3, 1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
                                 S.betas(), 1e-3, 1, None) == 2
+
+
+@pytest.mark.parametrize("P,K", [(32, 8), (6, 4), (5, 3), (3, 5), (1, 1), (7, 7)])
+def test_shard_partitions_are_the_owners(P, K):
+    """Rank r owns exactly the partitions p with floor(p*K/P) == r, as one
+    contiguous range; the ranges tile [0, P)."""
+    d = S.dims(P * 64, P, K)
+    seen = []
+    for r in range(K):
+        first, count = S.shard_partitions(d, r)
+        assert list(range(first, first + count)) == [p for p in range(P) if (p * K) // P == r]
+        seen += list(range(first, first + count))
+    assert seen == list(range(P))
+    with pytest.raises(S.ScapeError):
+        S.shard_partitions(d, K)
+    with pytest.raises(S.ScapeError):
+        S.shard_partitions(d, -1)
+
+
+def test_shard_calls_validate_before_any_hip_call():
+    L = S.lib()
+    d = S.dims(4096, 4, 2)
+    bt = S.betas()
+    assert L.scape_shard_compress(ctypes.byref(d), 10, 2, FAKE, FAKE, FAKE, FAKE, FAKE, bt, 1, FAKE, 1 << 30,
+                                  None) == 1  # rank out of range
+    assert L.scape_shard_compress(ctypes.byref(d), 10, 0, FAKE, FAKE, FAKE, FAKE, FAKE, bt, 0, FAKE, 1 << 30,
+                                  None) == 1  # step 0
+    assert L.scape_shard_compress(ctypes.byref(d), 10, 0, FAKE, FAKE, FAKE, FAKE, FAKE, bt, 1, FAKE, 16,
+                                  None) == 3  # workspace too small
+    assert L.scape_shard_select_initial(ctypes.byref(d), 2000, 0, FAKE, FAKE, FAKE, FAKE, bt, FAKE, 1 << 30,
+                                        None) == 2  # k > n_p
+    assert L.scape_shard_update(ctypes.byref(d), 10, 1, FAKE, FAKE, None, None, FAKE, bt, 1e-3, 1, None) == 1
+    # a rank that owns no partition (K > P) may pass no b_bar
+    d3 = S.dims(300, 3, 5)
+    assert S.shard_partitions(d3, 2) == (2, 0)
+    assert L.scape_shard_update(ctypes.byref(d3), 10, 2, FAKE, FAKE, None, None, FAKE, bt, 1e-3, 1, None) == 0

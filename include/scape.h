@@ -396,6 +396,19 @@ scape_status scape_mask_union(const scape_dims* dims, int64_t k, uint64_t* acc_b
 scape_status scape_mask_check(const scape_dims* dims, int64_t k, scape_mask_view m, uint32_t* result,
                               hipStream_t stream);
 
+/*
+ * Debug count of non-finite inputs: *nonfinite_out (device u64) += the
+ * number of NaN and +-inf values among x[0 .. count-1] (device fp32, any
+ * alignment).  The pages' workloads are finite; the step computes on
+ * whatever it is given (a NaN statistic sorts above +inf in the selection,
+ * NaN and inf propagate through the compression and AdamS), so a caller
+ * that wants its gradients checked calls this on them before the step, on
+ * the same stream.  It accumulates: the caller zeroes the counter, and one
+ * counter can cover several arrays.  count 0 launches nothing; count < 0,
+ * or a null x or counter with count > 0, is SCAPE_EINVAL.
+ */
+scape_status scape_count_nonfinite(const float* x, int64_t count, uint64_t* nonfinite_out, hipStream_t stream);
+
 /* -------------------------------------------------------------- utility */
 
 const char* scape_status_string(scape_status s);

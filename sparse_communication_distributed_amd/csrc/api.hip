@@ -856,6 +856,13 @@ scape_status scape_mask_union(const scape_dims* dims, int64_t k, uint64_t* acc_b
   return hip_check(launch_union(g, acc_bits, m.bits, count_out, stream), "union");
 }
 
+scape_status scape_count_nonfinite(const float* x, int64_t count, uint64_t* nonfinite_out, hipStream_t stream) {
+  if (count < 0) return fail(SCAPE_EINVAL, "count must be >= 0");
+  if (count == 0) return SCAPE_OK;
+  if (!x || !nonfinite_out) return fail(SCAPE_EINVAL, "null pointer argument");
+  return hip_check(launch_count_nonfinite(x, count, nonfinite_out, stream), "count non-finite");
+}
+
 scape_status scape_mask_check(const scape_dims* dims, int64_t k, scape_mask_view m, uint32_t* result,
                               hipStream_t stream) {
   Geom g;

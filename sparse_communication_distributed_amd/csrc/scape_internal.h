@@ -218,6 +218,8 @@ constexpr uint32_t kMaskBadPad = 8;    // bits set past n_p
 hipError_t launch_mask_check(const Geom& g, const uint64_t* bits, const uint32_t* idx, const uint32_t* tile_off,
                              const uint32_t* meta, uint32_t* res, hipStream_t s);
 hipError_t launch_union(const Geom& g, uint64_t* acc, const uint64_t* m, uint64_t* out, hipStream_t s);
+// *out += the number of NaN and +-inf values among x[0 .. n-1].
+hipError_t launch_count_nonfinite(const float* x, int64_t n, uint64_t* out, hipStream_t s);
 hipError_t launch_overlap(const Geom& g, const uint64_t* a, const uint64_t* b, uint64_t* out,
                           hipStream_t s);
 

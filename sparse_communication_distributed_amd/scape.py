@@ -67,6 +67,7 @@ _SIGS = {
     "scape_step_graph": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_int64, Betas, c_float, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "scape_mask_overlap": (c_int, [ctypes.POINTER(Dims), c_int64, MaskView, MaskView, c_void_p, c_void_p]),
+    "scape_count_nonfinite": (c_int, [c_void_p, c_int64, c_void_p, c_void_p]),
     "scape_offload_stage_bytes": (c_size_t, [ctypes.POINTER(Dims), c_int64, c_int32]),
     "scape_step_offload": (c_int, [ctypes.POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int64, Betas, c_float, c_int64, c_void_p, c_size_t, c_void_p, c_size_t, c_int32,
@@ -404,6 +405,16 @@ def shard_update(d: Dims, k: int, rank: int, params, m, v, b_bar, mask_blob, bt:
                                     _ptr(mask_blob), bt, lr, step_no, _stream(stream)))
 
 
+def count_nonfinite(x, count_out, count=None, stream=None) -> None:
+    """count_out (device u64 / int64 tensor of one element) += the number of
+    NaN and +-inf values among the first `count` (default: all) fp32
+    elements of x (device)."""
+    c = x.numel() if count is None else int(count)
+    _need(x, "x", max(c, 0))
+    _need(count_out, "count_out", 8, dtype=None)
+    _check(lib().scape_count_nonfinite(_ptr(x), c, _ptr(count_out), _stream(stream)))
+
+
 def mask_overlap(d: Dims, k: int, a: MaskView, b: MaskView, count_out, stream=None) -> None:
     _need(count_out, "count_out", 8, dtype=None)
     _check(lib().scape_mask_overlap(ctypes.byref(d), k, a, b, _ptr(count_out), _stream(stream)))
@@ -442,10 +453,11 @@ class ScapeOptimizer:
     grads [K][n] (fp32, device).  AdamS keeps no second moment (v_t is
     rebuilt every step); with ``store_v`` the step also writes the
     uncorrected v_t at the masked entries into ``v`` [n], else ``v`` is
-    None."""
+    None.  With ``count_nonfinite`` each step first counts the non-finite
+    values of its gradients on the device (``nonfinite_count()``)."""
 
     def __init__(self, params, P: int, K: int, k: int, beta1=0.9, beta2=0.95, eps=1e-8,
-                 weight_decay=0.0, lr=1e-3, device=None, store_v: bool = True):
+                 weight_decay=0.0, lr=1e-3, device=None, store_v: bool = True, count_nonfinite: bool = False):
         import torch
         self.n = params.numel()
         self.d = dims(self.n, P, K)
@@ -463,13 +475,25 @@ class ScapeOptimizer:
             raise ScapeError(2, f"invalid shape n={self.n} P={P} K={K} k={k}")
         self.mask = torch.zeros(mb, dtype=torch.uint8, device=dev)
         self.ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+        # debug switch: non-finite gradient values seen by the steps so far
+        self.nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
         self.t = 0
 
     def step(self, grads, stream=None) -> None:
         t = self.t + 1
+        if self.nonfinite is not None:
+            count_nonfinite(grads, self.nonfinite, self.K * self.n, stream)
         step(self.d, self.params, grads, self.m, self.v, self.e, self.mask, self.k, self.bt, self.lr,
              t, self.ws, stream)
         self.t = t  # a rejected call leaves the step count unchanged
+
+    def nonfinite_count(self) -> int:
+        """Non-finite gradient values the steps were given (NaN, +-inf),
+        with the optimizer built with count_nonfinite=True; waits for the
+        device."""
+        if self.nonfinite is None:
+            raise ValueError("the optimizer was built without count_nonfinite")
+        return int(self.nonfinite.item())
 
     def check(self, which: str = "next", stream=None) -> None:
         """Validates mask M_{t+1} ("next") or M_t ("current") against the

@@ -192,6 +192,17 @@ def test_component_validation():
     assert L.scape_mask_topk(None, 10, FAKE, mv, FAKE, ws, None) == 1
 
 
+def test_count_nonfinite_validation():
+    """The debug count of non-finite inputs checks its arguments before any
+    HIP call: a negative count, or a null array or counter with elements to
+    count, is EINVAL; an empty array launches nothing."""
+    L = S.lib()
+    assert L.scape_count_nonfinite(FAKE, -1, FAKE, None) == 1
+    assert L.scape_count_nonfinite(None, 5, FAKE, None) == 1
+    assert L.scape_count_nonfinite(FAKE, 5, None, None) == 1
+    assert L.scape_count_nonfinite(None, 0, None, None) == 0
+
+
 def test_offload_validation():
     L = S.lib()
     d = S.dims(4096, 4, 2)

@@ -398,6 +398,27 @@ def test_step_multi_pass_mixed_tensors(S, n_p, P, K, sp, store_v):
     run_lockstep(S, cfg, cfg.steps, store_v=store_v)
 
 
+@pytest.mark.parametrize("K,store_v", [(8, True), (12, False)])
+def test_step_multi_pass_dense_waves(S, K, store_v):
+    """The K-pass form where the mask crowds into one region of each
+    partition (gradients scaled by 1000 on 300 elements): 256-element chunks
+    then hold more than 128 masked elements, so the owner pass gathers the
+    other workers' values in several rounds of 64."""
+    n_p, P = 8192, 4
+    cfg = W.flat_config("mpdense", P * n_p, P, K, "0.98", steps=4, weight_decay=0.01)
+    assert S.step_pass_count(S.dims(cfg.n, P, K), cfg.k) == K
+    lo = 1000
+
+    def grads(t):
+        g = W.grads(cfg, t).copy()
+        for p in range(P):
+            g[:, p * n_p + lo:p * n_p + lo + 300] *= np.float32(1000.0)
+        return g
+
+    _, ora = run_lockstep(S, cfg, cfg.steps, grad_fn=grads, store_v=store_v)
+    assert max(int(np.bincount(st.idx // 256).max()) for st in ora.parts) > 128
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_step_multi_pass_60_steps(S):
@@ -870,3 +891,39 @@ def test_mask_check_passes_the_steps_masks(S):
     mv.meta = None
     S.mask_topk(d, cfg.k, dev(W.grads(cfg, 9)[0]), mv, opt.ws)
     S.mask_check(d, cfg.k, mv)
+
+
+@pytest.mark.parametrize("n,offset", [(1, 0), (4099, 1), (1 << 20, 0), (3 * 4096 + 7, 3)])
+def test_count_nonfinite(S, n, offset):
+    """The debug count of non-finite inputs: NaN (both signs), +inf and -inf
+    planted on the host are counted, and the finite extremes (largest
+    normal, a subnormal, -0) are not, at unaligned starts and ragged
+    lengths; a second call on a prefix adds to the same counter."""
+    rng = np.random.default_rng(n + offset)
+    x = rng.standard_normal(n + offset).astype(np.float32)
+    pos = rng.choice(n, min(n, 40), replace=False) + offset
+    kinds = np.array([np.nan, np.inf, -np.inf, -np.nan], dtype=np.float32)
+    x[pos[:len(pos) // 2 + 1]] = kinds[np.arange(len(pos) // 2 + 1) % 4]
+    fin = np.array([np.finfo(np.float32).max, -np.finfo(np.float32).max, 1e-40, -0.0], dtype=np.float32)
+    x[pos[len(pos) // 2 + 1:]] = fin[np.arange(len(pos) - len(pos) // 2 - 1) % 4]
+    xd = dev(x)[offset:]
+    cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    S.count_nonfinite(xd, cnt)
+    S.count_nonfinite(xd, cnt, count=n // 2)
+    torch.cuda.synchronize()
+    want = int(np.sum(~np.isfinite(x[offset:]))) + int(np.sum(~np.isfinite(x[offset:offset + n // 2])))
+    assert int(cnt.item()) == want
+
+
+def test_optimizer_counts_nonfinite_gradients(S):
+    """With the debug switch, a NaN and an inf injected into the gradients on
+    the host are reported after the step that received them."""
+    cfg = W.flat_config("nonfinite", 4 * 4096, 4, 2, "0.9", steps=2)
+    opt = S.ScapeOptimizer(dev(W.init_params(cfg)), cfg.P, cfg.K, cfg.k, count_nonfinite=True)
+    opt.step(dev(W.grads(cfg, 1)))
+    assert opt.nonfinite_count() == 0
+    g = W.grads(cfg, 2).copy()
+    g[1, 123] = np.nan
+    g[0, cfg.n - 1] = np.inf
+    opt.step(dev(g))
+    assert opt.nonfinite_count() == 2

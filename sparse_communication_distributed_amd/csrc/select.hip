@@ -29,6 +29,11 @@ __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
 // Chunks of 64 candidates a wave loads per round when it walks a slot.
 constexpr int kCandChunks = 4;
+// Tiles each wave of the sparse-mask emission takes, their loads issued
+// together (the rank-parallel emission of denser masks takes one: there a
+// tile's index writes dominate and more waves pay).
+constexpr int kEmitTiles = 4;
+__host__ __device__ constexpr int emit_tiles(bool ranks) { return ranks ? 1 : kEmitTiles; }
 
 // Exclusive scan over a block of kThreads (4 waves); `wtot` is LDS [4].
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
@@ -814,8 +819,10 @@ __device__ __forceinline__ uint32_t select_bit(uint64_t word, uint32_t r) {
   return pos;
 }
 
-// One wave per tile: completes the tile's mask words and writes its global
-// indices in order.  The threshold bin's candidates of the tile at or above
+// Each wave takes emit_tiles(RANKS) consecutive tiles (with the loads they
+// need issued together), and for each completes the tile's mask words and writes
+// its global indices in order.  The threshold bin's candidates of the tile
+// at or above
 // T (the resolved threshold composite) are assembled in LDS and ORed into
 // the words (written back only where bits were added; this wave is the only
 // writer of its tile's words).  Then, with the tile's offset:
@@ -832,66 +839,98 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
             const uint32_t* __restrict__ tile_off, uint32_t* __restrict__ idx) {
   __shared__ unsigned long long swords[kThreads / 64][kWordsPerTile];
   __shared__ uint32_t spre[RANKS ? kThreads / 64 : 1][kWordsPerTile];
+  constexpr int ET = emit_tiles(RANKS);
   const int p = g.sp0 + blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (t >= g.tpp) return;  // wave-uniform; the waves synchronise only among their own lanes
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  // the wave's tiles tw .. tw + ET - 1
+  const int64_t tw = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * ET;
+  if (tw >= g.tpp) return;  // wave-uniform; the waves synchronise only among their own lanes
   unsigned long long* wd = swords[wave];
-  const int64_t w = t * kWordsPerTile + lane;
   uint64_t* wb = bits + (int64_t)p * g.wpp;
-  uint64_t word = (w < g.wpp) ? wb[w] : 0ull;
-  uint32_t ct = cnt2[(int64_t)p * g.tpp + t];
-  if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
-  const int64_t base = (int64_t)tile_off[(int64_t)p * g.tpp + t];
-  if (ct) {  // wave-uniform
-    const uint64_t T = state[p].prefix;
-    wd[lane] = 0ull;
-    wave_lds_sync();
-    const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-    const uint32_t tile_lo = (uint32_t)(t * kTile);
-    for_each_cand(slot, ct, lane, [&](uint64_t c) {
-      const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
-      if (c >= T && jl < (uint32_t)kTile) atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
-    });
-    wave_lds_sync();
-    const uint64_t add = wd[lane];
-    if (add && w < g.wpp) {
-      word |= add;
-      wb[w] = word;
-    }
-    wave_lds_sync();
-  }
-  const uint32_t c = (uint32_t)__popcll(word);
-  uint32_t x = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if ((int)lane >= d) x += y;
-  }
   uint32_t* out = idx + (int64_t)p * g.k;
-  if (!RANKS) {
-    int64_t pos = base + (x - c);
-    const uint32_t jbase = (uint32_t)((int64_t)p * g.n_p + w * 64);
-    while (word) {
-      if (pos < g.k) out[pos] = jbase + (uint32_t)__builtin_ctzll(word);  // bound: malformed mask
-      ++pos;
-      word &= word - 1ull;
-    }
-    return;
-  }
-  const uint32_t sw = RANKS ? wave : 0u;  // this wave's rows of the LDS arrays
-  wd[lane] = word;
-  spre[sw][lane] = x - c;
-  const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
-  wave_lds_sync();
-  const uint32_t tbase = (uint32_t)((int64_t)p * g.n_p + t * kTile);
-  for (uint32_t r = lane; r < total; r += 64) {
-    uint32_t q = 0;
+  const uint64_t T = state[p].prefix;
+  // Every load the wave's tiles need before their words are complete is
+  // issued up front: the words, the candidate counts and offsets (lane j:
+  // tile j), then the first 64 candidates of each tile.
+  uint64_t words[ET];
 #pragma unroll
-    for (uint32_t step = 32; step >= 1; step >>= 1)
-      if (spre[sw][q + step] <= r) q += step;
-    const uint32_t j = select_bit(wd[q], r - spre[sw][q]);
-    if (base + r < g.k) out[base + r] = tbase + q * 64 + j;  // bound: malformed mask
+  for (int j = 0; j < ET; ++j) {
+    const int64_t w = (tw + j) * kWordsPerTile + lane;
+    words[j] = (tw + j < g.tpp && w < g.wpp) ? wb[w] : 0ull;
+  }
+  // one tile: wave-uniform (scalar) loads; several: lane j loads tile j's
+  const int64_t tl = tw + (ET == 1 ? 0 : lane);
+  const bool lt = (ET == 1 || lane < (uint32_t)ET) && tl < g.tpp;
+  uint32_t ctl = lt ? cnt2[(int64_t)p * g.tpp + tl] : 0u;
+  if (ctl > (uint32_t)kTile) ctl = (uint32_t)kTile;  // a slot holds at most one tile
+  const uint32_t bl = lt ? tile_off[(int64_t)p * g.tpp + tl] : 0u;
+  auto of_tile = [&](uint32_t v, int j) { return ET == 1 ? v : (uint32_t)__shfl((int)v, j, 64); };
+  uint64_t c0[ET];
+#pragma unroll
+  for (int j = 0; j < ET; ++j) {
+    const uint32_t ct = of_tile(ctl, j);
+    const uint64_t* slot = cand + ((int64_t)p * g.tpp + tw + j) * kTile;
+    c0[j] = (lane < ct) ? slot[lane] : 0ull;
+  }
+#pragma unroll
+  for (int j = 0; j < ET; ++j) {
+    const int64_t t = tw + j;
+    if (t >= g.tpp) break;  // wave-uniform
+    const int64_t w = t * kWordsPerTile + lane;
+    const uint32_t ct = of_tile(ctl, j);
+    const int64_t base = (int64_t)of_tile(bl, j);
+    uint64_t word = words[j];
+    if (ct) {  // wave-uniform
+      wd[lane] = 0ull;
+      wave_lds_sync();
+      const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+      const uint32_t tile_lo = (uint32_t)(t * kTile);
+      auto take = [&](uint64_t c) {
+        const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
+        if (c >= T && jl < (uint32_t)kTile) atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+      };
+      if (lane < ct) take(c0[j]);
+      if (ct > 64u) for_each_cand(slot + 64, ct - 64u, lane, take);  // wave-uniform
+      wave_lds_sync();
+      const uint64_t add = wd[lane];
+      if (add && w < g.wpp) {
+        word |= add;
+        wb[w] = word;
+      }
+      wave_lds_sync();
+    }
+    const uint32_t c = (uint32_t)__popcll(word);
+    uint32_t x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(x, d, 64);
+      if ((int)lane >= d) x += y;
+    }
+    if (!RANKS) {
+      int64_t pos = base + (x - c);
+      const uint32_t jbase = (uint32_t)((int64_t)p * g.n_p + w * 64);
+      while (word) {
+        if (pos < g.k) out[pos] = jbase + (uint32_t)__builtin_ctzll(word);  // bound: malformed mask
+        ++pos;
+        word &= word - 1ull;
+      }
+      continue;
+    }
+    const uint32_t sw = RANKS ? wave : 0u;  // this wave's rows of the LDS arrays
+    wd[lane] = word;
+    spre[sw][lane] = x - c;
+    const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
+    wave_lds_sync();
+    const uint32_t tbase = (uint32_t)((int64_t)p * g.n_p + t * kTile);
+    for (uint32_t r = lane; r < total; r += 64) {
+      uint32_t q = 0;
+#pragma unroll
+      for (uint32_t step = 32; step >= 1; step >>= 1)
+        if (spre[sw][q + step] <= r) q += step;
+      const uint32_t jj = select_bit(wd[q], r - spre[sw][q]);
+      if (base + r < g.k) out[base + r] = tbase + q * 64 + jj;  // bound: malformed mask
+    }
+    wave_lds_sync();  // the next tile rewrites this wave's LDS rows
   }
 }
 
@@ -1020,9 +1059,11 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
   finish_kernel<<<g.snp, kResolveThreads, 0, s>>>(g, w.hist, w.state, w.cand, w.cnt2, w.surv, w.nsurv, w.tilecnt,
                                                 tile_off, meta_out);
   if (mark) mark(ctx, 2);
-  const unsigned tblocks = (unsigned)((g.tpp + 3) / 4);
   // rank-parallel emission pays from a mask density of about 5% on
-  if (g.k * 20 >= g.n_p)
+  const bool ranks = g.k * 20 >= g.n_p;
+  const int et = 4 * emit_tiles(ranks);  // tiles per block
+  const unsigned tblocks = (unsigned)((g.tpp + et - 1) / et);
+  if (ranks)
     emit_kernel<true><<<dim3(tblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);
   else
     emit_kernel<false><<<dim3(tblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, bits, tile_off, idx);

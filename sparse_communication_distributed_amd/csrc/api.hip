@@ -73,6 +73,7 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   r.ws_tilecnt = o; o = align256(o + (size_t)P * r.tpp * 4);
   r.ws_surv = o;    o = align256(o + (size_t)P * kSurvivorCap * 8);
   r.ws_nsurv = o;   o = align256(o + (size_t)P * 4);
+  r.ws_arrive = o;  o = align256(o + (size_t)P * 4);
   r.ws_total = o;
   *g = r;
   return true;
@@ -188,6 +189,7 @@ Ws ws_view(const Geom& g, void* ws) {
   w.sel.tilecnt = reinterpret_cast<uint32_t*>(c + g.ws_tilecnt);
   w.sel.surv = reinterpret_cast<uint64_t*>(c + g.ws_surv);
   w.sel.nsurv = reinterpret_cast<uint32_t*>(c + g.ws_nsurv);
+  w.sel.arrive = reinterpret_cast<uint32_t*>(c + g.ws_arrive);
   return w;
 }
 
@@ -239,8 +241,10 @@ void select_mark(void* ctx, int id) {
 }
 
 // Level 1 with the exact fallback: for partitions flagged in the state,
-// count every key (source `src`), bound the capture at the threshold digit,
-// recapture, and redo level 1 on the recaptured keys.
+// count every key (source `src`) and bound the capture at the threshold
+// digit (the pass's last block per partition), then recapture and redo
+// level 1 on the recaptured keys (likewise): two launches, which do nothing
+// but read the state where no partition is flagged.
 scape_status run_fallback(const Geom& g, const Ws& w, int src, StatArgs a, bool vec, hipStream_t s) {
   scape_status st;
   a.state = w.sel.state;
@@ -248,10 +252,12 @@ scape_status run_fallback(const Geom& g, const Ws& w, int src, StatArgs a, bool 
   a.cand = w.sel.cand;
   a.cnt1 = w.sel.cnt1;
   a.hist = w.sel.hist;
+  a.arrive = w.sel.arrive;
+  a.target = capture_target(g);
+  a.then_mode = kScanBound;
   if ((st = hip_check(launch_stat(g, src, kPhaseHist, a, vec, s), "fallback count"))) return st;
-  if ((st = hip_check(launch_level1(g, w.sel, kScanBound, s), "fallback bound"))) return st;
-  if ((st = hip_check(launch_stat(g, src, kPhaseCapture, a, vec, s), "fallback capture"))) return st;
-  return hip_check(launch_level1(g, w.sel, kScanFinal, s), "fallback level 1");
+  a.then_mode = kScanFinal;
+  return hip_check(launch_stat(g, src, kPhaseCapture, a, vec, s), "fallback capture");
 }
 
 scape_status run_tail(const Geom& g, const Ws& w, scape_mask_view out, hipStream_t s, bool prof) {
@@ -272,7 +278,7 @@ scape_status run_fresh_select(const Geom& g, const Ws& w, int src, const StatArg
   scape_status st;
   if ((st = hip_check(launch_zero_u32(w.sel.hist + (int64_t)g.sp0 * kBins, (int64_t)g.snp * kBins, s), "zero")))
     return st;
-  if ((st = hip_check(launch_init_state(g, w.sel.state, s), "init"))) return st;
+  if ((st = hip_check(launch_init_state(g, w.sel, s), "init"))) return st;
   if (g.tpp >= 4 * kSampleStep) {
     StatArgs b = a;
     b.state = w.sel.state;

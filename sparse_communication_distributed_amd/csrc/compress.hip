@@ -22,7 +22,7 @@
 // elements 4*tid .. 4*tid+3 of each 1024-element chunk, so every global
 // access is a 16-byte-per-lane coalesced load or store when vector access
 // is possible (n_p % 4 == 0 and 16-byte aligned bases).
-#include "scape_internal.h"
+#include "level1.h"
 
 #pragma clang fp contract(off)
 
@@ -547,12 +547,12 @@ shard_pass_kernel(Geom g, int rank, const float* __restrict__ grads, float* __re
 // are skipped.
 template <int SRC, int PHASE, bool VEC>
 __global__ void __launch_bounds__(kThreads)
-stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float* __restrict__ stat,
+stat_kernel(Geom g, PartSel* __restrict__ state, int only_fb, const float* __restrict__ stat,
             const float* __restrict__ m, const float* __restrict__ grads, const float* __restrict__ e,
             const float* __restrict__ b, const float* __restrict__ mold, const uint64_t* __restrict__ bits,
             const uint32_t* __restrict__ tile_off, float b1, float c1, uint64_t* __restrict__ cand,
             uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int tile_step, int64_t g_stride,
-            int64_t e_stride, int64_t b_stride) {
+            int64_t e_stride, int64_t b_stride, int then_mode, uint32_t target, uint32_t* __restrict__ arrive) {
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[kBins];
@@ -640,7 +640,26 @@ stat_kernel(Geom g, const PartSel* __restrict__ state, int only_fb, const float*
     }
   }
   __syncthreads();
-  hist_merge(sh, hist + (int64_t)p * kBins);
+  uint32_t* gh = hist + (int64_t)p * kBins;
+  hist_merge(sh, gh);
+  if (!then_mode) return;  // kernel-uniform
+  // The last of the partition's blocks to arrive (its histogram now holds
+  // every block's counts) runs level 1 on it, zeroes its bins and resets
+  // the arrival count.
+  __shared__ int last;
+  __threadfence();  // this block's histogram atomics before its arrival
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(arrive + p, 1u) == (uint32_t)blocks_per_part() - 1u;
+  __syncthreads();
+  if (!last) return;  // block-uniform
+  __threadfence();
+  for (int i = threadIdx.x; i < kBins; i += kThreads)
+    sh[i] = __hip_atomic_load(gh + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  level1_block(g, p, sh, state, then_mode, target);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += kThreads) gh[i] = 0u;
+  if (threadIdx.x == 0) arrive[p] = 0u;
 }
 
 template <int SRC, int PHASE>
@@ -653,11 +672,11 @@ void launch_stat_t(const Geom& g, const StatArgs& a, bool vec, hipStream_t s) {
   if (vec)
     stat_kernel<SRC, PHASE, true><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                            a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist,
-                                                           ts, gs, es, bs);
+                                                           ts, gs, es, bs, a.then_mode, a.target, a.arrive);
   else
     stat_kernel<SRC, PHASE, false><<<grid, kThreads, 0, s>>>(g, a.state, a.only_fb, a.stat, a.m, a.grads, a.e, a.b,
                                                             a.mold, a.bits, a.tile_off, a.b1, a.c1, a.cand, a.cnt1, a.hist,
-                                                            ts, gs, es, bs);
+                                                            ts, gs, es, bs, a.then_mode, a.target, a.arrive);
 }
 
 }  // namespace

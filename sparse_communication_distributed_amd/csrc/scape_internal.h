@@ -101,14 +101,15 @@ struct Geom {
   // mask slot: offsets inside one slot, slot size
   size_t off_bits, off_idx, off_toff, off_meta, slot_bytes;
   // workspace offsets and total
-  size_t ws_b, ws_mold, ws_hist, ws_cand, ws_cnt1, ws_cnt2, ws_state, ws_tilecnt, ws_surv, ws_nsurv, ws_total;
+  size_t ws_b, ws_mold, ws_hist, ws_cand, ws_cnt1, ws_cnt2, ws_state, ws_tilecnt, ws_surv, ws_nsurv, ws_arrive,
+      ws_total;
 };
 
 // Returns false if dims/k are outside the limits.
 bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g);
 
 struct StatArgs {
-  const PartSel* state;
+  PartSel* state;
   int only_fb;
   const float* stat;
   const float* m;
@@ -124,6 +125,13 @@ struct StatArgs {
   uint32_t* hist;
   int tile_step;  // visit tiles 0, tile_step, 2*tile_step, ... (a sample when > 1)
   bool single_row;  // grads, e, b are the owner's rows alone (a rank's share), not [K] rows
+  // The fallback's passes (only_fb): after a partition's blocks have all
+  // merged their histograms, the last to arrive runs level 1 in this mode
+  // (kScanBound or kScanFinal; 0: none) with `target`, counting arrivals in
+  // arrive[p] (zero before the pass, and left zero).
+  int then_mode;
+  uint32_t target;
+  uint32_t* arrive;
 };
 
 // Buffers of the selection pipeline (workspace views).
@@ -136,6 +144,7 @@ struct SelectBufs {
   uint32_t* tilecnt;  // [P][tiles] selected elements per tile
   uint64_t* surv;     // [P][kSurvivorCap] candidates at the level-2 threshold digit
   uint32_t* nsurv;    // [P] their counts
+  uint32_t* arrive;   // [P] blocks arrived in a fallback pass
 };
 
 // ---- launch wrappers (each returns hipGetLastError() of its launches) ----
@@ -183,7 +192,9 @@ hipError_t launch_shard_pass(const Geom& g, int rank, const float* grads, float*
                              hipStream_t s);
 hipError_t launch_step_passes(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
 
-hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s);
+hipError_t launch_init_state(const Geom& g, const SelectBufs& w, hipStream_t s);
+// kCaptureMargin * k, at most n_p.
+uint32_t capture_target(const Geom& g);
 // target 0: the capture target of a step (kCaptureMargin * k)
 hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target = 0);
 // From level-1 digits to the mask: candidate select pass (writes every mask

@@ -16,16 +16,15 @@
 // digit are selected and written as whole mask words, the threshold
 // digit's captures are compacted in place and histogrammed on the level-2
 // digit (key bits 18..7).  One block per partition then resolves the
-// remaining levels (key bits 6..0, then the index bits) on those few.  The
-// emission marks the threshold bin's selected candidates, turns the words
-// into per-tile offsets (a single-pass scan with decoupled lookback) and
-// writes the ascending index list.
-#include "scape_internal.h"
+// remaining levels (key bits 6..0, then the index bits) on those few and
+// scans the per-tile counts into tile offsets.  The emission marks the
+// threshold bin's selected candidates in the words and writes the
+// ascending index list.
+#include "level1.h"
 
 namespace scape {
 namespace {
 
-__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
 // Chunks of 64 candidates a wave loads per round when it walks a slot.
 constexpr int kCandChunks = 4;
@@ -35,34 +34,7 @@ constexpr int kCandChunks = 4;
 constexpr int kEmitTiles = 4;
 __host__ __device__ constexpr int emit_tiles(bool ranks) { return ranks ? 1 : kEmitTiles; }
 
-// Exclusive scan over a block of kThreads (4 waves); `wtot` is LDS [4].
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
-  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if ((int)lane >= d) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) wtot[wave] = x;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    if (w < (int)wave) off += wtot[w];
-    tot += wtot[w];
-  }
-  *total = tot;
-  return off + x - v;
-}
 
-__device__ __forceinline__ PartSel fresh_sel(uint32_t k) {
-  PartSel s;
-  s.prefix = 0; s.mask = 0; s.r = k; s.done = 0; s.bin1 = 0; s.fault = 0; s.fb = 0; s.lo_fb = 0;
-  s.kth = 0xffffffffu; s.c1 = 0; s.lo_next = 0; s.bin2 = 0; s.done2 = 0; s.pad = 0;
-  return s;
-}
 
 // Block-wide minimum folded into *dst with one atomic per block.
 __device__ __forceinline__ void block_min_into(uint32_t v, uint32_t* smin, uint32_t* dst) {
@@ -81,143 +53,28 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
     p[i] = 0u;
 }
 
-__global__ void init_state_kernel(PartSel* state, int p0, int np, uint32_t k) {
+__global__ void init_state_kernel(PartSel* state, uint32_t* arrive, int p0, int np, uint32_t k) {
   const int p = p0 + blockIdx.x * blockDim.x + threadIdx.x;
   if (p < p0 + np) {
     PartSel s = fresh_sel(k);
     s.fb = 1;
     state[p] = s;
+    arrive[p] = 0u;
   }
 }
 
-// Level 1 of the threshold search for partition blockIdx.x, on the level-1
-// histogram (key bits 30..19; see kScan* for the modes): find the digit
-// (scanning from the largest) whose bin holds the k-th largest key, and
-// record the capture bound of the next step (the digit at which the count
-// from the top reaches `target`).  Always leaves the partition's bins
-// zeroed.
+// Level 1 of the threshold search for partition blockIdx.x (level1_block),
+// then the partition's bins zeroed.
 __global__ void __launch_bounds__(kThreads)
-level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, int mode, uint32_t target) {
-  __shared__ uint32_t wtot[kThreads / 64];
-  __shared__ int found;
-  __shared__ uint32_t s_lo;
-  __shared__ int s_dmin;
+level_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, uint32_t* __restrict__ arrive,
+                  int mode, uint32_t target) {
   const int p = g.sp0 + blockIdx.x;
   uint32_t* h = hist + (int64_t)p * kBins;
-  constexpr int nb = kBins;
-  constexpr int shift = 32 + kL1Shift;
-  const PartSel cur = state[p];
-  const bool active = (mode == kScanCheck) || cur.fb != 0;  // the other modes: fallback partitions only
-  const PartSel st = fresh_sel((uint32_t)g.k);
-  constexpr int per = (nb + kThreads - 1) / kThreads;
-  if (active && mode == kScanSample) {
-    // The bound for a first capture: the digit at which the count of the
-    // sampled keys from the top reaches `target` (scaled to the sample), or
-    // 0 (capture every key) if the sample holds fewer.
-    uint32_t s = 0;
-    for (int q = 0; q < per; ++q) s += h[nb - 1 - (threadIdx.x * per + q)];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan(s, wtot, &tot);
-    if (threadIdx.x == 0 && tot < target) state[p].lo_fb = 0u;
-    if (tot >= target && above < target && target <= above + s) {
-      uint32_t acc = above;
-      for (int q = 0; q < per; ++q) {
-        const int d = nb - 1 - (threadIdx.x * per + q);
-        acc += h[d];
-        if (acc >= target) {
-          state[p].lo_fb = (uint32_t)d << kL1Shift;
-          break;
-        }
-      }
-    }
-  } else if (active) {
-    // thread t owns descending positions [t*per, (t+1)*per): bin = nb-1-pos
-    uint32_t s = 0;
-    for (int q = 0; q < per; ++q) s += h[nb - 1 - (threadIdx.x * per + q)];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan(s, wtot, &tot);
-    if (threadIdx.x == 0) {
-      found = 0;
-      s_lo = 0xffffffffu;
-      s_dmin = nb;
-    }
-    __syncthreads();
-    // Capture bound for the next step: the digit at which the count of keys
-    // from the top reaches the target.
-    const bool bound = (mode == kScanCheck || mode == kScanFinal);
-    const int64_t need = bound ? ((tot >= target) ? (int64_t)target : -2) : -1;
-    if (need >= 1 && above < (uint64_t)need && (uint64_t)need <= (uint64_t)above + s) {
-      uint32_t acc = above;
-      for (int q = 0; q < per; ++q) {
-        const int d = nb - 1 - (threadIdx.x * per + q);
-        acc += h[d];
-        if (acc >= (uint32_t)need) {
-          s_lo = (uint32_t)d << kL1Shift;
-          break;
-        }
-      }
-    }
-    if (need == -2) {
-      // fewer keys than the target were captured: one bin below the lowest
-      // captured digit
-      for (int q = per - 1; q >= 0; --q) {
-        const int pos = threadIdx.x * per + q;
-        if (h[nb - 1 - pos]) {
-          atomicMin(&s_dmin, nb - 1 - pos);
-          break;
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) s_lo = (uint32_t)(s_dmin >= 1 && s_dmin < nb ? s_dmin - 1 : 0) << kL1Shift;
-    }
-    __syncthreads();
-    if (mode == kScanCheck && tot < st.r) {
-      if (threadIdx.x == 0) {
-        PartSel o = st;
-        o.fb = 1;
-        state[p] = o;
-        found = 1;
-      }
-    } else if (above < st.r && st.r <= above + s) {
-      uint32_t acc = above;
-      for (int q = 0; q < per; ++q) {
-        const int d = nb - 1 - (threadIdx.x * per + q);
-        const uint32_t c = h[d];
-        if (acc + c >= st.r) {
-          if (mode == kScanBound) {
-            PartSel o = cur;
-            o.lo_fb = (uint32_t)d << kL1Shift;
-            state[p] = o;
-          } else {
-            PartSel o = st;
-            o.r = st.r - acc;
-            o.prefix = (uint64_t)d << shift;
-            o.mask = ((uint64_t)(nb - 1) << shift) | (1ull << 63);  // bit 63 of every composite is zero
-            o.done = (c == o.r) ? 1u : 0u;
-            o.bin1 = (uint32_t)d;
-            o.c1 = c;
-            o.fb = 0;
-            state[p] = o;
-          }
-          found = 1;
-          break;
-        }
-        acc += c;
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && !found) {
-      PartSel o = cur;
-      o.fault |= 1u;
-      o.done = 1;
-      o.fb = 0;
-      state[p] = o;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && bound) state[p].lo_next = (s_lo == 0xffffffffu) ? 0u : s_lo;
-  }
+  // the fallback's statistic passes count their blocks' arrivals from zero
+  if (mode == kScanCheck && threadIdx.x == 0) arrive[p] = 0u;
+  level1_block(g, p, h, state, mode, target);
   __syncthreads();
-  for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0u;
+  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
 }
 
 __device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
@@ -1012,14 +869,13 @@ check_idx_kernel(Geom g, const uint64_t* __restrict__ bits, const uint32_t* __re
   }
 }
 
-// kCaptureMargin * k, at most n_p.
+}  // namespace
+
 uint32_t capture_target(const Geom& g) {
   double t = kCaptureMargin * (double)g.k;
   if (t > (double)g.n_p) t = (double)g.n_p;
   return (uint32_t)(t + 0.5);
 }
-
-}  // namespace
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
@@ -1029,15 +885,17 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_init_state(const Geom& g, PartSel* state, hipStream_t s) {
+hipError_t launch_init_state(const Geom& g, const SelectBufs& w, hipStream_t s) {
   if (g.snp < 1) return hipSuccess;
-  init_state_kernel<<<(g.snp + kThreads - 1) / kThreads, kThreads, 0, s>>>(state, g.sp0, g.snp, (uint32_t)g.k);
+  init_state_kernel<<<(g.snp + kThreads - 1) / kThreads, kThreads, 0, s>>>(w.state, w.arrive, g.sp0, g.snp,
+                                                                            (uint32_t)g.k);
   return hipGetLastError();
 }
 
 hipError_t launch_level1(const Geom& g, const SelectBufs& w, int mode, hipStream_t s, uint32_t target) {
   if (g.snp < 1) return hipSuccess;
-  level_scan_kernel<<<g.snp, kThreads, 0, s>>>(g, w.hist, w.state, mode, target ? target : capture_target(g));
+  level_scan_kernel<<<g.snp, kThreads, 0, s>>>(g, w.hist, w.state, w.arrive, mode,
+                                               target ? target : capture_target(g));
   return hipGetLastError();
 }
 

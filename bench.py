@@ -33,6 +33,10 @@ CPU_WAIT_S = 600.0  # bound on every wait of the CPU baseline
 # timed and warmup steps)
 EXTRA_STEPS = 10
 EXTRA_WARMUP = 3
+# Workloads this small run in tens of microseconds a step: they are timed
+# over SMALL_STEPS steps, so that the timed region is milliseconds long.
+SMALL_N = 1 << 22
+SMALL_STEPS = 200
 CPU_SHARE = 16  # host cores per GPU on the benchmark host
 METRIC = "optimizer-step params/s + HBM GB/s (% peak), Llama-1.8B shape, 99% sparsity"
 
@@ -619,7 +623,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra-configs", default="all", metavar="all|none|NAME[,NAME...]",
                     help="workloads measured after --config, at most "
-                         f"{EXTRA_STEPS} steps each, reported under 'configs' (default: all the others)")
+                         f"{EXTRA_STEPS} steps each ({SMALL_STEPS} for workloads of at most {SMALL_N} "
+                         "parameters), reported under 'configs' (default: all the others)")
     ap.add_argument("--overlap", action="store_true",
                     help="report |M_t ∩ M_{t+1}| / (P k) per step (untimed; on by default for the stress workload)")
     ap.add_argument("--offload", default="", metavar="CHUNK_PARTS[,CHUNK_PARTS...]",
@@ -665,8 +670,9 @@ def main():
     head = measure_workload(S, W, torch, cfg, args, args.steps, args.warmup, True, log)
     extras = {}
     for name in extra_workloads(args.extra_configs, cfg.name, W.CONFIGS):
-        extras[name] = measure_workload(S, W, torch, W.CONFIGS[name], args, min(args.steps, EXTRA_STEPS),
-                                        min(args.warmup, EXTRA_WARMUP), False, log)
+        cfg_x = W.CONFIGS[name]
+        steps_x = min(args.steps, EXTRA_STEPS) if cfg_x.n > SMALL_N else max(args.steps, SMALL_STEPS)
+        extras[name] = measure_workload(S, W, torch, cfg_x, args, steps_x, min(args.warmup, EXTRA_WARMUP), False, log)
 
     # the oracle on the host's cores, after every GPU measurement: run
     # before them (forked, ahead of the GPU's initialisation), it left the

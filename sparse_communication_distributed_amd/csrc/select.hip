@@ -33,6 +33,8 @@ constexpr int kCandChunks = 4;
 // tile's index writes dominate and more waves pay).
 constexpr int kEmitTiles = 4;
 __host__ __device__ constexpr int emit_tiles(bool ranks) { return ranks ? 1 : kEmitTiles; }
+// Entries of a wave's LDS index list in the emission of denser masks.
+constexpr int kEmitList = 1024;
 
 
 
@@ -655,27 +657,6 @@ finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
 }
 
 // Position of the r-th set bit (from 0) of a word with more than r set bits.
-__device__ __forceinline__ uint32_t select_bit(uint64_t word, uint32_t r) {
-  uint32_t pos = 0;
-  uint32_t half = (uint32_t)word;
-  const uint32_t c32 = (uint32_t)__popc(half);
-  if (r >= c32) {
-    r -= c32;
-    pos = 32;
-    half = (uint32_t)(word >> 32);
-  }
-#pragma unroll
-  for (int sh = 16; sh >= 1; sh >>= 1) {
-    const uint32_t c = (uint32_t)__popc(half & ((1u << sh) - 1u));
-    if (r >= c) {
-      r -= c;
-      pos += sh;
-      half >>= sh;
-    }
-  }
-  return pos;
-}
-
 // Each wave takes emit_tiles(RANKS) consecutive tiles (with the loads they
 // need issued together), and for each completes the tile's mask words and writes
 // its global indices in order.  The threshold bin's candidates of the tile
@@ -685,17 +666,16 @@ __device__ __forceinline__ uint32_t select_bit(uint64_t word, uint32_t r) {
 // writer of its tile's words).  Then, with the tile's offset:
 // RANKS false (sparse masks): each lane walks the set bits of its own word.
 // RANKS true (denser masks, where a lane's word holds several indices): the
-// lanes take ranks r, r + 64, ... within the tile, so consecutive lanes
-// write consecutive entries of the index list; rank r lies in the last word
-// whose exclusive popcount prefix is at most r (a binary search over the
-// tile's 64 prefixes in LDS), at that word's (r - prefix)-th set bit.
+// lanes write their indices into an LDS list at their ranks, and the wave
+// copies it out with consecutive lanes on consecutive entries of the index
+// list.
 template <bool RANKS>
 __global__ void __launch_bounds__(kThreads)
 emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restrict__ cand,
             const uint32_t* __restrict__ cnt2, uint64_t* __restrict__ bits,
             const uint32_t* __restrict__ tile_off, uint32_t* __restrict__ idx) {
   __shared__ unsigned long long swords[kThreads / 64][kWordsPerTile];
-  __shared__ uint32_t spre[RANKS ? kThreads / 64 : 1][kWordsPerTile];
+  __shared__ uint32_t slist[RANKS ? kThreads / 64 : 1][RANKS ? kEmitList : 1];
   constexpr int ET = emit_tiles(RANKS);
   const int p = g.sp0 + blockIdx.y;
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
@@ -773,21 +753,29 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
       }
       continue;
     }
-    const uint32_t sw = RANKS ? wave : 0u;  // this wave's rows of the LDS arrays
-    wd[lane] = word;
-    spre[sw][lane] = x - c;
+    // Denser masks: the lanes write their words' indices into the wave's
+    // LDS list at their ranks, kEmitList ranks a round, and the wave copies
+    // each round's list out with consecutive lanes on consecutive entries.
+    uint32_t* sl = slist[RANKS ? wave : 0u];
     const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
-    wave_lds_sync();
-    const uint32_t tbase = (uint32_t)((int64_t)p * g.n_p + t * kTile);
-    for (uint32_t r = lane; r < total; r += 64) {
-      uint32_t q = 0;
-#pragma unroll
-      for (uint32_t step = 32; step >= 1; step >>= 1)
-        if (spre[sw][q + step] <= r) q += step;
-      const uint32_t jj = select_bit(wd[q], r - spre[sw][q]);
-      if (base + r < g.k) out[base + r] = tbase + q * 64 + jj;  // bound: malformed mask
+    const uint32_t first = x - c;  // rank of this lane's first index
+    const uint32_t jbase = (uint32_t)((int64_t)p * g.n_p + w * 64);
+    for (uint32_t r0 = 0; r0 < total; r0 += kEmitList) {  // wave-uniform
+      uint64_t wv = word;
+      uint32_t r = first;
+      if (first + c > r0 && first < r0 + kEmitList) {
+        for (; wv && r < r0; ++r) wv &= wv - 1ull;  // ranks of earlier rounds
+        for (; wv && r < r0 + kEmitList; ++r) {
+          sl[r - r0] = jbase + (uint32_t)__builtin_ctzll(wv);
+          wv &= wv - 1ull;
+        }
+      }
+      wave_lds_sync();
+      const uint32_t cnt = (total - r0 < (uint32_t)kEmitList) ? total - r0 : (uint32_t)kEmitList;
+      for (uint32_t i = lane; i < cnt; i += 64)
+        if (base + r0 + i < g.k) out[base + r0 + i] = sl[i];  // bound: malformed mask
+      wave_lds_sync();  // the next round or tile rewrites the list
     }
-    wave_lds_sync();  // the next tile rewrites this wave's LDS rows
   }
 }
 

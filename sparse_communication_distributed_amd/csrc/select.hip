@@ -378,7 +378,8 @@ constexpr int kScanBatch = 16;
 // and the next step's capture bound is refined to the level-2 digit at
 // which the count from the top reaches the part of the target inside the
 // bin.  Leaves the partition's histogram bins zeroed and its survivor
-// count at zero.
+// count at zero (or, when the candidates left at the level-2 digit cannot
+// fit the survivor list, at their number).
 __global__ void __launch_bounds__(kThreads)
 l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, uint32_t* __restrict__ nsurv,
                uint32_t target) {
@@ -431,6 +432,9 @@ l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
         o.mask = cur.mask | dmask;
         o.bin2 = s_d;
         o.done2 = (s_c == o.r) ? 1u : 0u;
+        // more candidates at the level-2 digit than the survivor list
+        // holds (ties): the walk keeps no list, and the count says so
+        if (!o.done2 && s_c > (uint32_t)kSurvivorCap) nsurv[p] = s_c;
       }
       state[p] = o;
     }
@@ -466,6 +470,9 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
   uint32_t kmin = 0xffffffffu;
   uint64_t* sl = surv + (int64_t)p * kSurvivorCap;
   uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
+  // false when level 2 found more candidates at its digit than the list
+  // holds: then no wave appends (the walks of the later levels take over)
+  const bool listed = nsurv[p] <= (uint32_t)kSurvivorCap;
   for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
     const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
     uint32_t add = 0;
@@ -490,7 +497,9 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
         }
         const bool keep = at && !done2;
         const uint64_t kb = __ballot(keep);
-        if (kb) {  // wave-uniform
+        if (kb && !listed) {  // wave-uniform
+          if (keep) atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
+        } else if (kb) {  // wave-uniform
           // Once the count has passed the cap the list is abandoned and only
           // "more than the cap" matters, which the count already shows: no
           // further (contended) atomic.  A wave that reads a count at or

@@ -37,6 +37,8 @@ EXTRA_WARMUP = 3
 # over SMALL_STEPS steps, so that the timed region is milliseconds long.
 SMALL_N = 1 << 22
 SMALL_STEPS = 200
+# Device memory left free when the placement of e is chosen.
+PLACE_MARGIN = 8 << 30
 CPU_SHARE = 16  # host cores per GPU on the benchmark host
 METRIC = "optimizer-step params/s + HBM GB/s (% peak), Llama-1.8B shape, 99% sparsity"
 
@@ -462,6 +464,31 @@ def measure_workload(S, W, torch, cfg, args, steps, warmup, full, log_fn):
         t += 1
         S.step(d, params, pool[(t - 1) % len(pool)], m, v_out, e, mask, k, bt, cfg.lr, t, ws, stream)
 
+    # Placement of e (the error-feedback rows), chosen at setup: up to
+    # --place - 1 more allocations of e, as free memory allows, each taking
+    # e's role for two ordinary steps per round (S.choose_placement); the
+    # fastest keeps it.  Untimed, before the warmup.
+    if args.place > 1 and n > SMALL_N:
+        free, _ = torch.cuda.mem_get_info()
+        ncand = int(min(args.place - 1, (free - PLACE_MARGIN) // (e.numel() * 4)))
+        if ncand >= 1:
+            cands = [torch.empty_like(e) for _ in range(ncand)]
+
+            def run(x):
+                nonlocal e
+                e = x
+                one_step()
+                one_step()
+
+            e, place_ms = S.choose_placement(e, cands, run, rounds=2)
+            del cands
+            torch.cuda.empty_cache()
+            best = place_ms.index(min(place_ms))
+            rec["e_placement"] = {"allocations": ncand + 1, "ms_per_2_steps": place_ms, "chosen": best,
+                                  "steps": 4 * (ncand + 1)}
+            log_fn(f"{cfg.name}: e placement: {ncand + 1} allocations, two steps each "
+                   f"{', '.join(f'{x:.2f}' for x in place_ms)} ms, kept #{best}")
+
     for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
@@ -638,6 +665,9 @@ def main():
                     help="allocate the gradient sets before the optimizer state")
     ap.add_argument("--store-v", action="store_true",
                     help="the timed steps also store v_t at the masked entries (AdamS never reads it back)")
+    ap.add_argument("--place", type=int, default=4, metavar="N",
+                    help="choose the placement of e among N allocations at setup, by timing ordinary steps "
+                         "(S.choose_placement; 1: keep the first)")
     ap.add_argument("--calib", action="store_true",
                     help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
     ap.add_argument("--shard", type=int, default=0, metavar="RANKS",
@@ -720,8 +750,8 @@ def main():
                      "traffic_gbps": sp["traffic_gbps"]},
         "cpu_baseline": None,
     }
-    for key in ("bootstrap_step", "dense_adams", "step_storing_v", "stream_reference", "stream_calibration",
-                "mask_overlap", "graph"):
+    for key in ("e_placement", "bootstrap_step", "dense_adams", "step_storing_v", "stream_reference",
+                "stream_calibration", "mask_overlap", "graph"):
         if key in head:
             out[key] = head[key]
     if extras:

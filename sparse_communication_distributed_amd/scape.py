@@ -445,6 +445,41 @@ def profile_collect():
 # ---------------------------------------------------------------- optimizer
 
 
+def choose_placement(current, candidates, run_steps, rounds: int = 2):
+    """Physical placement of a large state tensor, chosen by measurement.
+
+    The step pass streams every worker row of e in lockstep, and its rate
+    depends on the physical memory behind e: some placements load the
+    memory channels unevenly.  `current` is the tensor in use and
+    `candidates` are separate allocations of its shape and dtype.
+    run_steps(t) runs real optimizer steps with tensor t in current's role
+    (on torch's current stream).  Each tensor takes the role in turn,
+    `rounds` times, after receiving the role's contents by an exact copy, so
+    the steps' results do not depend on the choice.  Returns the tensor that
+    ran fastest (holding the contents) and each one's best time in ms; the
+    caller drops the others."""
+    import torch
+    opts = [current] + list(candidates)
+    times = [float("inf")] * len(opts)
+    holder = 0
+    for _ in range(rounds):
+        for i, x in enumerate(opts):
+            if i != holder:
+                x.copy_(opts[holder])
+                holder = i
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run_steps(x)
+            e1.record()
+            e1.synchronize()
+            times[i] = min(times[i], e0.elapsed_time(e1))
+    best = min(range(len(opts)), key=times.__getitem__)
+    if best != holder:
+        opts[best].copy_(opts[holder])
+    torch.cuda.synchronize()
+    return opts[best], times
+
+
 class ScapeOptimizer:
     """Device state of one SCAPE optimizer over a flat fp32 buffer.
 
@@ -486,6 +521,26 @@ class ScapeOptimizer:
         step(self.d, self.params, grads, self.m, self.v, self.e, self.mask, self.k, self.bt, self.lr,
              t, self.ws, stream)
         self.t = t  # a rejected call leaves the step count unchanged
+
+    def place_error_feedback(self, grads, candidates: int = 3, rounds: int = 2) -> dict:
+        """Runs rounds * (candidates + 1) steps with `grads`, with e in its
+        current allocation and in `candidates` new ones in turn
+        (choose_placement), and keeps e in the fastest; the others are
+        freed.  The steps are ordinary steps (same results as calling
+        step() that many times).  Returns {"step_ms": [...], "chosen": i}."""
+        import torch
+        cands = [torch.empty_like(self.e) for _ in range(candidates)]
+
+        def run(x):
+            self.e = x
+            self.step(grads)
+
+        chosen, times = choose_placement(self.e, cands, run, rounds)
+        best = times.index(min(times))
+        self.e = chosen
+        del cands, chosen
+        torch.cuda.empty_cache()
+        return {"step_ms": times, "chosen": best}
 
     def nonfinite_count(self) -> int:
         """Non-finite gradient values the steps were given (NaN, +-inf),

@@ -927,3 +927,28 @@ def test_optimizer_counts_nonfinite_gradients(S):
     g[0, cfg.n - 1] = np.inf
     opt.step(dev(g))
     assert opt.nonfinite_count() == 2
+
+
+def test_error_feedback_placement_keeps_results(S):
+    """Choosing e's placement runs ordinary steps with e moved between
+    allocations by exact copies: the state afterwards, and after further
+    steps, is bitwise that of an optimizer that made the same steps without
+    moving e."""
+    cfg = W.flat_config("place", 4 * 8192, 4, 2, "0.99", steps=1)
+    w0 = dev(W.init_params(cfg))
+    a = S.ScapeOptimizer(w0.clone(), cfg.P, cfg.K, cfg.k)
+    b = S.ScapeOptimizer(w0.clone(), cfg.P, cfg.K, cfg.k)
+    g1 = dev(W.grads(cfg, 1))
+    info = a.place_error_feedback(g1, candidates=2, rounds=2)
+    for _ in range(2 * 3):
+        b.step(g1)
+    assert a.t == b.t == 6
+    assert len(info["step_ms"]) == 3 and 0 <= info["chosen"] < 3
+    for t in (2, 3):
+        g = dev(W.grads(cfg, t))
+        a.step(g)
+        b.step(g)
+    torch.cuda.synchronize()
+    for name in ("params", "m", "v", "e"):
+        assert torch.equal(getattr(a, name).view(torch.int32), getattr(b, name).view(torch.int32)), name
+    assert torch.equal(a.mask, b.mask)

@@ -123,12 +123,19 @@ def _open(path):
 
 
 def calibration_values(vals):
-    """The counter values of the 1 GiB calibration copies among all copy
-    dispatches of a run: those within a factor of two of the largest (the
-    workload's own small copies, such as uploads of host-drawn indices or a
-    mask check's read-back, use the same copy kernel)."""
-    top = max(vals)
-    return [v for v in vals if v >= 0.5 * top]
+    """The counter values (KiB) of the 1 GiB calibration copies among all
+    copy dispatches of a run.  The workload's own copies use the same copy
+    kernel: small ones (uploads of host-drawn indices, a mask check's
+    read-back) and whole-buffer ones (the error-feedback rows moved between
+    allocations while their placement is chosen).  A calibration copy reads
+    between an eighth and four times its 1 GiB on either counter; of the
+    copies in that window, those within a factor of two of the largest are
+    kept."""
+    win = [v for v in vals if GIB_KIB / 8 <= v <= 4 * GIB_KIB]
+    if not win:
+        raise SystemExit("no 1 GiB calibration copy among the copy dispatches (run with --calib)")
+    top = max(win)
+    return [v for v in win if v >= 0.5 * top]
 
 
 def read_counter(path, counter):

@@ -142,9 +142,13 @@ def test_extra_workloads_selection():
 
 def test_counter_calibration_ignores_small_copies():
     """The calibration uses the 1 GiB copies only, not the workload's own
-    small copies through the same copy kernel."""
+    copies through the same copy kernel: small uploads and read-backs, and
+    whole error-feedback buffers moved while their placement is chosen."""
     from sparse_communication_distributed_amd.prof_summary import calibration_values
-    gib = [2097152.0, 2097150.0, 2097160.0]
+    gib = [524288.0, 524280.0, 524300.0]   # FETCH_SIZE reads half of a 1 GiB copy
     small = [3.0, 12.5, 0.0, 400.0]
-    assert sorted(calibration_values(gib + small)) == sorted(gib)
-    assert calibration_values([5.0]) == [5.0]
+    placement = [14.2e6, 14.2e6, 28.4e6]   # 28 GB buffers moved between allocations
+    assert sorted(calibration_values(gib + small + placement)) == sorted(gib)
+    assert sorted(calibration_values([1048576.0, 1048570.0] + placement)) == [1048570.0, 1048576.0]
+    with pytest.raises(SystemExit, match="calibration"):
+        calibration_values(small + placement)

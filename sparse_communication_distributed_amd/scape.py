@@ -523,12 +523,18 @@ class ScapeOptimizer:
         self.t = t  # a rejected call leaves the step count unchanged
 
     def place_error_feedback(self, grads, candidates: int = 3, rounds: int = 2) -> dict:
-        """Runs rounds * (candidates + 1) steps with `grads`, with e in its
-        current allocation and in `candidates` new ones in turn
-        (choose_placement), and keeps e in the fastest; the others are
-        freed.  The steps are ordinary steps (same results as calling
-        step() that many times).  Returns {"step_ms": [...], "chosen": i}."""
+        """Chooses the allocation that holds e (choose_placement): timed
+        steps with `grads` run with e in its current allocation and in
+        `candidates` new ones in turn, `rounds` times, and e stays in the
+        fastest.  The optimizer's state (params, m, v, e, the masks and the
+        step count) is saved first and restored afterwards, so training
+        continues as if the call had not been made.  Needs device memory for
+        the candidates and the saved state while it runs.  Returns
+        {"step_ms": [...], "chosen": i}."""
         import torch
+        saved = {name: getattr(self, name).clone() for name in ("params", "m", "v", "e", "mask")
+                 if getattr(self, name) is not None}
+        t0 = self.t
         cands = [torch.empty_like(self.e) for _ in range(candidates)]
 
         def run(x):
@@ -536,11 +542,14 @@ class ScapeOptimizer:
             self.step(grads)
 
         chosen, times = choose_placement(self.e, cands, run, rounds)
-        best = times.index(min(times))
         self.e = chosen
-        del cands, chosen
+        for name, x in saved.items():
+            getattr(self, name).copy_(x)
+        self.t = t0
+        torch.cuda.synchronize()
+        del cands, chosen, saved
         torch.cuda.empty_cache()
-        return {"step_ms": times, "chosen": best}
+        return {"step_ms": times, "chosen": times.index(min(times))}
 
     def nonfinite_count(self) -> int:
         """Non-finite gradient values the steps were given (NaN, +-inf),

@@ -930,21 +930,23 @@ def test_optimizer_counts_nonfinite_gradients(S):
 
 
 def test_error_feedback_placement_keeps_results(S):
-    """Choosing e's placement runs ordinary steps with e moved between
-    allocations by exact copies: the state afterwards, and after further
-    steps, is bitwise that of an optimizer that made the same steps without
-    moving e."""
+    """Choosing e's placement leaves the optimizer as it was: after it, and
+    after further steps, every buffer is bitwise that of an optimizer that
+    never made the choice."""
     cfg = W.flat_config("place", 4 * 8192, 4, 2, "0.99", steps=1)
     w0 = dev(W.init_params(cfg))
     a = S.ScapeOptimizer(w0.clone(), cfg.P, cfg.K, cfg.k)
     b = S.ScapeOptimizer(w0.clone(), cfg.P, cfg.K, cfg.k)
-    g1 = dev(W.grads(cfg, 1))
-    info = a.place_error_feedback(g1, candidates=2, rounds=2)
-    for _ in range(2 * 3):
-        b.step(g1)
-    assert a.t == b.t == 6
+    for t in (1, 2):  # a state with residuals and a mask
+        g = dev(W.grads(cfg, t))
+        a.step(g)
+        b.step(g)
+    e_ptr = a.e.data_ptr()
+    info = a.place_error_feedback(dev(W.grads(cfg, 9)), candidates=2, rounds=2)
     assert len(info["step_ms"]) == 3 and 0 <= info["chosen"] < 3
-    for t in (2, 3):
+    assert (a.e.data_ptr() == e_ptr) == (info["chosen"] == 0)
+    assert a.t == b.t == 2
+    for t in (3, 4):
         g = dev(W.grads(cfg, t))
         a.step(g)
         b.step(g)

@@ -522,7 +522,7 @@ class ScapeOptimizer:
              t, self.ws, stream)
         self.t = t  # a rejected call leaves the step count unchanged
 
-    def place_error_feedback(self, grads, candidates: int = 3, rounds: int = 2) -> dict:
+    def place_error_feedback(self, grads, candidates: int = 4, rounds: int = 2) -> dict:
         """Chooses the allocation that holds e (choose_placement): timed
         steps with `grads` run with e in its current allocation and in
         `candidates` new ones in turn, `rounds` times, and e stays in the

@@ -185,12 +185,23 @@ constexpr int kWorkerChunkGroup = 2;
 constexpr int kModeAll = 0;
 constexpr int kModeWorker = 1;
 constexpr int kModeOwner = 2;
+//  kModeAllPre  the single-pass fused step for exactly kPreWorkers workers
+//               on layouts of few tiles (one block per CU or so), where
+//               each block's chain of dependent loads is the step's time:
+//               the whole tile is one chunk group, and both workers' g and e
+//               are loaded before any is used.
+constexpr int kModeAllPre = 3;
+constexpr int kPreWorkers = 2;
+constexpr int kPreMinWaves = 2;
+// Tiles (over all partitions) up to which the step takes kModeAllPre.
+constexpr int64_t kPreMaxTiles = 2048;
 
 // VOUT: v_t is stored at the masked elements (v non-null).  AdamS never
 // reads v back, so a caller may leave it out.
 template <bool STEP, bool VEC, bool SEG, bool VOUT, int MODE>
 __global__ void __launch_bounds__(kThreads, MODE == kModeOwner    ? kOwnerMinWaves
                                            : MODE == kModeWorker ? kWorkerMinWaves
+                                           : MODE == kModeAllPre ? kPreMinWaves
                                                                  : kStepMinWaves)
 compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
@@ -199,9 +210,14 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
                 uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int p0, int64_t e_stride,
                 const float* __restrict__ ibc_dev, int rot) {
-  static_assert(MODE == kModeAll || (MODE == kModeWorker && !STEP) || (MODE == kModeOwner && STEP),
+  static_assert(MODE == kModeAll || (MODE == kModeWorker && !STEP) || (MODE == kModeOwner && STEP) ||
+                    (MODE == kModeAllPre && STEP),
                 "worker passes compress only; the owner pass is a step pass");
-  constexpr int CG = (MODE == kModeOwner) ? kOwnerChunkGroup : (MODE == kModeWorker) ? kWorkerChunkGroup : kChunkGroup;
+  constexpr int CG = (MODE == kModeOwner)    ? kOwnerChunkGroup
+                     : (MODE == kModeWorker) ? kWorkerChunkGroup
+                     : (MODE == kModeAllPre) ? 4
+                                             : kChunkGroup;
+  constexpr bool ALLW = MODE == kModeAll || MODE == kModeAllPre;  // every worker in this pass
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[STEP ? kBins : 1];
@@ -221,7 +237,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
   const int owner = (int)(((int64_t)p * g.K) / g.P);
   // the one worker of a worker or owner pass
   const int wsel = (MODE == kModeWorker) ? (owner + 1 + rot) % g.K : owner;
-  const int nwork = (MODE == kModeAll) ? g.K : 1;
+  const int nwork = (MODE == kModeAll) ? g.K : (MODE == kModeAllPre) ? kPreWorkers : 1;
   const uint32_t lo = STEP ? lo_in[p] : 0u;
   const int lane16 = threadIdx.x & 15;
   const int sh4 = 4 * lane16;
@@ -282,53 +298,112 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
           }
         }
       }
-      for (int ii = 0; ii < nwork; ++ii) {
-        const int i = (MODE == kModeAll) ? ii : wsel;
-        const float* gt = grads + (int64_t)i * g.n + pbase + tb;
-        float* et = e + (int64_t)i * e_stride + ebase + tb;
-        float* bt = b + (int64_t)i * pk + rbase;
-        float ga[CG][4], ea[CG][4];
+      if constexpr (MODE == kModeAllPre) {
+        // one worker's compression, its part of the worker sum and the
+        // owner's capture, from its loaded g and e (the same steps as the
+        // loop over workers below)
+        auto work = [&](int i, const float* gt, float* et, float (&ga)[CG][4], float (&ea)[CG][4]) {
+          (void)gt;
+          float* bt = b + (int64_t)i * pk + rbase;
+          const bool own = STEP && (i == owner);  // block-uniform
 #pragma unroll
-        for (int u = 0; u < CG; ++u) {
-          if (o[u] < tn) {
-            load4(gt, o[u], tn, VEC, ga[u]);
-            load4(et, o[u], tn, VEC, ea[u]);
+          for (int u = 0; u < CG; ++u) {
+            float a[4];
+            if (o[u] < tn) {
+              float eo[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                a[q] = ga[u][q] + ea[u][q];
+                eo[q] = ((nib[u] >> q) & 1u) ? 0.0f : a[q];
+              }
+              store4(et, o[u], tn, VEC, eo);
+              if (nib[u]) {
+                uint32_t rr = rr0[u];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if ((nib[u] >> q) & 1u) {
+                    if ((!STEP || own) && (int64_t)rr < rlim) bt[rr] = a[q];
+                    ++rr;
+                    // the worker sum so far (the owner pass: the owner's value)
+                    if (STEP) S[u][q] = (MODE == kModeOwner || i == 0) ? a[q] : S[u][q] + a[q];
+                  }
+              }
+            }
+            if (own) {  // all lanes of the wave take part in the capture
+              uint32_t kk[4];
+              bool f[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const bool valid = o[u] + q < tn;
+                kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
+                f[q] = valid && kk[q] >= lo;
+              }
+              capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+            }
           }
-        }
-        const bool own = STEP && (i == owner);  // block-uniform
+        };
+        // both workers' g and e loaded before either is used
+        float ga[kPreWorkers][CG][4], ea[kPreWorkers][CG][4];
 #pragma unroll
-        for (int u = 0; u < CG; ++u) {
-          float a[4];
-          if (o[u] < tn) {
-            float eo[4];
+        for (int i = 0; i < kPreWorkers; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              a[q] = ga[u][q] + ea[u][q];
-              eo[q] = ((nib[u] >> q) & 1u) ? 0.0f : a[q];
+          for (int u = 0; u < CG; ++u)
+            if (o[u] < tn) {
+              load4(grads + (int64_t)i * g.n + pbase + tb, o[u], tn, VEC, ga[i][u]);
+              load4(e + (int64_t)i * e_stride + ebase + tb, o[u], tn, VEC, ea[i][u]);
             }
-            store4(et, o[u], tn, VEC, eo);
-            if (nib[u]) {
-              uint32_t rr = rr0[u];
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if ((nib[u] >> q) & 1u) {
-                  if ((!STEP || own) && (int64_t)rr < rlim) bt[rr] = a[q];
-                  ++rr;
-                  // the worker sum so far (the owner pass: the owner's value)
-                  if (STEP) S[u][q] = (MODE == kModeOwner || i == 0) ? a[q] : S[u][q] + a[q];
-                }
+        for (int i = 0; i < kPreWorkers; ++i)
+          work(i, grads + (int64_t)i * g.n + pbase + tb, e + (int64_t)i * e_stride + ebase + tb, ga[i], ea[i]);
+      } else {
+        for (int ii = 0; ii < nwork; ++ii) {
+          const int i = (MODE == kModeAll) ? ii : wsel;
+          const float* gt = grads + (int64_t)i * g.n + pbase + tb;
+          float* et = e + (int64_t)i * e_stride + ebase + tb;
+          float* bt = b + (int64_t)i * pk + rbase;
+          float ga[CG][4], ea[CG][4];
+#pragma unroll
+          for (int u = 0; u < CG; ++u) {
+            if (o[u] < tn) {
+              load4(gt, o[u], tn, VEC, ga[u]);
+              load4(et, o[u], tn, VEC, ea[u]);
             }
           }
-          if (own) {  // all lanes of the wave take part in the capture
-            uint32_t kk[4];
-            bool f[4];
+          const bool own = STEP && (i == owner);  // block-uniform
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const bool valid = o[u] + q < tn;
-              kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
-              f[q] = valid && kk[q] >= lo;
+          for (int u = 0; u < CG; ++u) {
+            float a[4];
+            if (o[u] < tn) {
+              float eo[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                a[q] = ga[u][q] + ea[u][q];
+                eo[q] = ((nib[u] >> q) & 1u) ? 0.0f : a[q];
+              }
+              store4(et, o[u], tn, VEC, eo);
+              if (nib[u]) {
+                uint32_t rr = rr0[u];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if ((nib[u] >> q) & 1u) {
+                    if ((!STEP || own) && (int64_t)rr < rlim) bt[rr] = a[q];
+                    ++rr;
+                    // the worker sum so far (the owner pass: the owner's value)
+                    if (STEP) S[u][q] = (MODE == kModeOwner || i == 0) ? a[q] : S[u][q] + a[q];
+                  }
+              }
             }
-            capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+            if (own) {  // all lanes of the wave take part in the capture
+              uint32_t kk[4];
+              bool f[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const bool valid = o[u] + q < tn;
+                kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
+                f[q] = valid && kk[q] >= lo;
+              }
+              capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+            }
           }
         }
       }
@@ -736,7 +811,9 @@ void launch_step_mode(const Geom& g, const StepArgs& a, bool vec, bool seg, hipS
 }
 
 hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s) {
-  launch_step_mode<kModeAll>(g, a, vec, seg, s);
+  // two workers on few tiles: the latency form (kModeAllPre)
+  if (g.K == kPreWorkers && (int64_t)g.P * g.tpp <= kPreMaxTiles) launch_step_mode<kModeAllPre>(g, a, vec, seg, s);
+  else launch_step_mode<kModeAll>(g, a, vec, seg, s);
   return hipGetLastError();
 }
 

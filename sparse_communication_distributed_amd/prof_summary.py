@@ -81,9 +81,10 @@ def step_pass_role(name: str):
     """Role of a launch in the step pass, from its template arguments
     compress_kernel<STEP, VEC, SEG, VOUT, MODE>: "worker" for a non-owner
     worker pass (STEP false, MODE 1), "owner" for the owner pass (MODE 2) or
-    the single step pass (MODE 0) that stores no v (STEP true, VOUT false),
-    "owner_v" for those that store v; None for anything else (the component
-    compression has STEP false, MODE 0)."""
+    the single step pass (MODE 0, or its latency form for small layouts,
+    MODE 3) that stores no v (STEP true, VOUT false), "owner_v" for those
+    that store v; None for anything else (the component compression has
+    STEP false, MODE 0)."""
     n = short_name(name)
     if not n.startswith(STEP_KERNEL + "<"):
         return None
@@ -92,7 +93,7 @@ def step_pass_role(name: str):
         return None
     if args[0] == "false" and args[4] == "1":
         return "worker"
-    if args[0] == "true" and args[4] in ("0", "2"):  # the single pass, or the owner pass
+    if args[0] == "true" and args[4] in ("0", "2", "3"):  # the single pass, or the owner pass
         return "owner" if args[3] == "false" else "owner_v"
     return None
 

@@ -64,6 +64,8 @@ def test_prof_summary_short_names_and_roles():
         == "vectorized_elementwise_kernel<…>"
     assert short_name("void scape::(anonymous namespace)::zero_u32_kernel(unsigned int*, long)") == "zero_u32_kernel"
     assert [step_pass_role(x) for x in (OWNER, OWNER_V, WORKER, COMP)] == ["owner", "owner_v", "worker", None]
+    small = OWNER.replace("<true, true, true, false, 2>", "<true, true, true, false, 3>")
+    assert step_pass_role(small) == "owner"  # the latency form of the single pass
 
 
 def test_prof_summary_step_pass_of_k_launches(tmp_path):

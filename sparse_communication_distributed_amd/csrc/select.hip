@@ -228,29 +228,6 @@ __device__ __forceinline__ void for_each_cand(const uint64_t* __restrict__ slot,
   }
 }
 
-// The tiles of partition p with compacted candidates, one wave per tile
-// (each wave takes tiles wave_id, wave_id + nwaves, ...): the counts are
-// loaded 64 tiles at a time (lane i: the batch's i-th tile) and only tiles
-// with candidates are visited, in ascending order.
-template <typename F>
-__device__ __forceinline__ void for_each_tile(const Geom& g, int p, const uint32_t* __restrict__ cnt2,
-                                              F&& f) {
-  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
-  const int64_t t0 = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const uint32_t lane = lane_id();
-  for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
-    const int64_t tl = tb + (int64_t)lane * nw;
-    uint32_t ct = (tl < g.tpp) ? cnt2[(int64_t)p * g.tpp + tl] : 0u;
-    if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
-    uint64_t nz = __ballot(ct != 0u);
-    while (nz) {  // wave-uniform
-      const int j = __builtin_ctzll(nz);
-      nz &= nz - 1;
-      f(tb + (int64_t)j * nw, (uint32_t)__shfl((int)ct, j, 64));
-    }
-  }
-}
-
 // ---- the threshold search inside the level-1 threshold bin ----
 // One block of kResolveThreads per partition.
 constexpr int kResolveThreads = 1024;
@@ -445,19 +422,38 @@ l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
   for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
 }
 
-// One wave per tile over the threshold bin's compacted candidates, after
-// level 2: adds to the tile's count the candidates above the level-2
-// threshold digit (and those at it, when that digit decides the search);
-// when it does not, histograms the level-3 digit (key bits 6..0) of the
-// candidates at it and appends them to the partition's survivor list (at
-// most kSurvivorCap kept; the count goes on).  When the level-2 digit
-// decides, the smallest key at it is folded into the state's k-th key.
+// Survivors a bin_walk block stages in LDS before it reserves their range of
+// the partition's list with one atomic.
+constexpr int kWalkStage = 512;
+// Tiles each wave of bin_walk's flattened walk takes, at most (fewer where
+// the layout has fewer than kSelectWaves * kFlatTilesPerWave tiles).
+constexpr int kFlatTilesPerWave = 32;
+
+// One wave per tile, or per batch of tiles, over the threshold bin's
+// compacted candidates, after level 2: adds to each tile's count the
+// candidates above the level-2 threshold digit (and those at it, when that
+// digit decides the search); when it does not, histograms the level-3 digit
+// (key bits 6..0) of the candidates at it and, when level 2 counted no more
+// of them than the survivor list holds, appends them to the list.  When the
+// level-2 digit decides, the smallest key at it is folded into the state's
+// k-th key.  Each wave takes tiles wave_id, wave_id + nwaves, ... in
+// batches of 64 (lane i: the batch's i-th tile, its candidate count and its
+// tile count).  FLAT (waves with several tiles of few candidates each): the
+// wave walks the batch's candidates as one flattened sequence, as walk_bin
+// does, so that kWalkBatch loads per lane are in flight whatever the tiles'
+// sizes.  Otherwise it walks the tiles with candidates one by one, and the
+// first 64 candidates of a tile are loaded while the tile before it is
+// walked.
+template <bool FLAT>
 __global__ void __launch_bounds__(kThreads)
 bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict__ cand,
                 const uint32_t* __restrict__ cnt2, uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ hist,
                 uint64_t* __restrict__ surv, uint32_t* __restrict__ nsurv) {
   __shared__ uint32_t sh[1 << (kL1Shift - kDigitBits)];
-  __shared__ uint32_t smin;
+  __shared__ unsigned long long sstage[kWalkStage];
+  __shared__ uint32_t spre[FLAT ? kThreads / 64 : 1][64];
+  __shared__ uint32_t sadd[FLAT ? kThreads / 64 : 1][64];
+  __shared__ uint32_t smin, sn, sfill, sbase;
   constexpr int nb3 = 1 << (kL1Shift - kDigitBits);
   const int p = g.sp0 + blockIdx.y;
   const PartSel st = state[p];
@@ -465,70 +461,177 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
   const bool done2 = st.done2 != 0;
   const int sh2 = g.levels[0].shift, sh3 = g.levels[1].shift;
   const uint32_t d2 = st.bin2;
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < nb3; i += kThreads) sh[i] = 0u;
-  if (threadIdx.x == 0) smin = 0xffffffffu;
+  if (FLAT) sadd[wave][lane] = 0u;
+  if (threadIdx.x == 0) {
+    smin = 0xffffffffu;
+    sn = 0u;     // stage positions handed out
+    sfill = 0u;  // stage entries written: a prefix of the stage
+  }
   __syncthreads();
-  const uint32_t lane = lane_id();
   uint32_t kmin = 0xffffffffu;
   uint64_t* sl = surv + (int64_t)p * kSurvivorCap;
   uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
+  const uint32_t* c2p = cnt2 + (int64_t)p * g.tpp;
+  const uint64_t* cp = cand + (int64_t)p * g.tpp * kTile;
   // false when level 2 found more candidates at its digit than the list
   // holds: then no wave appends (the walks of the later levels take over)
   const bool listed = nsurv[p] <= (uint32_t)kSurvivorCap;
-  for_each_tile(g, p, cnt2, [&](int64_t t, uint32_t ct) {
-    const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-    uint32_t add = 0;
-    for (uint32_t base = 0; base < ct; base += 64 * kCandChunks) {
-      uint64_t cc[kCandChunks];
-#pragma unroll
-      for (int u = 0; u < kCandChunks; ++u) {
-        const uint32_t i = base + 64 * u + lane;
-        cc[u] = (i < ct) ? slot[i] : 0ull;
+
+  // One candidate per lane, called by the whole wave (valid: the lane holds
+  // one).  Returns whether it adds to its tile's count.
+  auto take = [&](uint64_t c, bool valid) -> bool {
+    const uint32_t dd = (uint32_t)(c >> sh2) & (uint32_t)(kBins - 1);
+    const bool at = valid && dd == d2;
+    if (at && done2) {
+      const uint32_t key = (uint32_t)(c >> 32);
+      kmin = key < kmin ? key : kmin;
+    }
+    const bool keep = at && !done2;
+    const uint64_t kb = __ballot(keep);
+    if (kb && !listed) {  // wave-uniform
+      if (keep) atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
+    } else if (kb) {  // wave-uniform
+      // Level 2 counted these candidates, no more than the list holds, so
+      // each has a place in it.  They go to the block's LDS stage; a chunk
+      // that no longer fits there reserves its own range of the list at once
+      // (positions are handed out in order, so the chunks that fit form a
+      // prefix of the stage).
+      const uint32_t nk = (uint32_t)__popcll(kb);
+      uint32_t pos = 0u;
+      if (lane == 0) pos = atomicAdd(&sn, nk);
+      pos = (uint32_t)__shfl((int)pos, 0, 64);
+      const bool staged = pos + nk <= (uint32_t)kWalkStage;  // wave-uniform
+      if (staged) {
+        if (lane == 0) atomicAdd(&sfill, nk);
+      } else {
+        if (lane == 0) pos = atomicAdd(nsurv + p, nk);
+        pos = (uint32_t)__shfl((int)pos, 0, 64);
       }
-#pragma unroll
-      for (int u = 0; u < kCandChunks; ++u) {
-        if (base + 64 * u >= ct) break;  // wave-uniform
-        const uint64_t c = cc[u];
-        const bool valid = base + 64 * u + lane < ct;
-        const uint32_t dd = (uint32_t)(c >> sh2) & (uint32_t)(kBins - 1);
-        const bool at = valid && dd == d2;
-        add += (valid && (dd > d2 || (done2 && at))) ? 1u : 0u;
-        if (at && done2) {
-          const uint32_t key = (uint32_t)(c >> 32);
-          kmin = key < kmin ? key : kmin;
-        }
-        const bool keep = at && !done2;
-        const uint64_t kb = __ballot(keep);
-        if (kb && !listed) {  // wave-uniform
-          if (keep) atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
-        } else if (kb) {  // wave-uniform
-          // Once the count has passed the cap the list is abandoned and only
-          // "more than the cap" matters, which the count already shows: no
-          // further (contended) atomic.  A wave that reads a count at or
-          // below the cap adds, so the count exceeds the cap exactly when the
-          // candidates do.
-          uint32_t pos = (uint32_t)kSurvivorCap;
-          if (lane == 0) {
-            const uint32_t seen = __hip_atomic_load(nsurv + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (seen <= (uint32_t)kSurvivorCap) pos = atomicAdd(nsurv + p, (uint32_t)__popcll(kb));
-          }
-          pos = (uint32_t)__shfl((int)pos, 0, 64) + mbcnt(kb);
-          if (keep) {
-            atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
-            if (pos < (uint32_t)kSurvivorCap) sl[pos] = c;
-          }
-        }
+      pos += mbcnt(kb);
+      if (keep) {
+        atomicAdd(&sh[(uint32_t)(c >> sh3) & (uint32_t)(nb3 - 1)], 1u);
+        if (staged)
+          sstage[pos] = c;
+        else if (pos < (uint32_t)kSurvivorCap)
+          sl[pos] = c;
       }
     }
+    return valid && (dd > d2 || (done2 && at));
+  };
+
+  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t t0 = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
+    const int64_t tl = tb + (int64_t)lane * nw;
+    uint32_t ct = (tl < g.tpp) ? c2p[tl] : 0u;
+    const uint32_t tv = (tl < g.tpp) ? tc[tl] : 0u;
+    if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
+    if constexpr (FLAT) {
+      uint32_t* pre = spre[wave];
+      uint32_t* ad = sadd[wave];
+      uint32_t x = ct;
 #pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) add += __shfl_xor(add, dd, 64);
-    if (lane == 0 && add) tc[t] += add;  // this wave alone walks tile t here
-  });
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if ((int)lane >= d) x += y;
+      }
+      const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
+      if (total == 0) continue;  // wave-uniform
+      pre[lane] = x - ct;
+      wave_lds_sync();
+      for (uint32_t i0 = 0; i0 < total; i0 += 64 * kWalkBatch) {
+        uint64_t cc[kWalkBatch];
+        uint32_t jj[kWalkBatch];
+#pragma unroll
+        for (int u = 0; u < kWalkBatch; ++u) {
+          const uint32_t i = i0 + 64 * u + lane;
+          uint32_t j = 0;
+#pragma unroll
+          for (uint32_t step = 32; step >= 1; step >>= 1)
+            if (pre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
+          jj[u] = j;
+          cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kTile + (i - pre[j])] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kWalkBatch; ++u) {
+          if (i0 + 64 * u >= total) break;  // wave-uniform
+          const bool valid = i0 + 64 * u + lane < total;
+          const bool up = take(cc[u], valid);
+          // the chunk's lanes hold consecutive entries, so each tile's
+          // entries are a run of lanes: the run's first lane adds its count
+          const uint32_t j = jj[u];
+          const uint32_t jp = (uint32_t)__shfl_up((int)j, 1, 64);
+          const uint64_t heads = __ballot(valid && (lane == 0 || j != jp));
+          const uint64_t ups = __ballot(up);
+          if ((heads >> lane) & 1ull) {
+            const uint64_t later = lane == 63 ? 0ull : heads & (~0ull << (lane + 1));
+            const uint64_t below_end = later ? (1ull << __builtin_ctzll(later)) - 1ull : ~0ull;
+            const uint32_t n = (uint32_t)__popcll(ups & below_end & (~0ull << lane));
+            if (n) atomicAdd(&ad[j], n);
+          }
+        }
+      }
+      wave_lds_sync();
+      const uint32_t a = ad[lane];
+      if (a) tc[tl] = tv + a;  // this wave alone walks tile tl here
+      ad[lane] = 0u;
+      wave_lds_sync();
+    } else {
+      uint64_t nz = __ballot(ct != 0u);
+      uint64_t cnext = 0ull;
+      if (nz) {  // wave-uniform
+        const int j = __builtin_ctzll(nz);
+        const uint32_t nn = (uint32_t)__shfl((int)ct, j, 64);
+        if (lane < nn) cnext = cp[(tb + (int64_t)j * nw) * kTile + lane];
+      }
+      while (nz) {  // wave-uniform
+        const int j = __builtin_ctzll(nz);
+        nz &= nz - 1;
+        const int64_t t = tb + (int64_t)j * nw;
+        const uint32_t n1 = (uint32_t)__shfl((int)ct, j, 64);
+        const uint32_t tvj = (uint32_t)__shfl((int)tv, j, 64);
+        const uint64_t c0 = cnext;
+        if (nz) {
+          const int jn = __builtin_ctzll(nz);
+          const uint32_t nn = (uint32_t)__shfl((int)ct, jn, 64);
+          cnext = (lane < nn) ? cp[(tb + (int64_t)jn * nw) * kTile + lane] : 0ull;
+        }
+        const uint64_t* slot = cp + t * kTile;
+        uint32_t add = 0;
+        for (uint32_t base = 0; base < n1; base += 64 * kCandChunks) {
+          uint64_t cc[kCandChunks];
+#pragma unroll
+          for (int u = 0; u < kCandChunks; ++u) {
+            const uint32_t i = base + 64 * u + lane;
+            cc[u] = (base == 0 && u == 0) ? c0 : ((i < n1) ? slot[i] : 0ull);
+          }
+#pragma unroll
+          for (int u = 0; u < kCandChunks; ++u) {
+            if (base + 64 * u >= n1) break;  // wave-uniform
+            add += take(cc[u], base + 64 * u + lane < n1) ? 1u : 0u;
+          }
+        }
+#pragma unroll
+        for (int dd = 32; dd >= 1; dd >>= 1) add += __shfl_xor(add, dd, 64);
+        if (lane == 0 && add) tc[t] = tvj + add;  // this wave alone walks tile t here
+      }
+    }
+  }
   __syncthreads();
   uint32_t* h = hist + (int64_t)p * kBins;
   for (int i = threadIdx.x; i < nb3; i += kThreads) {
     const uint32_t c = sh[i];
     if (c) atomicAdd(h + i, c);
+  }
+  const uint32_t fill = sfill;
+  if (fill) {  // block-uniform: the staged survivors take one range of the list
+    if (threadIdx.x == 0) sbase = atomicAdd(nsurv + p, fill);
+    __syncthreads();
+    const uint32_t b0 = sbase;
+    for (uint32_t i = threadIdx.x; i < fill; i += kThreads)
+      if (b0 + i < (uint32_t)kSurvivorCap) sl[b0 + i] = sstage[i];
   }
   if (done2) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
@@ -911,13 +1014,26 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
                                                               w.tilecnt);
   if (mark) mark(ctx, 1);
   l2_scan_kernel<<<g.snp, kThreads, 0, s>>>(g, w.hist, w.state, w.nsurv, capture_target(g));
-  bin_walk_kernel<<<dim3(sblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, w.tilecnt, w.hist, w.surv,
-                                                          w.nsurv);
+  // rank-parallel emission, and the per-tile bin walk, pay from a mask
+  // density of about 5% on (many candidates per tile)
+  const bool ranks = g.k * 20 >= g.n_p;
+  // the bin walk flattens a wave's tiles at sparser masks, where it takes
+  // up to kFlatTilesPerWave of them
+  int64_t wpw = tpw;
+  if (!ranks) {
+    wpw = ((int64_t)g.snp * g.tpp + kSelectWaves - 1) / kSelectWaves;
+    wpw = wpw < 1 ? 1 : (wpw > kFlatTilesPerWave ? kFlatTilesPerWave : wpw);
+  }
+  const unsigned wblocks = (unsigned)((g.tpp + 4 * wpw - 1) / (4 * wpw));
+  if (!ranks && wpw > 1)
+    bin_walk_kernel<true><<<dim3(wblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, w.tilecnt, w.hist,
+                                                                    w.surv, w.nsurv);
+  else
+    bin_walk_kernel<false><<<dim3(wblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt2, w.tilecnt, w.hist,
+                                                                     w.surv, w.nsurv);
   finish_kernel<<<g.snp, kResolveThreads, 0, s>>>(g, w.hist, w.state, w.cand, w.cnt2, w.surv, w.nsurv, w.tilecnt,
                                                 tile_off, meta_out);
   if (mark) mark(ctx, 2);
-  // rank-parallel emission pays from a mask density of about 5% on
-  const bool ranks = g.k * 20 >= g.n_p;
   const int et = 4 * emit_tiles(ranks);  // tiles per block
   const unsigned tblocks = (unsigned)((g.tpp + et - 1) / et);
   if (ranks)

@@ -127,6 +127,50 @@ def test_mask_topk_first_capture(S, kind, P, n_p, k):
     check_mask(*S.mask_slot_tensors(d, k, blob, 0), oracle_topk_local(stat, P, n_p, k), n_p)
 
 
+def _planted_ties(P, n_p, k, count, where, seed):
+    """Normal keys with `count` copies (random signs) of one magnitude v in
+    each partition: v is the (k - count // 2)-th largest magnitude, so the
+    k-th key lies inside the tied group and the level-2 digit that holds it
+    has about `count` candidates.  where = "block": the copies take every
+    5th position of the first four tiles; "spread": evenly over the
+    partition."""
+    x = _stat_case("normal", P, n_p, seed).reshape(P, n_p)
+    rng = np.random.default_rng(seed + 1)
+    for p in range(P):
+        v = np.sort(np.abs(x[p]))[n_p - (k - count // 2)]
+        pos = np.arange(count) * 5 if where == "block" else np.linspace(0, n_p - 1, count).astype(np.int64)
+        x[p, pos] = np.where(rng.random(count) < 0.5, -v, v).astype(F32)
+    return x.reshape(-1)
+
+
+@pytest.mark.parametrize("kind,P,n_p,k", [
+    ("normal", 2, 5000 * 4096 + 77, 20_000),  # two tiles per wave, ragged tail
+    ("block", 2, 5000 * 4096, 30_000),        # 3000 tied survivors in one block: more than its LDS stage
+    ("spread", 2, 5000 * 4096, 30_000),       # 3000 tied survivors over every block
+    ("spread_many", 2, 5000 * 4096, 30_000),  # 6000 tied: more than the survivor list holds
+    ("normal", 3, 3000 * 4096, 1),
+    ("normal", 2, 5000 * 4096 + 77, 2_048_000),  # 10%: tiles walked one by one, two per wave
+])
+def test_mask_topk_tile_batches(S, kind, P, n_p, k):
+    """Layouts of more than 8192 tiles: the bin walk takes several tiles per
+    wave, as one flattened sequence at sparse masks and one by one at dense
+    ones; the survivors at the level-2 digit go through the blocks' LDS
+    stages, past them, or (too many for the list) to the later levels'
+    walks.  The mask is exact in every case."""
+    seed = 501 + P + k
+    if kind == "normal":
+        stat = _stat_case("normal", P, n_p, seed)
+    else:
+        count = 6000 if kind == "spread_many" else 3000
+        stat = _planted_ties(P, n_p, k, count, "block" if kind == "block" else "spread", seed)
+    d = S.dims(P * n_p, P, 1)
+    blob = torch.zeros(S.mask_bytes(d, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+    S.mask_topk(d, k, dev(stat), S.mask_slot(d, k, blob, 1), ws)
+    torch.cuda.synchronize()
+    check_mask(*S.mask_slot_tensors(d, k, blob, 1), oracle_topk_local(stat, P, n_p, k), n_p)
+
+
 def test_mask_topk_repeated_calls_reuse_workspace(S):
     """A second call on a dirty workspace gives the same (correct) mask."""
     P, n_p, k = 4, 70_000, 999

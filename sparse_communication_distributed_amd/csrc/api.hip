@@ -55,6 +55,16 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   r.nlevels = nl;
   r.sp0 = 0;
   r.snp = P;
+  // the level-2 histogram in a pass of its own: masks under 5% density on
+  // layouts of more than kSelectWaves tiles, about kHistBlocks blocks in
+  // all, no more than one per 64 tiles of a partition
+  r.hparts = 0;
+  if (k * 20 < n_p && (int64_t)P * r.tpp > kSelectWaves) {
+    int64_t h = kHistBlocks / P;
+    const int64_t hmax = (r.tpp + 63) / 64;
+    if (h > hmax) h = hmax;
+    r.hparts = (int)(h < 1 ? 1 : h);
+  }
   // mask slot: bits, idx, tile_off, then the threshold record u32[3P]
   r.off_bits = 0;
   r.off_idx = align256((size_t)P * r.wpp * 8);
@@ -74,6 +84,7 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   r.ws_surv = o;    o = align256(o + (size_t)P * kSurvivorCap * 8);
   r.ws_nsurv = o;   o = align256(o + (size_t)P * 4);
   r.ws_arrive = o;  o = align256(o + (size_t)P * 4);
+  r.ws_part = o;    o = align256(o + (size_t)P * r.hparts * kBins * 4);
   r.ws_total = o;
   *g = r;
   return true;
@@ -190,6 +201,7 @@ Ws ws_view(const Geom& g, void* ws) {
   w.sel.surv = reinterpret_cast<uint64_t*>(c + g.ws_surv);
   w.sel.nsurv = reinterpret_cast<uint32_t*>(c + g.ws_nsurv);
   w.sel.arrive = reinterpret_cast<uint32_t*>(c + g.ws_arrive);
+  w.sel.part = reinterpret_cast<uint32_t*>(c + g.ws_part);
   return w;
 }
 

@@ -30,6 +30,12 @@ constexpr int kStatBlocks = 8192;
 constexpr int kSelectTilesPerWave = 8;
 constexpr int64_t kSelectWaves = 8192;
 constexpr int kThreads = 256;
+// At sparse masks on such layouts, the level-2 histogram of the threshold
+// bin has a pass of its own: about kHistBlocks blocks in all, each writing
+// its partial histogram with plain stores.  (Merged with atomics by every
+// block of the candidate select pass, it costs millions of device-scope
+// atomics per step at the largest layouts.)
+constexpr int kHistBlocks = 512;
 
 // Statistic sources and phases of stat_kernel.
 constexpr int kSrcStat = 0;    // key of a given array
@@ -97,12 +103,13 @@ struct Geom {
   uint32_t idx_mask;  // (1 << idx_bits) - 1
   int nlevels;        // levels after level 1 (level 2 first)
   int sp0, snp;       // partitions the selection kernels work on: [sp0, sp0 + snp)
+  int hparts;         // level-2 histogram parts per partition (0: merged by the select pass)
   Level levels[8];
   // mask slot: offsets inside one slot, slot size
   size_t off_bits, off_idx, off_toff, off_meta, slot_bytes;
   // workspace offsets and total
   size_t ws_b, ws_mold, ws_hist, ws_cand, ws_cnt1, ws_cnt2, ws_state, ws_tilecnt, ws_surv, ws_nsurv, ws_arrive,
-      ws_total;
+      ws_part, ws_total;
 };
 
 // Returns false if dims/k are outside the limits.
@@ -145,6 +152,7 @@ struct SelectBufs {
   uint64_t* surv;     // [P][kSurvivorCap] candidates at the level-2 threshold digit
   uint32_t* nsurv;    // [P] their counts
   uint32_t* arrive;   // [P] blocks arrived in a fallback pass
+  uint32_t* part;     // [P][hparts][kBins] level-2 histogram parts
 };
 
 // ---- launch wrappers (each returns hipGetLastError() of its launches) ----

@@ -92,19 +92,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave per tile: reads the tile's captured candidates in rounds of
-// kCandChunks chunks of 64; selects the digits above the level-1 threshold
+// Tiles whose first 64 captured candidates cand_select loads together.
+constexpr int kPreTiles = 4;
+
+// One wave per tile: reads the tile's captured candidates (the first 64
+// with those of the next kPreTiles - 1 tiles of the wave, the rest in rounds
+// of kCandChunks chunks of 64); selects the digits above the level-1 threshold
 // digit into the tile's 64 mask words (written whole, so every word of the
 // partition is written) and counts them; compacts the threshold digit's
 // candidates in place, in order (a write position never passes the
-// candidates already read), and histograms their level-2 digit.
+// candidates already read), and (HIST) histograms their level-2 digit,
+// merging the block's histogram into the partition's with atomics.
+template <bool HIST>
 __global__ void __launch_bounds__(kThreads)
 cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ cand,
                    const uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2,
                    uint32_t* __restrict__ hist, uint64_t* __restrict__ bits,
                    uint32_t* __restrict__ tilecnt) {
   __shared__ unsigned long long words[kThreads / 64][kWordsPerTile];
-  __shared__ uint32_t sh[kBins];
+  __shared__ uint32_t sh[HIST ? kBins : 1];
   __shared__ uint32_t smin;
   const int p = g.sp0 + blockIdx.y;
   const PartSel st = state[p];
@@ -114,55 +120,50 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   unsigned long long* wd = words[wave];
   uint32_t kmin = 0xffffffffu;  // smallest key selected whole from the threshold digit
-  for (int i = threadIdx.x; i < kBins; i += kThreads) sh[i] = 0;
+  if (HIST)
+    for (int i = threadIdx.x; i < kBins; i += kThreads) sh[i] = 0;
   if (threadIdx.x == 0) smin = 0xffffffffu;
   __syncthreads();
   // The wave takes tiles t0, t0 + nw, ... in batches of up to 64: lane i
-  // loads the capture count of the batch's i-th tile, and the first 64
-  // captures of the next tile are loaded while a tile is processed, so that
-  // a tile costs no dependent global load of its own.
+  // loads the capture count of the batch's i-th tile.  The first 64
+  // captures of kPreTiles tiles are loaded together before the first of
+  // them is processed, so a group of tiles costs one dependent global load
+  // rather than one per tile.
   const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
   const int64_t t0 = (int64_t)blockIdx.x * (kThreads / 64) + wave;
   const uint32_t* c1p = cnt1 + (int64_t)p * g.tpp;
+  uint64_t* cpart = cand + (int64_t)p * g.tpp * kTile;
   for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
     const int64_t tl = tb + (int64_t)lane * nw;
     uint32_t cv = (tl < g.tpp) ? c1p[tl] : 0u;
     if (cv > (uint32_t)kTile) cv = (uint32_t)kTile;  // a slot holds at most one tile
     const int64_t left = (g.tpp - tb + nw - 1) / nw;
     const int nb = left < 64 ? (int)left : 64;
-    uint64_t cnext = 0ull;
-    {
-      const uint32_t nn = (uint32_t)__shfl((int)cv, 0, 64);
-      const uint64_t* ns = cand + ((int64_t)p * g.tpp + tb) * kTile;
-      if (lane < nn) cnext = ns[lane];
-    }
-    for (int j = 0; j < nb; ++j) {
-      const int64_t t = tb + (int64_t)j * nw;
-      const uint32_t n1 = (uint32_t)__shfl((int)cv, j, 64);
-      const uint64_t c0 = cnext;
-      if (j + 1 < nb) {
-        const uint32_t nn = (uint32_t)__shfl((int)cv, j + 1, 64);
-        const uint64_t* ns = cand + ((int64_t)p * g.tpp + t + nw) * kTile;
-        cnext = (lane < nn) ? ns[lane] : 0ull;
+    for (int j0 = 0; j0 < nb; j0 += kPreTiles) {
+      uint64_t cpre[kPreTiles];
+#pragma unroll
+      for (int u = 0; u < kPreTiles; ++u) {
+        const int j = j0 + u;
+        const uint32_t nn = (uint32_t)__shfl((int)cv, j & 63, 64);
+        cpre[u] = (j < nb && lane < nn) ? cpart[(tb + (int64_t)j * nw) * kTile + lane] : 0ull;
       }
-      wd[lane] = 0ull;
-      wave_lds_sync();
-      uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
-      const uint32_t tile_lo = (uint32_t)(t * kTile);
-      uint32_t n2 = 0;
-      // rounds of kCandChunks chunks of 64, all loaded before any is used
-      for (uint32_t base = 0; base < n1; base += 64 * kCandChunks) {
-        uint64_t cc[kCandChunks];
+      // Wait for the group's loads here, once: the tiles' own code then
+      // has no load to wait for (unless a tile holds more than 64
+      // captures), so it never waits for the stores of the tiles before it.
 #pragma unroll
-        for (int u = 0; u < kCandChunks; ++u) {
-          const uint32_t i = base + 64 * u + lane;
-          cc[u] = (base == 0 && u == 0) ? c0 : ((i < n1) ? slot[i] : 0ull);
-        }
+      for (int u = 0; u < kPreTiles; ++u) asm volatile("" ::"v"(cpre[u]));
 #pragma unroll
-        for (int u = 0; u < kCandChunks; ++u) {
-          if (base + 64 * u >= n1) break;  // wave-uniform
-          const uint64_t c = cc[u];
-          const bool valid = base + 64 * u + lane < n1;
+      for (int u = 0; u < kPreTiles; ++u) {
+        const int j = j0 + u;
+        if (j >= nb) break;  // wave-uniform
+        const int64_t t = tb + (int64_t)j * nw;
+        const uint32_t n1 = (uint32_t)__shfl((int)cv, j, 64);
+        wd[lane] = 0ull;
+        wave_lds_sync();
+        uint64_t* slot = cpart + t * kTile;
+        const uint32_t tile_lo = (uint32_t)(t * kTile);
+        uint32_t n2 = 0;
+        auto take = [&](uint64_t c, bool valid) {
           const uint32_t d1 = (uint32_t)(c >> (32 + kL1Shift)) & (kBins - 1);
           const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
           const bool ok = valid && jl < (uint32_t)kTile;  // false only for a corrupted slot
@@ -180,30 +181,48 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
           const uint64_t kb = __ballot(keep);
           if (keep) {
             slot[n2 + mbcnt(kb)] = c;
-            atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
+            if (HIST) atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
           }
           n2 += (uint32_t)__popcll(kb);
-        }
-      }
-      wave_lds_sync();
-      const int64_t w = t * kWordsPerTile + lane;
-      const unsigned long long word = wd[lane];
-      if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = word;
-      uint32_t pc = (uint32_t)__popcll(word);
+        };
+        if (n1) take(cpre[u], lane < n1);  // wave-uniform
+        // the rest in rounds of kCandChunks chunks of 64, all loaded before
+        // any is used
+        for (uint32_t base = 64; base < n1; base += 64 * kCandChunks) {
+          uint64_t cc[kCandChunks];
 #pragma unroll
-      for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
-      if (lane == 0) {
-        cnt2[(int64_t)p * g.tpp + t] = n2;
-        tilecnt[(int64_t)p * g.tpp + t] = pc;
+          for (int q = 0; q < kCandChunks; ++q) {
+            const uint32_t i = base + 64 * q + lane;
+            cc[q] = (i < n1) ? slot[i] : 0ull;
+          }
+#pragma unroll
+          for (int q = 0; q < kCandChunks; ++q) {
+            if (base + 64 * q >= n1) break;  // wave-uniform
+            take(cc[q], base + 64 * q + lane < n1);
+          }
+        }
+        wave_lds_sync();
+        const int64_t w = t * kWordsPerTile + lane;
+        const unsigned long long word = wd[lane];
+        if (w < g.wpp) bits[(int64_t)p * g.wpp + w] = word;
+        uint32_t pc = (uint32_t)__popcll(word);
+#pragma unroll
+        for (int dd = 32; dd >= 1; dd >>= 1) pc += __shfl_xor(pc, dd, 64);
+        if (lane == 0) {
+          cnt2[(int64_t)p * g.tpp + t] = n2;
+          tilecnt[(int64_t)p * g.tpp + t] = pc;
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
     }
   }
   __syncthreads();
-  uint32_t* h = hist + (int64_t)p * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) {
-    const uint32_t c = sh[i];
-    if (c) atomicAdd(h + i, c);
+  if (HIST) {
+    uint32_t* h = hist + (int64_t)p * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kThreads) {
+      const uint32_t c = sh[i];
+      if (c) atomicAdd(h + i, c);
+    }
   }
   if (done) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
@@ -347,6 +366,66 @@ __device__ __forceinline__ void walk_bin(const Geom& g, int p, const uint64_t* _
   }
 }
 
+// The level-2 histogram of the threshold bin's compacted candidates as a
+// pass of its own (layouts with g.hparts > 0): block (h, p) walks its share
+// of partition p's tiles, as walk_bin walks a partition's (the batch's
+// candidates as one flattened sequence), histograms their level-2 digit
+// (key bits 18..7) in LDS and stores the kBins counts whole to part
+// [p][h][*], so no atomics leave the block.  Partitions whose search level
+// 1 finished have no candidates compacted and get zero counts.
+constexpr int kHistThreads = 1024;
+constexpr int kHistWaves = kHistThreads / 64;
+__global__ void __launch_bounds__(kHistThreads)
+l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
+               uint32_t* __restrict__ part) {
+  __shared__ uint32_t sh[kBins];
+  __shared__ uint32_t spre[kHistWaves][64];
+  const int p = g.sp0 + blockIdx.y;
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) sh[i] = 0u;
+  __syncthreads();
+  const int shift = g.levels[0].shift;
+  uint32_t* pre = spre[wave];
+  const uint32_t* c2p = cnt2 + (int64_t)p * g.tpp;
+  const uint64_t* cp = cand + (int64_t)p * g.tpp * kTile;
+  const int64_t nw = (int64_t)gridDim.x * kHistWaves;
+  const int64_t t0 = (int64_t)blockIdx.x * kHistWaves + wave;
+  for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
+    const int64_t tl = tb + (int64_t)lane * nw;
+    uint32_t ct = (tl < g.tpp) ? c2p[tl] : 0u;
+    if (ct > (uint32_t)kTile) ct = (uint32_t)kTile;  // a slot holds at most one tile
+    uint32_t x = ct;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(x, d, 64);
+      if ((int)lane >= d) x += y;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)x, 63, 64);
+    if (total == 0) continue;  // wave-uniform
+    pre[lane] = x - ct;
+    wave_lds_sync();
+    for (uint32_t i0 = 0; i0 < total; i0 += 64 * kWalkBatch) {
+      uint64_t cc[kWalkBatch];
+#pragma unroll
+      for (int u = 0; u < kWalkBatch; ++u) {
+        const uint32_t i = i0 + 64 * u + lane;
+        uint32_t j = 0;
+#pragma unroll
+        for (uint32_t step = 32; step >= 1; step >>= 1)
+          if (pre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
+        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kTile + (i - pre[j])] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kWalkBatch; ++u)
+        if (i0 + 64 * u + lane < total) atomicAdd(&sh[(uint32_t)(cc[u] >> shift) & (uint32_t)(kBins - 1)], 1u);
+    }
+    wave_lds_sync();
+  }
+  __syncthreads();
+  uint32_t* out = part + ((int64_t)p * gridDim.x + blockIdx.x) * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) out[i] = sh[i];
+}
+
 constexpr int kScanBatch = 16;
 
 // ---- the threshold search inside the level-1 bin, and the tile offsets ----
@@ -359,16 +438,55 @@ constexpr int kScanBatch = 16;
 // bin.  Leaves the partition's histogram bins zeroed and its survivor
 // count at zero (or, when the candidates left at the level-2 digit cannot
 // fit the survivor list, at their number).
+template <bool PARTS>
 __global__ void __launch_bounds__(kThreads)
-l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state, uint32_t* __restrict__ nsurv,
-               uint32_t target) {
+l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, const uint32_t* __restrict__ part, PartSel* __restrict__ state,
+               uint32_t* __restrict__ nsurv, uint32_t target) {
   __shared__ uint32_t wtot[kThreads / 64];
   __shared__ uint32_t s_d, s_c, s_above, s_lo;
+  __shared__ uint32_t hs[PARTS ? kBins : 1];
   const int p = g.sp0 + blockIdx.x;
-  uint32_t* h = hist + (int64_t)p * kBins;
+  uint32_t* gh = hist + (int64_t)p * kBins;
   const PartSel cur = state[p];
   if (threadIdx.x == 0) nsurv[p] = 0u;
   if (!cur.done && !cur.fb) {
+    if constexpr (PARTS) {
+      // the sum of the partition's g.hparts parts: thread i adds bins
+      // 4i .. 4i+3 (and the same 1024 bins on) of every part, with 16-byte
+      // loads, four parts at a time
+      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+      const int H = g.hparts;
+      const v4u* pp = reinterpret_cast<const v4u*>(part + (int64_t)p * H * kBins);
+      constexpr int R = kBins / (4 * kThreads), stride = kBins / 4;
+      v4u acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = v4u{0u, 0u, 0u, 0u};
+      int q = 0;
+      for (; q + 4 <= H; q += 4) {
+        v4u x[4][R];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int r = 0; r < R; ++r) x[a][r] = pp[(int64_t)(q + a) * stride + r * kThreads + threadIdx.x];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] += x[a][r];
+      }
+      for (; q < H; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += pp[(int64_t)q * stride + r * kThreads + threadIdx.x];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int b = 4 * (r * kThreads + threadIdx.x);
+        hs[b] = acc[r].x;
+        hs[b + 1] = acc[r].y;
+        hs[b + 2] = acc[r].z;
+        hs[b + 3] = acc[r].w;
+      }
+      __syncthreads();
+    }
+    const uint32_t* h = PARTS ? hs : gh;
     const int shift = g.levels[0].shift;
     constexpr int nb = kBins, per = kBins / kThreads;
     uint32_t s = 0;
@@ -419,7 +537,8 @@ l2_scan_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
+  if (!PARTS)
+    for (int i = threadIdx.x; i < kBins; i += kThreads) gh[i] = 0u;
 }
 
 // Survivors a bin_walk block stages in LDS before it reserves their range of
@@ -1010,10 +1129,19 @@ hipError_t launch_select_tail(const Geom& g, const SelectBufs& w, uint64_t* bits
   int64_t tpw = ((int64_t)g.snp * g.tpp + kSelectWaves - 1) / kSelectWaves;
   tpw = tpw < 1 ? 1 : (tpw > kSelectTilesPerWave ? kSelectTilesPerWave : tpw);
   const unsigned sblocks = (unsigned)((g.tpp + 4 * tpw - 1) / (4 * tpw));
-  cand_select_kernel<<<dim3(sblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist, bits,
-                                                              w.tilecnt);
+  if (g.hparts) {
+    cand_select_kernel<false><<<dim3(sblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist,
+                                                                       bits, w.tilecnt);
+    l2_hist_kernel<<<dim3(g.hparts, g.snp), kHistThreads, 0, s>>>(g, w.cand, w.cnt2, w.part);
+  } else {
+    cand_select_kernel<true><<<dim3(sblocks, g.snp), kThreads, 0, s>>>(g, w.state, w.cand, w.cnt1, w.cnt2, w.hist,
+                                                                      bits, w.tilecnt);
+  }
   if (mark) mark(ctx, 1);
-  l2_scan_kernel<<<g.snp, kThreads, 0, s>>>(g, w.hist, w.state, w.nsurv, capture_target(g));
+  if (g.hparts)
+    l2_scan_kernel<true><<<g.snp, kThreads, 0, s>>>(g, w.hist, w.part, w.state, w.nsurv, capture_target(g));
+  else
+    l2_scan_kernel<false><<<g.snp, kThreads, 0, s>>>(g, w.hist, w.part, w.state, w.nsurv, capture_target(g));
   // rank-parallel emission, and the per-tile bin walk, pay from a mask
   // density of about 5% on (many candidates per tile)
   const bool ranks = g.k * 20 >= g.n_p;

@@ -230,7 +230,9 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
 // The compacted candidate lists are walked one wave per tile.
 // Candidates 0 .. ct-1 of a slot, read by the wave in rounds of
 // kCandChunks chunks of 64 (all loaded before any is used); f(c) runs on
-// the lanes that hold a candidate.
+// the lanes that hold a candidate.  Every load of a round is waited for at
+// once, so none is left outstanding after the loop (code after it then has
+// no reason to wait for the stores issued since).
 template <typename F>
 __device__ __forceinline__ void for_each_cand(const uint64_t* __restrict__ slot, uint32_t ct, uint32_t lane,
                                               F&& f) {
@@ -241,6 +243,8 @@ __device__ __forceinline__ void for_each_cand(const uint64_t* __restrict__ slot,
       const uint32_t i = base + 64 * u + lane;
       cc[u] = (i < ct) ? slot[i] : 0ull;
     }
+#pragma unroll
+    for (int u = 0; u < kCandChunks; ++u) asm volatile("" ::"v"(cc[u]));
 #pragma unroll
     for (int u = 0; u < kCandChunks; ++u)
       if (base + 64 * u + lane < ct) f(cc[u]);
@@ -942,6 +946,11 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
     const uint64_t* slot = cand + ((int64_t)p * g.tpp + tw + j) * kTile;
     c0[j] = (lane < ct) ? slot[lane] : 0ull;
   }
+  // Wait for these loads here, once, before the first store: a wait placed
+  // between the tiles would also wait for the stores of the tiles before.
+#pragma unroll
+  for (int j = 0; j < ET; ++j) asm volatile("" ::"v"(words[j]), "v"(c0[j]));
+  asm volatile("" ::"v"(bl));
 #pragma unroll
   for (int j = 0; j < ET; ++j) {
     const int64_t t = tw + j;

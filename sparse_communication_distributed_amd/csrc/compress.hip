@@ -217,7 +217,6 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                      : (MODE == kModeWorker) ? kWorkerChunkGroup
                      : (MODE == kModeAllPre) ? 4
                                              : kChunkGroup;
-  constexpr bool ALLW = MODE == kModeAll || MODE == kModeAllPre;  // every worker in this pass
   __shared__ uint64_t sw[kWordsPerTile];
   __shared__ uint32_t spre[kWordsPerTile];
   __shared__ uint32_t sh[STEP ? kBins : 1];

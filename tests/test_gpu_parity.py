@@ -380,6 +380,22 @@ def test_step_tiny_200_steps(S):
     run_lockstep(S, cfg, 200, rtol_end=1e-6)
 
 
+@pytest.mark.parametrize("law", ["tensor_sigma", "stress_t3"])
+def test_step_large_sparse_layout(S, law):
+    """A layout of more than 8192 tiles at 1% density, as the large
+    workloads are: the select pass leaves the level-2 histogram to its own
+    pass (parts per partition), and the bin walk takes two tiles per wave as
+    one flattened sequence, its survivors staged per block (the stress law's
+    ties overflow the survivor list at step 1).  Masks and state match the
+    oracle bit for bit over three steps (two for the stress law, whose host
+    generator ranks every partition's magnitudes)."""
+    steps = 3 if law == "tensor_sigma" else 2
+    cfg = W.flat_config("large_sparse", 3 * 3000 * 4096, 3, 2, "0.99", steps=steps, grad_law=law)
+    d = S.dims(cfg.n, cfg.P, cfg.K)
+    assert S.step_pass_count(d, cfg.k) == 1
+    run_lockstep(S, cfg, cfg.steps)
+
+
 @pytest.mark.parametrize("n_p,P,K,sp,law", [
     (10_007, 3, 2, "0.9", "tensor_sigma"),     # ragged, scalar path, P % K != 0
     (3 * 4096 + 100, 4, 4, "0.99", "tensor_sigma"),

@@ -15,7 +15,9 @@
 // select pass then reads only the captures: digits above the threshold
 // digit are selected and written as whole mask words, the threshold
 // digit's captures are compacted in place and histogrammed on the level-2
-// digit (key bits 18..7).  One block per partition resolves level 2; a
+// digit (key bits 18..7): merged per block with atomics, or, at sparse
+// masks on large layouts, by a pass of its own that stores partial
+// histograms.  One block per partition resolves level 2; a
 // pass over the compacted candidates counts those above the level-2 digit
 // per tile and keeps the few at it; one block per partition then resolves
 // the remaining levels (key bits 6..0, then the index bits) on those few

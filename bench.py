@@ -665,9 +665,9 @@ def main():
                     help="allocate the gradient sets before the optimizer state")
     ap.add_argument("--store-v", action="store_true",
                     help="the timed steps also store v_t at the masked entries (AdamS never reads it back)")
-    ap.add_argument("--place", type=int, default=5, metavar="N",
-                    help="choose the placement of e among N allocations at setup, by timing ordinary steps "
-                         "(S.choose_placement; 1: keep the first)")
+    ap.add_argument("--place", type=int, default=17, metavar="N",
+                    help="choose the placement of e among up to N allocations (as free memory allows) at setup, "
+                         "by timing ordinary steps (S.choose_placement; 1: keep the first)")
     ap.add_argument("--calib", action="store_true",
                     help="also time a plain device copy of 1 GiB (the counter calibration kernel)")
     ap.add_argument("--shard", type=int, default=0, metavar="RANKS",

@@ -94,14 +94,12 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Tiles whose first kPreChunks * 64 captured candidates cand_select loads
-// together.
+// Tiles whose first 64 captured candidates cand_select loads together.
 constexpr int kPreTiles = 4;
-constexpr int kPreChunks = 3;
 
-// One wave per tile: reads the tile's captured candidates (the first
-// kPreChunks * 64 with those of the next kPreTiles - 1 tiles of the wave,
-// the rest in rounds of kCandChunks chunks of 64); selects the digits above the level-1 threshold
+// One wave per tile: reads the tile's captured candidates (the first 64
+// with those of the next kPreTiles - 1 tiles of the wave, the rest in rounds
+// of kCandChunks chunks of 64); selects the digits above the level-1 threshold
 // digit into the tile's 64 mask words (written whole, so every word of the
 // partition is written) and counts them; compacts the threshold digit's
 // candidates in place, in order (a write position never passes the
@@ -144,25 +142,18 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
     const int64_t left = (g.tpp - tb + nw - 1) / nw;
     const int nb = left < 64 ? (int)left : 64;
     for (int j0 = 0; j0 < nb; j0 += kPreTiles) {
-      uint64_t cpre[kPreTiles][kPreChunks];
+      uint64_t cpre[kPreTiles];
 #pragma unroll
       for (int u = 0; u < kPreTiles; ++u) {
         const int j = j0 + u;
         const uint32_t nn = (uint32_t)__shfl((int)cv, j & 63, 64);
-#pragma unroll
-        for (int q = 0; q < kPreChunks; ++q) {
-          const uint32_t i = 64 * q + lane;
-          cpre[u][q] = (j < nb && i < nn) ? cpart[(tb + (int64_t)j * nw) * kTile + i] : 0ull;
-        }
+        cpre[u] = (j < nb && lane < nn) ? cpart[(tb + (int64_t)j * nw) * kTile + lane] : 0ull;
       }
       // Wait for the group's loads here, once: the tiles' own code then
-      // has no load to wait for (unless a tile holds more than
-      // kPreChunks * 64 captures), so it never waits for the stores of the
-      // tiles before it.
+      // has no load to wait for (unless a tile holds more than 64
+      // captures), so it never waits for the stores of the tiles before it.
 #pragma unroll
-      for (int u = 0; u < kPreTiles; ++u)
-#pragma unroll
-        for (int q = 0; q < kPreChunks; ++q) asm volatile("" ::"v"(cpre[u][q]));
+      for (int u = 0; u < kPreTiles; ++u) asm volatile("" ::"v"(cpre[u]));
 #pragma unroll
       for (int u = 0; u < kPreTiles; ++u) {
         const int j = j0 + u;
@@ -196,12 +187,10 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
           }
           n2 += (uint32_t)__popcll(kb);
         };
-#pragma unroll
-        for (int q = 0; q < kPreChunks; ++q)
-          if (64u * q < n1) take(cpre[u][q], 64u * q + lane < n1);  // wave-uniform
+        if (n1) take(cpre[u], lane < n1);  // wave-uniform
         // the rest in rounds of kCandChunks chunks of 64, all loaded before
         // any is used
-        for (uint32_t base = 64 * kPreChunks; base < n1; base += 64 * kCandChunks) {
+        for (uint32_t base = 64; base < n1; base += 64 * kCandChunks) {
           uint64_t cc[kCandChunks];
 #pragma unroll
           for (int q = 0; q < kCandChunks; ++q) {

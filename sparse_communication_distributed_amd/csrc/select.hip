@@ -14,8 +14,9 @@
 // from a histogram of a sample of tiles (kScanSample).  The candidate
 // select pass then reads only the captures: digits above the threshold
 // digit are selected and written as whole mask words, the threshold
-// digit's captures are compacted in place and histogrammed on the level-2
-// digit (key bits 18..7): merged per block with atomics, or, at sparse
+// digit's captures are compacted in place, as 32-bit entries (the key bits
+// below the level-1 digit and the offset in the tile), and histogrammed on
+// the level-2 digit (key bits 18..7): merged per block with atomics, or, at sparse
 // masks on large layouts, by a pass of its own that stores partial
 // histograms.  One block per partition resolves level 2; a
 // pass over the compacted candidates counts those above the level-2 digit
@@ -39,6 +40,23 @@ constexpr int kEmitTiles = 4;
 __host__ __device__ constexpr int emit_tiles(bool ranks) { return ranks ? 1 : kEmitTiles; }
 // Entries of a wave's LDS index list in the emission of denser masks.
 constexpr int kEmitList = 1024;
+
+// The threshold bin's candidates, once compacted by the candidate select
+// pass, are 32-bit entries at the start of their tile's slot: the key's bits
+// below the level-1 digit (18..0) over the element's offset in the tile
+// (12 bits).  The partition's level-1 digit, the tile and idx_mask give the
+// composite back.
+constexpr int kOffBits = 12;
+static_assert((int64_t(1) << kOffBits) == kTile && kL1Shift + kOffBits <= 32, "a bin entry fits 32 bits");
+__device__ __forceinline__ uint32_t bin_entry(uint64_t c, uint32_t jl) {
+  return (((uint32_t)(c >> 32) & ((1u << kL1Shift) - 1u)) << kOffBits) | jl;
+}
+// hi: the level-1 digit in place (bin1 << kL1Shift); tile_lo: the tile's
+// first local index
+__device__ __forceinline__ uint64_t bin_composite(uint32_t e, uint32_t hi, uint32_t tile_lo, uint32_t idx_mask) {
+  const uint32_t key = hi | (e >> kOffBits);
+  return ((uint64_t)key << 32) | (uint64_t)(idx_mask - (tile_lo + (e & (uint32_t)(kTile - 1))));
+}
 
 
 
@@ -102,8 +120,9 @@ constexpr int kPreTiles = 4;
 // of kCandChunks chunks of 64); selects the digits above the level-1 threshold
 // digit into the tile's 64 mask words (written whole, so every word of the
 // partition is written) and counts them; compacts the threshold digit's
-// candidates in place, in order (a write position never passes the
-// candidates already read), and (HIST) histograms their level-2 digit,
+// candidates in place, in order, as bin entries (a write never passes the
+// bytes of the candidates already read), and (HIST) histograms their
+// level-2 digit,
 // merging the block's histogram into the partition's with atomics.
 template <bool HIST>
 __global__ void __launch_bounds__(kThreads)
@@ -163,6 +182,7 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
         wd[lane] = 0ull;
         wave_lds_sync();
         uint64_t* slot = cpart + t * kTile;
+        uint32_t* slot32 = reinterpret_cast<uint32_t*>(slot);
         const uint32_t tile_lo = (uint32_t)(t * kTile);
         uint32_t n2 = 0;
         auto take = [&](uint64_t c, bool valid) {
@@ -178,11 +198,11 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
               kmin = key < kmin ? key : kmin;
             }
           }
-          // in-place compaction: a write lands at a position already read
-          // (n2 never passes the candidates read so far)
+          // in-place compaction into 32-bit entries: a write lands in bytes
+          // already read (n2 never passes the candidates read so far)
           const uint64_t kb = __ballot(keep);
           if (keep) {
-            slot[n2 + mbcnt(kb)] = c;
+            slot32[n2 + mbcnt(kb)] = bin_entry(c, jl);
             if (HIST) atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
           }
           n2 += (uint32_t)__popcll(kb);
@@ -229,21 +249,20 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   if (done) block_min_into(kmin, &smin, &state[p].kth);  // block-uniform
 }
 
-// The compacted candidate lists are walked one wave per tile.
-// Candidates 0 .. ct-1 of a slot, read by the wave in rounds of
-// kCandChunks chunks of 64 (all loaded before any is used); f(c) runs on
-// the lanes that hold a candidate.  Every load of a round is waited for at
-// once, so none is left outstanding after the loop (code after it then has
-// no reason to wait for the stores issued since).
+// Bin entries 0 .. ct-1 of a tile (the compacted threshold bin), read by
+// the wave in rounds of kCandChunks chunks of 64 (all loaded before any is
+// used); f(e) runs on the lanes that hold an entry.  Every load of a round
+// is waited for at once, so none is left outstanding after the loop (code
+// after it then has no reason to wait for the stores issued since).
 template <typename F>
-__device__ __forceinline__ void for_each_cand(const uint64_t* __restrict__ slot, uint32_t ct, uint32_t lane,
-                                              F&& f) {
+__device__ __forceinline__ void for_each_entry(const uint32_t* __restrict__ ent, uint32_t ct, uint32_t lane,
+                                               F&& f) {
   for (uint32_t base = 0; base < ct; base += 64 * kCandChunks) {
-    uint64_t cc[kCandChunks];
+    uint32_t cc[kCandChunks];
 #pragma unroll
     for (int u = 0; u < kCandChunks; ++u) {
       const uint32_t i = base + 64 * u + lane;
-      cc[u] = (i < ct) ? slot[i] : 0ull;
+      cc[u] = (i < ct) ? ent[i] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < kCandChunks; ++u) asm volatile("" ::"v"(cc[u]));
@@ -321,18 +340,20 @@ __device__ DigitFind find_digit(const uint32_t* h, int nb, uint32_t rank, uint32
   return r;
 }
 
-// The threshold bin's candidates of partition p (compacted in place in the
-// tile slots), walked by the block's waves.  A wave takes 64 tiles at a
+// The threshold bin's candidates of partition p (the bin entries at the
+// start of the tile slots), walked by the block's waves.  A wave takes 64 tiles at a
 // time (wave w: tiles w, w + W, ..., W waves), scans their counts and walks
 // the 64 slots as one flattened sequence: lane i takes entries i, i + 64,
 // ... and finds its tile by a binary search over the 64 prefixes in LDS, so
 // kWalkBatch loads per lane are in flight at once whatever the tiles' sizes.
-// f(c, j) runs for each candidate c of the batch's tile j; after a batch,
-// end(t, j) runs on the lane of each tile t with candidates (j = the lane).
+// f(c, j) runs for each candidate's composite c (hi: the level-1 digit in
+// place) of the batch's tile j; after a batch, end(t, j) runs on the lane of
+// each tile t with candidates (j = the lane).
 constexpr int kWalkBatch = 8;
 template <typename F, typename E>
-__device__ __forceinline__ void walk_bin(const Geom& g, int p, const uint64_t* __restrict__ cand,
+__device__ __forceinline__ void walk_bin(const Geom& g, int p, uint32_t hi, const uint64_t* __restrict__ cand,
                                          const uint32_t* __restrict__ cnt2, uint32_t* spre, F&& f, E&& end) {
+  const uint32_t* cp = reinterpret_cast<const uint32_t*>(cand + (int64_t)p * g.tpp * kTile);
   const int64_t nw = kResolveWaves;
   const uint32_t lane = lane_id();
   for (int64_t tb = threadIdx.x >> 6; tb < g.tpp; tb += 64 * nw) {
@@ -350,7 +371,7 @@ __device__ __forceinline__ void walk_bin(const Geom& g, int p, const uint64_t* _
     spre[lane] = x - ct;
     wave_lds_sync();
     for (uint32_t i0 = 0; i0 < total; i0 += 64 * kWalkBatch) {
-      uint64_t cc[kWalkBatch];
+      uint32_t cc[kWalkBatch];
       uint32_t jj[kWalkBatch];
 #pragma unroll
       for (int u = 0; u < kWalkBatch; ++u) {
@@ -360,11 +381,12 @@ __device__ __forceinline__ void walk_bin(const Geom& g, int p, const uint64_t* _
         for (uint32_t step = 32; step >= 1; step >>= 1)
           if (spre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
         jj[u] = j;
-        cc[u] = (i < total) ? cand[((int64_t)p * g.tpp + tb + (int64_t)j * nw) * kTile + (i - spre[j])] : 0ull;
+        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * (2 * kTile) + (i - spre[j])] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kWalkBatch; ++u)
-        if (i0 + 64 * u + lane < total) f(cc[u], jj[u]);
+        if (i0 + 64 * u + lane < total)
+          f(bin_composite(cc[u], hi, (uint32_t)((tb + (int64_t)jj[u] * nw) * kTile), g.idx_mask), jj[u]);
     }
     wave_lds_sync();
     if (ct) end(tl, lane);
@@ -374,9 +396,9 @@ __device__ __forceinline__ void walk_bin(const Geom& g, int p, const uint64_t* _
 
 // The level-2 histogram of the threshold bin's compacted candidates as a
 // pass of its own (layouts with g.hparts > 0): block (h, p) walks its share
-// of partition p's tiles, as walk_bin walks a partition's (the batch's
-// candidates as one flattened sequence), histograms their level-2 digit
-// (key bits 18..7) in LDS and stores the kBins counts whole to part
+// of partition p's tiles, as walk_bin walks a partition's (the batch's bin
+// entries as one flattened sequence), histograms their level-2 digit
+// (key bits 18..7, which a bin entry holds whole) in LDS and stores the kBins counts whole to part
 // [p][h][*], so no atomics leave the block.  Partitions whose search level
 // 1 finished have no candidates compacted and get zero counts.
 constexpr int kHistThreads = 1024;
@@ -390,10 +412,10 @@ l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __rest
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < kBins; i += kHistThreads) sh[i] = 0u;
   __syncthreads();
-  const int shift = g.levels[0].shift;
+  const int shift = g.levels[0].shift - 32 + kOffBits;  // the level-2 digit in a bin entry
   uint32_t* pre = spre[wave];
   const uint32_t* c2p = cnt2 + (int64_t)p * g.tpp;
-  const uint64_t* cp = cand + (int64_t)p * g.tpp * kTile;
+  const uint32_t* cp = reinterpret_cast<const uint32_t*>(cand + (int64_t)p * g.tpp * kTile);
   const int64_t nw = (int64_t)gridDim.x * kHistWaves;
   const int64_t t0 = (int64_t)blockIdx.x * kHistWaves + wave;
   for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
@@ -411,7 +433,7 @@ l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __rest
     pre[lane] = x - ct;
     wave_lds_sync();
     for (uint32_t i0 = 0; i0 < total; i0 += 64 * kWalkBatch) {
-      uint64_t cc[kWalkBatch];
+      uint32_t cc[kWalkBatch];
 #pragma unroll
       for (int u = 0; u < kWalkBatch; ++u) {
         const uint32_t i = i0 + 64 * u + lane;
@@ -419,7 +441,7 @@ l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __rest
 #pragma unroll
         for (uint32_t step = 32; step >= 1; step >>= 1)
           if (pre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
-        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kTile + (i - pre[j])] : 0ull;
+        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * (2 * kTile) + (i - pre[j])] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kWalkBatch; ++u)
@@ -599,7 +621,8 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
   uint64_t* sl = surv + (int64_t)p * kSurvivorCap;
   uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
   const uint32_t* c2p = cnt2 + (int64_t)p * g.tpp;
-  const uint64_t* cp = cand + (int64_t)p * g.tpp * kTile;
+  const uint32_t* cp = reinterpret_cast<const uint32_t*>(cand + (int64_t)p * g.tpp * kTile);
+  const uint32_t hi = st.bin1 << kL1Shift;
   // false when level 2 found more candidates at its digit than the list
   // holds: then no wave appends (the walks of the later levels take over)
   const bool listed = nsurv[p] <= (uint32_t)kSurvivorCap;
@@ -667,7 +690,7 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
       pre[lane] = x - ct;
       wave_lds_sync();
       for (uint32_t i0 = 0; i0 < total; i0 += 64 * kWalkBatch) {
-        uint64_t cc[kWalkBatch];
+        uint32_t cc[kWalkBatch];
         uint32_t jj[kWalkBatch];
 #pragma unroll
         for (int u = 0; u < kWalkBatch; ++u) {
@@ -677,13 +700,14 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
           for (uint32_t step = 32; step >= 1; step >>= 1)
             if (pre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
           jj[u] = j;
-          cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kTile + (i - pre[j])] : 0ull;
+          cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * (2 * kTile) + (i - pre[j])] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kWalkBatch; ++u) {
           if (i0 + 64 * u >= total) break;  // wave-uniform
           const bool valid = i0 + 64 * u + lane < total;
-          const bool up = take(cc[u], valid);
+          const uint32_t tile_lo = (uint32_t)((tb + (int64_t)jj[u] * nw) * kTile);
+          const bool up = take(bin_composite(cc[u], hi, tile_lo, g.idx_mask), valid);
           // the chunk's lanes hold consecutive entries, so each tile's
           // entries are a run of lanes: the run's first lane adds its count
           const uint32_t j = jj[u];
@@ -705,11 +729,11 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
       wave_lds_sync();
     } else {
       uint64_t nz = __ballot(ct != 0u);
-      uint64_t cnext = 0ull;
+      uint32_t cnext = 0u;
       if (nz) {  // wave-uniform
         const int j = __builtin_ctzll(nz);
         const uint32_t nn = (uint32_t)__shfl((int)ct, j, 64);
-        if (lane < nn) cnext = cp[(tb + (int64_t)j * nw) * kTile + lane];
+        if (lane < nn) cnext = cp[(tb + (int64_t)j * nw) * (2 * kTile) + lane];
       }
       while (nz) {  // wave-uniform
         const int j = __builtin_ctzll(nz);
@@ -717,25 +741,26 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
         const int64_t t = tb + (int64_t)j * nw;
         const uint32_t n1 = (uint32_t)__shfl((int)ct, j, 64);
         const uint32_t tvj = (uint32_t)__shfl((int)tv, j, 64);
-        const uint64_t c0 = cnext;
+        const uint32_t c0 = cnext;
         if (nz) {
           const int jn = __builtin_ctzll(nz);
           const uint32_t nn = (uint32_t)__shfl((int)ct, jn, 64);
-          cnext = (lane < nn) ? cp[(tb + (int64_t)jn * nw) * kTile + lane] : 0ull;
+          cnext = (lane < nn) ? cp[(tb + (int64_t)jn * nw) * (2 * kTile) + lane] : 0u;
         }
-        const uint64_t* slot = cp + t * kTile;
+        const uint32_t* ent = cp + t * (2 * kTile);
+        const uint32_t tile_lo = (uint32_t)(t * kTile);
         uint32_t add = 0;
         for (uint32_t base = 0; base < n1; base += 64 * kCandChunks) {
-          uint64_t cc[kCandChunks];
+          uint32_t cc[kCandChunks];
 #pragma unroll
           for (int u = 0; u < kCandChunks; ++u) {
             const uint32_t i = base + 64 * u + lane;
-            cc[u] = (base == 0 && u == 0) ? c0 : ((i < n1) ? slot[i] : 0ull);
+            cc[u] = (base == 0 && u == 0) ? c0 : ((i < n1) ? ent[i] : 0u);
           }
 #pragma unroll
           for (int u = 0; u < kCandChunks; ++u) {
             if (base + 64 * u >= n1) break;  // wave-uniform
-            add += take(cc[u], base + 64 * u + lane < n1) ? 1u : 0u;
+            add += take(bin_composite(cc[u], hi, tile_lo, g.idx_mask), base + 64 * u + lane < n1) ? 1u : 0u;
           }
         }
 #pragma unroll
@@ -810,7 +835,7 @@ finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
             if ((c & pm) == pv) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
           }
         } else {
-          walk_bin(g, p, cand, cnt2, spre[wave],
+          walk_bin(g, p, st.bin1 << kL1Shift, cand, cnt2, spre[wave],
                    [&](uint64_t c, uint32_t) {
                      if ((c & pm) == pv) atomicAdd(&sh[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
                    },
@@ -841,7 +866,7 @@ finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
         if (c >= T && jl < (uint32_t)g.n_p) atomicAdd(tc + jl / kTile, 1u);
       }
     } else {
-      walk_bin(g, p, cand, cnt2, spre[wave],
+      walk_bin(g, p, st.bin1 << kL1Shift, cand, cnt2, spre[wave],
                [&](uint64_t c, uint32_t j) {
                  if (((uint32_t)(c >> sh2) & (uint32_t)(kBins - 1)) == d2 && c >= T) atomicAdd(&scnt[wave][j], 1u);
                },
@@ -925,6 +950,7 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
   uint64_t* wb = bits + (int64_t)p * g.wpp;
   uint32_t* out = idx + (int64_t)p * g.k;
   const uint64_t T = state[p].prefix;
+  const uint32_t hi = state[p].bin1 << kL1Shift;
   // Every load the wave's tiles need before their words are complete is
   // issued up front: the words, the candidate counts and offsets (lane j:
   // tile j), then the first 64 candidates of each tile.
@@ -941,12 +967,12 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
   if (ctl > (uint32_t)kTile) ctl = (uint32_t)kTile;  // a slot holds at most one tile
   const uint32_t bl = lt ? tile_off[(int64_t)p * g.tpp + tl] : 0u;
   auto of_tile = [&](uint32_t v, int j) { return ET == 1 ? v : (uint32_t)__shfl((int)v, j, 64); };
-  uint64_t c0[ET];
+  uint32_t c0[ET];
 #pragma unroll
   for (int j = 0; j < ET; ++j) {
     const uint32_t ct = of_tile(ctl, j);
-    const uint64_t* slot = cand + ((int64_t)p * g.tpp + tw + j) * kTile;
-    c0[j] = (lane < ct) ? slot[lane] : 0ull;
+    const uint32_t* ent = reinterpret_cast<const uint32_t*>(cand + ((int64_t)p * g.tpp + tw + j) * kTile);
+    c0[j] = (lane < ct) ? ent[lane] : 0u;
   }
   // Wait for these loads here, once, before the first store: a wait placed
   // between the tiles would also wait for the stores of the tiles before.
@@ -964,14 +990,14 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
     if (ct) {  // wave-uniform
       wd[lane] = 0ull;
       wave_lds_sync();
-      const uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+      const uint32_t* ent = reinterpret_cast<const uint32_t*>(cand + ((int64_t)p * g.tpp + t) * kTile);
       const uint32_t tile_lo = (uint32_t)(t * kTile);
-      auto take = [&](uint64_t c) {
-        const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
-        if (c >= T && jl < (uint32_t)kTile) atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
+      auto take = [&](uint32_t e) {
+        const uint32_t jl = e & (uint32_t)(kTile - 1);
+        if (bin_composite(e, hi, tile_lo, g.idx_mask) >= T) atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
       };
       if (lane < ct) take(c0[j]);
-      if (ct > 64u) for_each_cand(slot + 64, ct - 64u, lane, take);  // wave-uniform
+      if (ct > 64u) for_each_entry(ent + 64, ct - 64u, lane, take);  // wave-uniform
       wave_lds_sync();
       const uint64_t add = wd[lane];
       if (add && w < g.wpp) {

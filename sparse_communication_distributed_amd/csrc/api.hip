@@ -76,7 +76,7 @@ bool make_geom(int64_t n, int P, int K, int64_t k, Geom* g) {
   r.ws_b = o;       o = align256(o + (size_t)K * P * k * 4);
   r.ws_mold = o;    o = align256(o + (size_t)P * k * 4);
   r.ws_hist = o;    o = align256(o + (size_t)P * kBins * 4);
-  r.ws_cand = o;    o = align256(o + (size_t)P * r.tpp * kTile * 8);
+  r.ws_cand = o;    o = align256(o + (size_t)P * r.tpp * kSlotWords * 4);
   r.ws_cnt1 = o;    o = align256(o + (size_t)P * r.tpp * 4);
   r.ws_cnt2 = o;    o = align256(o + (size_t)P * r.tpp * 4);
   r.ws_state = o;   o = align256(o + (size_t)P * sizeof(PartSel));
@@ -193,7 +193,7 @@ Ws ws_view(const Geom& g, void* ws) {
   w.b = reinterpret_cast<float*>(c + g.ws_b);
   w.mold = reinterpret_cast<float*>(c + g.ws_mold);
   w.sel.hist = reinterpret_cast<uint32_t*>(c + g.ws_hist);
-  w.sel.cand = reinterpret_cast<uint64_t*>(c + g.ws_cand);
+  w.sel.cand = reinterpret_cast<uint32_t*>(c + g.ws_cand);
   w.sel.cnt1 = reinterpret_cast<uint32_t*>(c + g.ws_cnt1);
   w.sel.cnt2 = reinterpret_cast<uint32_t*>(c + g.ws_cnt2);
   w.sel.state = reinterpret_cast<PartSel*>(c + g.ws_state);

@@ -5,9 +5,9 @@
 //    technical summary §2), fused with the owner's first-moment statistic
 //    (technical summary §2, lagged mask built from first-moment statistics)
 //    and the capture of the selection candidates: owner keys at or above a
-//    per-partition bound `lo` are written, as unique (key, index)
-//    composites, to a per-tile candidate slot, and a level-1 histogram of
-//    the captured keys is kept.  The step runs it as one pass over all
+//    per-partition bound `lo` are written, each with its offset in the tile
+//    (key and offset identify the element), to a per-tile candidate slot,
+//    and a level-1 histogram of the captured keys is kept.  The step runs it as one pass over all
 //    workers, or as one pass per non-owner worker followed by the owner's
 //    pass (MODE below).
 //  * stat_kernel: the statistic alone, for the step-1 bootstrap (from
@@ -104,13 +104,13 @@ __device__ __forceinline__ void load_tile_words(const uint64_t* __restrict__ bit
   }
 }
 
-// Wave-cooperative capture of the lane's 4 keys (elements lj .. lj+3):
-// flagged keys are appended to the tile's candidate slot at positions
-// handed out by the LDS counter `tcnt`, and counted in the LDS histogram.
-// Every lane of the wave must call this (ballots and a lane-0 broadcast).
+// Wave-cooperative capture of the lane's 4 keys (elements lj .. lj+3 of
+// the partition): flagged keys are appended to the tile's candidate slot,
+// the key and its offset in the tile at positions handed out by the LDS
+// counter `tcnt`, and counted in the LDS histogram.  Every lane of the wave
+// must call this (ballots and a lane-0 broadcast).
 __device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], uint32_t lj,
-                                         uint32_t idx_mask, uint64_t* __restrict__ slot,
-                                         uint32_t* tcnt, uint32_t* sh) {
+                                         uint32_t* __restrict__ slot, uint32_t* tcnt, uint32_t* sh) {
   uint64_t B[4];
   uint32_t pre[4], tot = 0;
 #pragma unroll
@@ -123,11 +123,13 @@ __device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], 
   uint32_t base = 0;
   if ((threadIdx.x & 63) == 0) base = atomicAdd(tcnt, tot);
   base = __shfl(base, 0, 64);
+  uint16_t* offs = reinterpret_cast<uint16_t*>(slot + kTile);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (f[q]) {
-      const uint32_t j = lj + q;
-      slot[base + pre[q] + mbcnt(B[q])] = ((uint64_t)kk[q] << 32) | (uint64_t)(idx_mask - j);
+      const uint32_t pos = base + pre[q] + mbcnt(B[q]);
+      slot[pos] = kk[q];
+      offs[pos] = (uint16_t)((lj + q) & (uint32_t)(kTile - 1));
       atomicAdd(&sh[kk[q] >> kL1Shift], 1u);
     }
   }
@@ -207,7 +209,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
                 float* __restrict__ b, float* __restrict__ m, float* __restrict__ v,
                 float* __restrict__ w, float* __restrict__ mold, AdamsC ac,
-                const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
+                const uint32_t* __restrict__ lo_in, uint32_t* __restrict__ cand,
                 uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int p0, int64_t e_stride,
                 const float* __restrict__ ibc_dev, int rot) {
   static_assert(MODE == kModeAll || (MODE == kModeWorker && !STEP) || (MODE == kModeOwner && STEP) ||
@@ -256,7 +258,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
     // ranks stay inside partition p's k entries for any mask with k bits per
     // partition; the bound keeps a malformed mask in bounds
     const int64_t rlim = (int64_t)(p + 1) * g.k - rbase;
-    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    uint32_t* slot = cand + ((int64_t)p * g.tpp + t) * kSlotWords;
     const float* mt = m + pbase + tb;
 
     for (int cg = 0; cg < 4; cg += CG) {
@@ -337,7 +339,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
                 f[q] = valid && kk[q] >= lo;
               }
-              capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+              capture4(kk, f, (uint32_t)tb + o[u], slot, &tcnt, sh);
             }
           }
         };
@@ -401,7 +403,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
                 kk[q] = valid ? stat_key(ma[u][q], a[q], ac.b1, ac.c1) : 0u;
                 f[q] = valid && kk[q] >= lo;
               }
-              capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+              capture4(kk, f, (uint32_t)tb + o[u], slot, &tcnt, sh);
             }
           }
         }
@@ -520,7 +522,7 @@ __global__ void __launch_bounds__(kThreads, kWorkerMinWaves)
 shard_pass_kernel(Geom g, int rank, const float* __restrict__ grads, float* __restrict__ e,
                   const uint64_t* __restrict__ bits, const uint32_t* __restrict__ tile_off,
                   float* __restrict__ b, const float* __restrict__ m, float b1, float c1,
-                  const uint32_t* __restrict__ lo_in, uint64_t* __restrict__ cand,
+                  const uint32_t* __restrict__ lo_in, uint32_t* __restrict__ cand,
                   uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist) {
   constexpr int CG = kWorkerChunkGroup;
   __shared__ uint64_t sw[kWordsPerTile];
@@ -546,7 +548,7 @@ shard_pass_kernel(Geom g, int rank, const float* __restrict__ grads, float* __re
     const uint32_t tn = (uint32_t)min<int64_t>(kTile, g.n_p - tb);
     const int64_t rbase = (int64_t)p * g.k + tile_off[(int64_t)p * g.tpp + t];
     const int64_t rlim = (int64_t)(p + 1) * g.k - rbase;  // a malformed mask stays in bounds
-    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    uint32_t* slot = cand + ((int64_t)p * g.tpp + t) * kSlotWords;
     const float* gt = grads + pbase + tb;
     float* et = e + pbase + tb;
     const float* mt = m + pbase + tb;
@@ -598,7 +600,7 @@ shard_pass_kernel(Geom g, int rank, const float* __restrict__ grads, float* __re
             kk[q] = valid ? stat_key(ma[u][q], a[q], b1, c1) : 0u;
             f[q] = valid && kk[q] >= lo;
           }
-          capture4(kk, f, (uint32_t)tb + o[u], g.idx_mask, slot, &tcnt, sh);
+          capture4(kk, f, (uint32_t)tb + o[u], slot, &tcnt, sh);
         }
       }
     }
@@ -624,7 +626,7 @@ __global__ void __launch_bounds__(kThreads)
 stat_kernel(Geom g, PartSel* __restrict__ state, int only_fb, const float* __restrict__ stat,
             const float* __restrict__ m, const float* __restrict__ grads, const float* __restrict__ e,
             const float* __restrict__ b, const float* __restrict__ mold, const uint64_t* __restrict__ bits,
-            const uint32_t* __restrict__ tile_off, float b1, float c1, uint64_t* __restrict__ cand,
+            const uint32_t* __restrict__ tile_off, float b1, float c1, uint32_t* __restrict__ cand,
             uint32_t* __restrict__ cnt1, uint32_t* __restrict__ hist, int tile_step, int64_t g_stride,
             int64_t e_stride, int64_t b_stride, int then_mode, uint32_t target, uint32_t* __restrict__ arrive) {
   __shared__ uint64_t sw[kWordsPerTile];
@@ -655,7 +657,7 @@ stat_kernel(Geom g, PartSel* __restrict__ state, int only_fb, const float* __res
     __syncthreads();
     const int64_t rbase = (SRC == 2) ? (int64_t)p * g.k + tile_off[(int64_t)p * g.tpp + t] : 0;
     const int64_t rend = (int64_t)(p + 1) * g.k;
-    uint64_t* slot = cand + ((int64_t)p * g.tpp + t) * kTile;
+    uint32_t* slot = cand + ((int64_t)p * g.tpp + t) * kSlotWords;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int64_t lj = t * kTile + c * 1024 + 4 * threadIdx.x;
@@ -705,7 +707,7 @@ stat_kernel(Geom g, PartSel* __restrict__ state, int only_fb, const float* __res
         bool f[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) f[q] = (lj + q < g.n_p) && kk[q] >= lo;
-        capture4(kk, f, (uint32_t)lj, g.idx_mask, slot, &tcnt, sh);
+        capture4(kk, f, (uint32_t)lj, slot, &tcnt, sh);
       }
     }
     if (PHASE == 1) {
@@ -818,7 +820,7 @@ hipError_t launch_step_pass(const Geom& g, const StepArgs& a, bool vec, bool seg
 
 hipError_t launch_shard_pass(const Geom& g, int rank, const float* grads, float* e, const uint64_t* bits,
                              const uint32_t* tile_off, float* b, const float* m, float b1, float c1,
-                             const uint32_t* lo, uint64_t* cand, uint32_t* cnt1, uint32_t* hist, bool vec,
+                             const uint32_t* lo, uint32_t* cand, uint32_t* cnt1, uint32_t* hist, bool vec,
                              hipStream_t s) {
   const dim3 grid = stream_grid(g.P, g.G);
   if (vec)

@@ -13,6 +13,10 @@ namespace scape {
 // Compaction / work tile: 4096 elements = 64 mask words.
 constexpr int64_t kTile = 4096;
 constexpr int kWordsPerTile = 64;
+// A tile's candidate slot, in 32-bit words: the captured keys u32[kTile],
+// then their offsets in the tile u16[kTile].  After the candidate select
+// pass, the keys' place holds the threshold bin's 32-bit entries.
+constexpr int64_t kSlotWords = kTile + kTile / 2;
 // Radix digit width and histogram size for the threshold search.
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
@@ -127,7 +131,7 @@ struct StatArgs {
   const uint64_t* bits;
   const uint32_t* tile_off;
   float b1, c1;
-  uint64_t* cand;
+  uint32_t* cand;  // candidate slots, kSlotWords per tile
   uint32_t* cnt1;
   uint32_t* hist;
   int tile_step;  // visit tiles 0, tile_step, 2*tile_step, ... (a sample when > 1)
@@ -144,7 +148,7 @@ struct StatArgs {
 // Buffers of the selection pipeline (workspace views).
 struct SelectBufs {
   uint32_t* hist;
-  uint64_t* cand;
+  uint32_t* cand;  // candidate slots, kSlotWords per tile
   uint32_t* cnt1;
   uint32_t* cnt2;
   PartSel* state;
@@ -168,7 +172,7 @@ struct StepArgs {
   float* mold;               // [P*k] pre-update m of the masked elements
   float b1, b2, c1, c2, ibc1, ibc2, eps, wd, lr;
   const uint32_t* lo;        // [P] capture bounds
-  uint64_t* cand;
+  uint32_t* cand;  // candidate slots, kSlotWords per tile
   uint32_t* cnt1;
   uint32_t* hist;
   int p0, nparts;            // partitions of this launch
@@ -196,7 +200,7 @@ bool multi_pass_pays(const Geom& g);
 // the partitions the rank owns.
 hipError_t launch_shard_pass(const Geom& g, int rank, const float* grads, float* e, const uint64_t* bits,
                              const uint32_t* tile_off, float* b, const float* m, float b1, float c1,
-                             const uint32_t* lo, uint64_t* cand, uint32_t* cnt1, uint32_t* hist, bool vec,
+                             const uint32_t* lo, uint32_t* cand, uint32_t* cnt1, uint32_t* hist, bool vec,
                              hipStream_t s);
 hipError_t launch_step_passes(const Geom& g, const StepArgs& a, bool vec, bool seg, hipStream_t s);
 

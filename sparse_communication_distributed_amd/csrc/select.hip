@@ -6,7 +6,8 @@
 //     c = (key << 32) | (idx_mask - local_index)
 // so that "the k largest composites" is exactly "the k largest keys, ties to
 // the lower index".  The streaming pass that produces the keys captures,
-// per tile, every key at or above a bound `lo` together with a level-1
+// per tile, every key at or above a bound `lo` (with the element's offset
+// in the tile) together with a level-1
 // histogram (key bits 30..19) of the captured keys.  If a partition captured
 // at least k keys, its top k lie among the captures; otherwise an exact
 // fallback recounts all its keys to find the level-1 digit and recaptures
@@ -42,14 +43,14 @@ __host__ __device__ constexpr int emit_tiles(bool ranks) { return ranks ? 1 : kE
 constexpr int kEmitList = 1024;
 
 // The threshold bin's candidates, once compacted by the candidate select
-// pass, are 32-bit entries at the start of their tile's slot: the key's bits
-// below the level-1 digit (18..0) over the element's offset in the tile
-// (12 bits).  The partition's level-1 digit, the tile and idx_mask give the
+// pass, are 32-bit entries in the keys' place of their tile's slot: the
+// key's bits below the level-1 digit (18..0) over the element's offset in
+// the tile (12 bits).  The partition's level-1 digit, the tile and idx_mask give the
 // composite back.
 constexpr int kOffBits = 12;
 static_assert((int64_t(1) << kOffBits) == kTile && kL1Shift + kOffBits <= 32, "a bin entry fits 32 bits");
-__device__ __forceinline__ uint32_t bin_entry(uint64_t c, uint32_t jl) {
-  return (((uint32_t)(c >> 32) & ((1u << kL1Shift) - 1u)) << kOffBits) | jl;
+__device__ __forceinline__ uint32_t bin_entry(uint32_t key, uint32_t jl) {
+  return ((key & ((1u << kL1Shift) - 1u)) << kOffBits) | jl;
 }
 // hi: the level-1 digit in place (bin1 << kL1Shift); tile_lo: the tile's
 // first local index
@@ -115,18 +116,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Tiles whose first 64 captured candidates cand_select loads together.
 constexpr int kPreTiles = 4;
 
-// One wave per tile: reads the tile's captured candidates (the first 64
-// with those of the next kPreTiles - 1 tiles of the wave, the rest in rounds
-// of kCandChunks chunks of 64); selects the digits above the level-1 threshold
-// digit into the tile's 64 mask words (written whole, so every word of the
-// partition is written) and counts them; compacts the threshold digit's
-// candidates in place, in order, as bin entries (a write never passes the
-// bytes of the candidates already read), and (HIST) histograms their
-// level-2 digit,
-// merging the block's histogram into the partition's with atomics.
+// One wave per tile: reads the tile's captured keys and offsets (the first
+// 64 with those of the next kPreTiles - 1 tiles of the wave, the rest in
+// rounds of kCandChunks chunks of 64); selects the digits above the level-1
+// threshold digit into the tile's 64 mask words (written whole, so every
+// word of the partition is written) and counts them; compacts the threshold
+// digit's candidates in place, in order, as bin entries over the keys (a
+// write never passes the keys already read), and (HIST) histograms their
+// level-2 digit, merging the block's histogram into the partition's with
+// atomics.
 template <bool HIST>
 __global__ void __launch_bounds__(kThreads)
-cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ cand,
+cand_select_kernel(Geom g, PartSel* __restrict__ state, uint32_t* __restrict__ cand,
                    const uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2,
                    uint32_t* __restrict__ hist, uint64_t* __restrict__ bits,
                    uint32_t* __restrict__ tilecnt) {
@@ -137,7 +138,7 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   const PartSel st = state[p];
   const uint32_t B1 = st.bin1;
   const bool done = st.done != 0;
-  const int l2shift = g.levels[0].shift;
+  const int l2shift = g.levels[0].shift - 32;  // the level-2 digit in a key
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   unsigned long long* wd = words[wave];
   uint32_t kmin = 0xffffffffu;  // smallest key selected whole from the threshold digit
@@ -153,7 +154,7 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
   const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
   const int64_t t0 = (int64_t)blockIdx.x * (kThreads / 64) + wave;
   const uint32_t* c1p = cnt1 + (int64_t)p * g.tpp;
-  uint64_t* cpart = cand + (int64_t)p * g.tpp * kTile;
+  uint32_t* cpart = cand + (int64_t)p * g.tpp * kSlotWords;
   for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
     const int64_t tl = tb + (int64_t)lane * nw;
     uint32_t cv = (tl < g.tpp) ? c1p[tl] : 0u;
@@ -161,18 +162,21 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
     const int64_t left = (g.tpp - tb + nw - 1) / nw;
     const int nb = left < 64 ? (int)left : 64;
     for (int j0 = 0; j0 < nb; j0 += kPreTiles) {
-      uint64_t cpre[kPreTiles];
+      uint32_t kpre[kPreTiles], opre[kPreTiles];
 #pragma unroll
       for (int u = 0; u < kPreTiles; ++u) {
         const int j = j0 + u;
         const uint32_t nn = (uint32_t)__shfl((int)cv, j & 63, 64);
-        cpre[u] = (j < nb && lane < nn) ? cpart[(tb + (int64_t)j * nw) * kTile + lane] : 0ull;
+        const uint32_t* sj = cpart + (tb + (int64_t)j * nw) * kSlotWords;
+        const bool in = j < nb && lane < nn;
+        kpre[u] = in ? sj[lane] : 0u;
+        opre[u] = in ? reinterpret_cast<const uint16_t*>(sj + kTile)[lane] : 0u;
       }
       // Wait for the group's loads here, once: the tiles' own code then
       // has no load to wait for (unless a tile holds more than 64
       // captures), so it never waits for the stores of the tiles before it.
 #pragma unroll
-      for (int u = 0; u < kPreTiles; ++u) asm volatile("" ::"v"(cpre[u]));
+      for (int u = 0; u < kPreTiles; ++u) asm volatile("" ::"v"(kpre[u]), "v"(opre[u]));
 #pragma unroll
       for (int u = 0; u < kPreTiles; ++u) {
         const int j = j0 + u;
@@ -181,46 +185,41 @@ cand_select_kernel(Geom g, PartSel* __restrict__ state, uint64_t* __restrict__ c
         const uint32_t n1 = (uint32_t)__shfl((int)cv, j, 64);
         wd[lane] = 0ull;
         wave_lds_sync();
-        uint64_t* slot = cpart + t * kTile;
-        uint32_t* slot32 = reinterpret_cast<uint32_t*>(slot);
-        const uint32_t tile_lo = (uint32_t)(t * kTile);
+        uint32_t* slot = cpart + t * kSlotWords;
+        const uint16_t* offs = reinterpret_cast<const uint16_t*>(slot + kTile);
         uint32_t n2 = 0;
-        auto take = [&](uint64_t c, bool valid) {
-          const uint32_t d1 = (uint32_t)(c >> (32 + kL1Shift)) & (kBins - 1);
-          const uint32_t jl = g.idx_mask - (uint32_t)c - tile_lo;
-          const bool ok = valid && jl < (uint32_t)kTile;  // false only for a corrupted slot
-          const bool sel = ok && (d1 > B1 || (done && d1 == B1));
-          const bool keep = ok && !done && d1 == B1;
+        auto take = [&](uint32_t key, uint32_t jl, bool valid) {
+          const uint32_t d1 = (key >> kL1Shift) & (kBins - 1);
+          const bool sel = valid && (d1 > B1 || (done && d1 == B1));
+          const bool keep = valid && !done && d1 == B1;
           if (sel) {
             atomicOr(&wd[jl >> 6], 1ull << (jl & 63));
-            if (d1 == B1) {
-              const uint32_t key = (uint32_t)(c >> 32);
-              kmin = key < kmin ? key : kmin;
-            }
+            if (d1 == B1) kmin = key < kmin ? key : kmin;
           }
-          // in-place compaction into 32-bit entries: a write lands in bytes
+          // in-place compaction into bin entries: a write lands on a key
           // already read (n2 never passes the candidates read so far)
           const uint64_t kb = __ballot(keep);
           if (keep) {
-            slot32[n2 + mbcnt(kb)] = bin_entry(c, jl);
-            if (HIST) atomicAdd(&sh[(uint32_t)(c >> l2shift) & (kBins - 1)], 1u);
+            slot[n2 + mbcnt(kb)] = bin_entry(key, jl);
+            if (HIST) atomicAdd(&sh[(key >> l2shift) & (kBins - 1)], 1u);
           }
           n2 += (uint32_t)__popcll(kb);
         };
-        if (n1) take(cpre[u], lane < n1);  // wave-uniform
+        if (n1) take(kpre[u], opre[u] & (uint32_t)(kTile - 1), lane < n1);  // wave-uniform
         // the rest in rounds of kCandChunks chunks of 64, all loaded before
         // any is used
         for (uint32_t base = 64; base < n1; base += 64 * kCandChunks) {
-          uint64_t cc[kCandChunks];
+          uint32_t kc[kCandChunks], oc[kCandChunks];
 #pragma unroll
           for (int q = 0; q < kCandChunks; ++q) {
             const uint32_t i = base + 64 * q + lane;
-            cc[q] = (i < n1) ? slot[i] : 0ull;
+            kc[q] = (i < n1) ? slot[i] : 0u;
+            oc[q] = (i < n1) ? offs[i] : 0u;
           }
 #pragma unroll
           for (int q = 0; q < kCandChunks; ++q) {
             if (base + 64 * q >= n1) break;  // wave-uniform
-            take(cc[q], base + 64 * q + lane < n1);
+            take(kc[q], oc[q] & (uint32_t)(kTile - 1), base + 64 * q + lane < n1);
           }
         }
         wave_lds_sync();
@@ -351,9 +350,9 @@ __device__ DigitFind find_digit(const uint32_t* h, int nb, uint32_t rank, uint32
 // each tile t with candidates (j = the lane).
 constexpr int kWalkBatch = 8;
 template <typename F, typename E>
-__device__ __forceinline__ void walk_bin(const Geom& g, int p, uint32_t hi, const uint64_t* __restrict__ cand,
+__device__ __forceinline__ void walk_bin(const Geom& g, int p, uint32_t hi, const uint32_t* __restrict__ cand,
                                          const uint32_t* __restrict__ cnt2, uint32_t* spre, F&& f, E&& end) {
-  const uint32_t* cp = reinterpret_cast<const uint32_t*>(cand + (int64_t)p * g.tpp * kTile);
+  const uint32_t* cp = cand + (int64_t)p * g.tpp * kSlotWords;
   const int64_t nw = kResolveWaves;
   const uint32_t lane = lane_id();
   for (int64_t tb = threadIdx.x >> 6; tb < g.tpp; tb += 64 * nw) {
@@ -381,7 +380,7 @@ __device__ __forceinline__ void walk_bin(const Geom& g, int p, uint32_t hi, cons
         for (uint32_t step = 32; step >= 1; step >>= 1)
           if (spre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
         jj[u] = j;
-        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * (2 * kTile) + (i - spre[j])] : 0u;
+        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kSlotWords + (i - spre[j])] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kWalkBatch; ++u)
@@ -404,7 +403,7 @@ __device__ __forceinline__ void walk_bin(const Geom& g, int p, uint32_t hi, cons
 constexpr int kHistThreads = 1024;
 constexpr int kHistWaves = kHistThreads / 64;
 __global__ void __launch_bounds__(kHistThreads)
-l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
+l2_hist_kernel(Geom g, const uint32_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
                uint32_t* __restrict__ part) {
   __shared__ uint32_t sh[kBins];
   __shared__ uint32_t spre[kHistWaves][64];
@@ -415,7 +414,7 @@ l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __rest
   const int shift = g.levels[0].shift - 32 + kOffBits;  // the level-2 digit in a bin entry
   uint32_t* pre = spre[wave];
   const uint32_t* c2p = cnt2 + (int64_t)p * g.tpp;
-  const uint32_t* cp = reinterpret_cast<const uint32_t*>(cand + (int64_t)p * g.tpp * kTile);
+  const uint32_t* cp = cand + (int64_t)p * g.tpp * kSlotWords;
   const int64_t nw = (int64_t)gridDim.x * kHistWaves;
   const int64_t t0 = (int64_t)blockIdx.x * kHistWaves + wave;
   for (int64_t tb = t0; tb < g.tpp; tb += 64 * nw) {
@@ -441,7 +440,7 @@ l2_hist_kernel(Geom g, const uint64_t* __restrict__ cand, const uint32_t* __rest
 #pragma unroll
         for (uint32_t step = 32; step >= 1; step >>= 1)
           if (pre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
-        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * (2 * kTile) + (i - pre[j])] : 0u;
+        cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kSlotWords + (i - pre[j])] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kWalkBatch; ++u)
@@ -593,7 +592,7 @@ constexpr int kFlatTilesPerWave = 32;
 // walked.
 template <bool FLAT>
 __global__ void __launch_bounds__(kThreads)
-bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict__ cand,
+bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint32_t* __restrict__ cand,
                 const uint32_t* __restrict__ cnt2, uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ hist,
                 uint64_t* __restrict__ surv, uint32_t* __restrict__ nsurv) {
   __shared__ uint32_t sh[1 << (kL1Shift - kDigitBits)];
@@ -621,7 +620,7 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
   uint64_t* sl = surv + (int64_t)p * kSurvivorCap;
   uint32_t* tc = tilecnt + (int64_t)p * g.tpp;
   const uint32_t* c2p = cnt2 + (int64_t)p * g.tpp;
-  const uint32_t* cp = reinterpret_cast<const uint32_t*>(cand + (int64_t)p * g.tpp * kTile);
+  const uint32_t* cp = cand + (int64_t)p * g.tpp * kSlotWords;
   const uint32_t hi = st.bin1 << kL1Shift;
   // false when level 2 found more candidates at its digit than the list
   // holds: then no wave appends (the walks of the later levels take over)
@@ -700,7 +699,7 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
           for (uint32_t step = 32; step >= 1; step >>= 1)
             if (pre[j + step] <= i) j += step;  // the last tile whose prefix is at most i
           jj[u] = j;
-          cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * (2 * kTile) + (i - pre[j])] : 0u;
+          cc[u] = (i < total) ? cp[(tb + (int64_t)j * nw) * kSlotWords + (i - pre[j])] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kWalkBatch; ++u) {
@@ -733,7 +732,7 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
       if (nz) {  // wave-uniform
         const int j = __builtin_ctzll(nz);
         const uint32_t nn = (uint32_t)__shfl((int)ct, j, 64);
-        if (lane < nn) cnext = cp[(tb + (int64_t)j * nw) * (2 * kTile) + lane];
+        if (lane < nn) cnext = cp[(tb + (int64_t)j * nw) * kSlotWords + lane];
       }
       while (nz) {  // wave-uniform
         const int j = __builtin_ctzll(nz);
@@ -745,9 +744,9 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
         if (nz) {
           const int jn = __builtin_ctzll(nz);
           const uint32_t nn = (uint32_t)__shfl((int)ct, jn, 64);
-          cnext = (lane < nn) ? cp[(tb + (int64_t)jn * nw) * (2 * kTile) + lane] : 0u;
+          cnext = (lane < nn) ? cp[(tb + (int64_t)jn * nw) * kSlotWords + lane] : 0u;
         }
-        const uint32_t* ent = cp + t * (2 * kTile);
+        const uint32_t* ent = cp + t * kSlotWords;
         const uint32_t tile_lo = (uint32_t)(t * kTile);
         uint32_t add = 0;
         for (uint32_t base = 0; base < n1; base += 64 * kCandChunks) {
@@ -796,7 +795,7 @@ bin_walk_kernel(Geom g, PartSel* __restrict__ state, const uint64_t* __restrict_
 // partition's histogram bins zeroed.
 __global__ void __launch_bounds__(kResolveThreads)
 finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
-              const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
+              const uint32_t* __restrict__ cand, const uint32_t* __restrict__ cnt2,
               const uint64_t* __restrict__ surv, const uint32_t* __restrict__ nsurv,
               uint32_t* __restrict__ tilecnt, uint32_t* __restrict__ tile_off, uint32_t* __restrict__ meta_out) {
   __shared__ uint32_t sh[kBins];
@@ -935,7 +934,7 @@ finish_kernel(Geom g, uint32_t* __restrict__ hist, PartSel* __restrict__ state,
 // list.
 template <bool RANKS>
 __global__ void __launch_bounds__(kThreads)
-emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restrict__ cand,
+emit_kernel(Geom g, const PartSel* __restrict__ state, const uint32_t* __restrict__ cand,
             const uint32_t* __restrict__ cnt2, uint64_t* __restrict__ bits,
             const uint32_t* __restrict__ tile_off, uint32_t* __restrict__ idx) {
   __shared__ unsigned long long swords[kThreads / 64][kWordsPerTile];
@@ -971,7 +970,7 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
 #pragma unroll
   for (int j = 0; j < ET; ++j) {
     const uint32_t ct = of_tile(ctl, j);
-    const uint32_t* ent = reinterpret_cast<const uint32_t*>(cand + ((int64_t)p * g.tpp + tw + j) * kTile);
+    const uint32_t* ent = cand + ((int64_t)p * g.tpp + tw + j) * kSlotWords;
     c0[j] = (lane < ct) ? ent[lane] : 0u;
   }
   // Wait for these loads here, once, before the first store: a wait placed
@@ -990,7 +989,7 @@ emit_kernel(Geom g, const PartSel* __restrict__ state, const uint64_t* __restric
     if (ct) {  // wave-uniform
       wd[lane] = 0ull;
       wave_lds_sync();
-      const uint32_t* ent = reinterpret_cast<const uint32_t*>(cand + ((int64_t)p * g.tpp + t) * kTile);
+      const uint32_t* ent = cand + ((int64_t)p * g.tpp + t) * kSlotWords;
       const uint32_t tile_lo = (uint32_t)(t * kTile);
       auto take = [&](uint32_t e) {
         const uint32_t jl = e & (uint32_t)(kTile - 1);

@@ -129,14 +129,14 @@ scape_status check_betas(const scape_betas& b, float lr) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-// Whole 64-byte segments of w, m (and v) per 16 elements: needs aligned
-// segments.  A segment costs the read of w's line, which the update reads
-// anyway, so without v it pays at any density; with v it also reads v's
-// line, which pays only where masked elements are not too rare (at a
-// density of 0.1% that read costs more than the whole writes save).
+// Whole 64-byte lines of w, m (and v) per 16 elements: needs 64-byte
+// aligned rows (the lines follow the rows' alignment, whatever a
+// partition's first element).  A line costs the read of w's line, which the
+// update reads anyway, so without v it pays at any density; with v it also
+// reads v's line, which pays only where masked elements are not too rare (at
+// a density of 0.1% that read costs more than the whole writes save).
 bool seg_ok(const Geom& g, const void* w, const void* m, const void* v) {
-  return g.n_p % 16 == 0 && (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0 &&
-         (v == nullptr || g.k * 200 >= g.n_p);
+  return (((uintptr_t)w | (uintptr_t)m | (uintptr_t)v) & 63u) == 0 && (v == nullptr || g.k * 200 >= g.n_p);
 }
 
 // fp32(1 / (1 - beta^t)), beta^t formed by t binary64 multiplications by

@@ -135,6 +135,16 @@ __device__ __forceinline__ void capture4(const uint32_t kk[4], const bool f[4], 
   }
 }
 
+// The lanes that write this lane's 64-byte line of w / m / v as one
+// segment.  A line is 4 lanes x 4 elements; where the partition's first
+// element is not 16-aligned, the lines start `sl` lanes before the
+// partition's 4-lane groups (sl = (partition base mod 16) / 4).  A line that
+// crosses the wave's 256 elements is written by each of its lanes alone.
+__device__ __forceinline__ uint64_t seg_lanes(uint32_t lane, uint32_t sl) {
+  const int l0 = (int)((lane + sl) & ~3u) - (int)sl;
+  return (l0 >= 0 && l0 <= 60) ? (0xfull << l0) : (1ull << lane);
+}
+
 // Grid of the streaming passes: (G, partitions); the dispatcher fills the
 // device partition by partition, G blocks each.
 __device__ __forceinline__ int block_part() { return blockIdx.y; }
@@ -233,6 +243,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
   const int p = p0 + block_part();
   const int64_t ebase = (int64_t)(p - p0) * g.n_p;
   const int64_t pbase = (int64_t)p * g.n_p;
+  const uint32_t sl = (uint32_t)(pbase & 15) >> 2;  // line shift of SEG (w, m, v 64-byte aligned)
   const int64_t wbase = (int64_t)p * g.wpp;
   const int64_t pk = (int64_t)g.P * g.k;
   const int owner = (int)(((int64_t)p * g.K) / g.P);
@@ -291,7 +302,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
           if (SEG) {
             const uint32_t lane = threadIdx.x & 63u;
             const uint64_t act = __ballot(nib[u] != 0u);
-            if (((act >> (lane & ~3u)) & 0xfull) && o[u] < tn) load4t(wt0, o[u], wpre[u]);
+            if ((act & seg_lanes(lane, sl)) && o[u] < tn) load4t(wt0, o[u], wpre[u]);
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -425,7 +436,7 @@ compress_kernel(Geom g, const float* __restrict__ grads, float* __restrict__ e,
             // measured faster than scattered element writes.
             const uint32_t lane = threadIdx.x & 63u;
             const uint64_t act = __ballot(nib[u] != 0u);
-            if (!((act >> (lane & ~3u)) & 0xfull) || o[u] >= tn) continue;
+            if (!(act & seg_lanes(lane, sl)) || o[u] >= tn) continue;
             if (MODE == kModeOwner) {
 #pragma unroll
               for (int q = 0; q < 4; ++q) wo[q] = wpre[u][q];

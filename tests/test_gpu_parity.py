@@ -414,7 +414,7 @@ def test_step_small_shapes(S, n_p, P, K, sp, law):
 
 
 @pytest.mark.parametrize("n_p,P,K,sp,law", [
-    (7652, 3, 2, "0.9", "tensor_sigma"),          # n_p % 16 == 4: vector streams, element-wise AdamS
+    (7652, 3, 2, "0.9", "tensor_sigma"),          # n_p % 16 == 4: vector streams, AdamS lines shifted per partition
     (3 * 4096 + 100, 4, 4, "0.99", "tensor_sigma"),  # several tiles and a ragged tail
     (5003, 2, 3, "0.95", "tensor_sigma"),         # odd n_p: scalar path
     (12_000, 2, 2, "0.999", "stress_t3"),         # duplicate magnitudes across tensor scales
@@ -445,7 +445,8 @@ def test_step_multi_pass(S, n_p, P, K, sp, law, offset, store_v):
 
 
 @pytest.mark.parametrize("n_p,P,K,sp,store_v", [
-    (8228, 8, 8, "0.99", True),       # n_p % 16 == 4: element-wise AdamS stores
+    (8228, 8, 8, "0.99", True),       # n_p % 16 == 4: AdamS lines shifted per partition
+    (8232, 8, 8, "0.99", False),      # n_p % 16 == 8 (the Llama-500M layout's), no v
     (5003, 4, 8, "0.995", True),      # odd n_p: scalar path, K > P
     (8192, 16, 8, "0.99", False),     # whole-segment AdamS stores, no v
 ])
@@ -521,15 +522,17 @@ def test_step_extreme_gradients(S):
 @pytest.mark.parametrize("n_p,offset,sp", [
     (4096 + 160, 0, "0.9"),    # n_p % 16 == 0, 64-byte aligned rows: whole-segment w/m/v writes
     (4096 + 160, 4, "0.9"),    # 16-byte but not 64-byte aligned: per-element writes, vector streams
-    (4096 + 164, 0, "0.9"),    # n_p % 16 == 4: per-element writes, vector streams
+    (4096 + 164, 0, "0.9"),    # n_p % 16 == 4: whole lines, shifted per partition
+    (4096 + 168, 0, "0.99"),   # n_p % 16 == 8
+    (4096 + 172, 0, "0.9"),    # n_p % 16 == 12
     (4096 + 160, 1, "0.9"),    # 4-byte aligned: scalar path
     (4096 + 160, 0, "0.999"),  # aligned, but masked elements too rare: per-element writes
 ])
 def test_step_adams_store_paths(S, n_p, offset, sp):
     """The step pass writes the AdamS results either as whole 64-byte
-    segments or element by element, chosen by the alignment of w, m, v,
-    n_p and the mask density; every choice gives the oracle's state bit for
-    bit."""
+    lines of w, m, v (shifted per partition where n_p % 16 != 0) or element
+    by element, chosen by the alignment of w, m, v and the mask density;
+    every choice gives the oracle's state bit for bit."""
     cfg = W.flat_config("align", 3 * n_p, 3, 2, sp, steps=3, weight_decay=0.01)
     run_lockstep(S, cfg, cfg.steps, offset=offset)
 
@@ -539,7 +542,7 @@ def test_step_adams_store_paths(S, n_p, offset, sp):
     (4096 + 160, 4, "0.9"),    # per-element writes, vector streams
     (4096 + 160, 1, "0.9"),    # scalar path
     (4096 + 160, 0, "0.999"),  # whole segments still (no v line to read)
-    (4096 + 164, 0, "0.9"),    # n_p % 16 == 4: per-element writes
+    (4096 + 164, 0, "0.9"),    # n_p % 16 == 4: whole lines, shifted per partition
 ])
 def test_step_without_v(S, n_p, offset, sp):
     """v not stored (AdamS keeps no second moment): w, m, e and the masks

@@ -469,6 +469,17 @@ def measure_workload(S, W, torch, cfg, args, steps, warmup, full, log_fn):
     # e's role for two ordinary steps per round (S.choose_placement); the
     # fastest keeps it.  Untimed, before the warmup.
     if args.place > 1 and n > SMALL_N:
+        # The gradient sets after the first lend their memory to more
+        # allocations of e while the placement is chosen, so its steps all
+        # take the first set.  Afterwards the state is put back to its
+        # initial values (no step has run yet), the sets are generated
+        # again, and the same number of ordinary steps runs over all of
+        # them: the steps that follow are those of a run that cycled every
+        # set from the start.
+        assert t == 0
+        lent = len(pool) - 1
+        del pool[1:]
+        torch.cuda.empty_cache()
         free, _ = torch.cuda.mem_get_info()
         ncand = int(min(args.place - 1, (free - PLACE_MARGIN) // (e.numel() * 4)))
         if ncand >= 1:
@@ -485,9 +496,25 @@ def measure_workload(S, W, torch, cfg, args, steps, warmup, full, log_fn):
             torch.cuda.empty_cache()
             best = place_ms.index(min(place_ms))
             rec["e_placement"] = {"allocations": ncand + 1, "ms_per_2_steps": place_ms, "chosen": best,
-                                  "steps": 4 * (ncand + 1)}
+                                  "steps": 4 * (ncand + 1), "gradient_sets_lent": lent}
             log_fn(f"{cfg.name}: e placement: {ncand + 1} allocations, two steps each "
                    f"{', '.join(f'{x:.2f}' for x in place_ms)} ms, kept #{best}")
+        if lent:
+            placed = t
+            W.device_init_params(cfg, args.seed, params)
+            for x in (m, v, e, mask):
+                if x is not None:
+                    x.zero_()
+            t = 0
+            sigma = W.device_sigma(cfg, args.seed, dev)
+            for s in range(1, lent + 1):
+                gset = torch.empty((K, n), dtype=torch.float32, device=dev)
+                W.device_grads(cfg, s + 1, args.seed, sigma, gset)
+                pool.append(gset)
+            del sigma
+            for _ in range(placed):
+                one_step()
+            torch.cuda.synchronize()
 
     for _ in range(warmup):
         one_step()
